@@ -1,0 +1,187 @@
+"""Python wrapper of the fp64 CPU oracle (oracle/gla_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg are its only callers.  The product package
+never imports this module.
+
+The oracle computes the gated bidirectional linear-attention token mixer of
+"SANA-Video 2.0" (NVlabs Sana docs, section Architecture: gated bidirectional
+linear attention with Wan 3D rotary position embeddings) in plain IEEE double
+arithmetic, one (b, h) head at a time: first the state S and normaliser z,
+then every token's output.  See the header of gla_oracle.c for the exact
+form and the readings it takes where the pages are silent.
+
+Inputs are bf16 bit patterns (numpy uint16 arrays, or torch bfloat16 CPU
+tensors which are viewed as such), layout [B, N, H, D] contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgla_oracle.so")
+_lib = None
+
+EPS = 1e-6
+
+
+def build() -> str:
+    """Compile gla_oracle.c into oracle/libgla_oracle.so with gcc (OpenMP)."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+           "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lp = ctypes.POINTER(ctypes.c_long)
+    c_int, c_long, c_double = ctypes.c_int, ctypes.c_long, ctypes.c_double
+    grid = [c_int, c_int, c_int, c_int, c_double, c_long, c_long, c_long]
+    lib.gla_oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.gla_oracle_bf16_to_f64.restype = c_double
+    lib.gla_oracle_num_threads.argtypes = []
+    lib.gla_oracle_num_threads.restype = c_int
+    lib.gla_oracle_axis_split.argtypes = [c_int] + [ctypes.POINTER(c_int)] * 3
+    lib.gla_oracle_axis_split.restype = None
+    lib.gla_oracle_angle.argtypes = [c_int, c_double, c_int, c_long, c_long, c_long]
+    lib.gla_oracle_angle.restype = c_double
+    lib.gla_oracle_rotate.argtypes = [c_int, c_int, c_int, c_int, c_double, c_long, c_long,
+                                      c_long, c_long, dp, dp]
+    lib.gla_oracle_rotate.restype = c_int
+    lib.gla_oracle_state.argtypes = [u16p, u16p, c_int, c_int, c_int, c_int] + grid + [dp, dp]
+    lib.gla_oracle_state.restype = c_int
+    lib.gla_oracle_rows.argtypes = ([u16p, u16p, c_int, c_int, c_int, c_int] + grid +
+                                    [c_int, c_int, dp, dp, c_double, lp, c_long, dp])
+    lib.gla_oracle_rows.restype = c_int
+    lib.gla_oracle_forward.argtypes = ([u16p] * 4 + [c_int] * 4 + grid + [c_double, dp])
+    lib.gla_oracle_forward.restype = c_int
+    _lib = lib
+    return lib
+
+
+@dataclass(frozen=True)
+class Grid:
+    """Latent grid (frames T, rows Hh, columns W) with RoPE base and index offsets."""
+    T: int
+    Hh: int
+    W: int
+    theta: float = 10000.0
+    t0: int = 0
+    y0: int = 0
+    x0: int = 0
+
+    @property
+    def N(self) -> int:
+        return self.T * self.Hh * self.W
+
+
+def _grid_args(grid):
+    if grid is None:
+        return [0, 1, 1, 1, 10000.0, 0, 0, 0]
+    return [1, grid.T, grid.Hh, grid.W, float(grid.theta), grid.t0, grid.y0, grid.x0]
+
+
+def as_bits(a) -> np.ndarray:
+    """bf16 data as a C-contiguous uint16 numpy array of its bit patterns."""
+    if isinstance(a, np.ndarray):
+        if a.dtype != np.uint16:
+            raise TypeError("oracle inputs must be bf16 bit patterns (uint16)")
+        return np.ascontiguousarray(a)
+    import torch  # only to view a bfloat16 tensor's bits
+    if a.dtype != torch.bfloat16:
+        raise TypeError("oracle inputs must be bfloat16")
+    return a.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _p(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+
+
+def num_threads() -> int:
+    return _load().gla_oracle_num_threads()
+
+
+def bf16_to_f64(bits: int) -> float:
+    return _load().gla_oracle_bf16_to_f64(int(bits))
+
+
+def axis_split(D: int):
+    """Pair counts (Pt, Py, Px) of the t/y/x axis blocks of RoPE."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _load().gla_oracle_axis_split(D, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return a.value, b.value, c.value
+
+
+def angle(D: int, theta: float, p: int, t: int, y: int, x: int) -> float:
+    return _load().gla_oracle_angle(D, float(theta), p, t, y, x)
+
+
+def rotate(u, grid: Grid, n: int) -> np.ndarray:
+    """R_n u for a length-D float vector u, token n of the grid."""
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    out = np.empty_like(u)
+    _check(_load().gla_oracle_rotate(u.shape[0], grid.T, grid.Hh, grid.W, float(grid.theta),
+                                     grid.t0, grid.y0, grid.x0, n,
+                                     _p(u, ctypes.c_double), _p(out, ctypes.c_double)))
+    return out
+
+
+def state(k, v, grid: Grid | None):
+    """(S, z) of every head: S [B, H, D, D] (S[d, e]), z [B, H, D], fp64."""
+    k, v = as_bits(k), as_bits(v)
+    B, N, H, D = k.shape
+    S = np.empty((B, H, D, D), np.float64)
+    z = np.empty((B, H, D), np.float64)
+    _check(_load().gla_oracle_state(_p(k, ctypes.c_uint16), _p(v, ctypes.c_uint16), B, N, H, D,
+                                    *_grid_args(grid), _p(S, ctypes.c_double),
+                                    _p(z, ctypes.c_double)))
+    return S, z
+
+
+def rows(q, g, grid: Grid | None, b: int, h: int, S_bh, z_bh, token_rows, eps: float = EPS):
+    """Outputs [len(token_rows), D] of head (b, h) at the given tokens."""
+    q, g = as_bits(q), as_bits(g)
+    B, N, H, D = q.shape
+    S_bh = np.ascontiguousarray(S_bh, dtype=np.float64)
+    z_bh = np.ascontiguousarray(z_bh, dtype=np.float64)
+    r = np.ascontiguousarray(token_rows, dtype=np.int64)
+    out = np.empty((r.shape[0], D), np.float64)
+    _check(_load().gla_oracle_rows(_p(q, ctypes.c_uint16), _p(g, ctypes.c_uint16), B, N, H, D,
+                                   *_grid_args(grid), b, h, _p(S_bh, ctypes.c_double),
+                                   _p(z_bh, ctypes.c_double), float(eps),
+                                   _p(r, ctypes.c_long), r.shape[0], _p(out, ctypes.c_double)))
+    return out
+
+
+def forward(q, k, v, g, grid: Grid | None, eps: float = EPS) -> np.ndarray:
+    """Whole forward pass: o [B, N, H, D] in fp64."""
+    q, k, v, g = (as_bits(a) for a in (q, k, v, g))
+    B, N, H, D = q.shape
+    for a in (k, v, g):
+        if a.shape != q.shape:
+            raise ValueError("q, k, v, g must share one [B, N, H, D] shape")
+    out = np.empty((B, N, H, D), np.float64)
+    _check(_load().gla_oracle_forward(*(_p(a, ctypes.c_uint16) for a in (q, k, v, g)),
+                                      B, N, H, D, *_grid_args(grid), float(eps),
+                                      _p(out, ctypes.c_double)))
+    return out

@@ -1,0 +1,317 @@
+/*
+ * gla_oracle.c -- plain fp64 CPU oracle for the gated bidirectional
+ * linear-attention token mixer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
+ * benchmark's CPU-baseline leg are the only callers.  The product library
+ * never links, loads or calls this file, and this file includes nothing
+ * from the product (no shared headers, tables or helpers).
+ *
+ * What is computed (the method, as the pages describe it):
+ *   - "SANA-Video 2.0" (NVlabs Sana docs), section Architecture: 75% of the
+ *     layers are gated *bidirectional* linear attention, positions use Wan 3D
+ *     rotary embeddings, latent patches are (1,1,1).
+ *   - "SANA-Video 2.0: Hybrid Linear Attention with Attention Residuals for
+ *     Efficient Video Generation" (mlsanity index), Abstract: gated linear
+ *     attention does the O(N) mixing.
+ * The pages give no formula.  The fixed form followed here, per (b, h):
+ *     phi(u) = max(u, 0)                              (feature map)
+ *     R_n    = block-diagonal rotation of token n     (3D RoPE)
+ *     S      = sum_n (R_n phi(k_n)) v_n^T             (D x D)
+ *     z      = sum_n phi(k_n)                         (D)
+ *     o_n[e] = sigmoid(g_n[e]) * ((R_n phi(q_n))^T S)[e] / (phi(q_n).z + eps)
+ * "Bidirectional" is read as: no causal mask, S and z sum over all N tokens.
+ *
+ * RoPE reading (the pages only name "Wan 3D rotary position embeddings"):
+ *   - the D/2 rotation pairs are (2i, 2i+1), interleaved;
+ *   - pairs are split into axis blocks in the order (t, y, x) with
+ *     Py = Px = floor(D/6) and Pt = D/2 - 2*floor(D/6);
+ *   - pair j of an axis block with Pa pairs has frequency
+ *     omega_j = theta^(-2j / (2 Pa)), theta = 10000 by default;
+ *   - the angle is (grid index + offset) * omega_j;
+ *   - the rotation of (a, b) by angle w is (a cos w - b sin w, a sin w + b cos w);
+ *   - RoPE is applied after phi, to q and k in the numerator only; the
+ *     denominator uses the unrotated features.
+ * Token order: n = (t*Hh + y)*W + x, row-major over the latent grid.
+ *
+ * Arithmetic: every input is a bf16 bit pattern widened exactly to double;
+ * all arithmetic is IEEE double in the order written; nothing is blocked,
+ * fused or reordered beyond the definition above.  OpenMP runs independent
+ * (b, h) heads in parallel; each head's sums run sequentially over n.
+ *
+ * Pins (what checks this file against something other than itself) live in
+ * tests/test_oracle.py: quadratic brute force, hand-derived closed forms,
+ * rotation invariants, special cases.  The frequency constants omega_j are
+ * a reading of the pages and are "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum {
+  ORACLE_OK = 0,
+  ORACLE_ERR_ARG = -1,
+  ORACLE_ERR_GRID = -2,
+  ORACLE_ERR_ALLOC = -3
+};
+
+/* Grid description used when RoPE is on.  rope == NULL means RoPE off. */
+typedef struct {
+  int T, Hh, W;          /* latent grid: frames, rows, columns */
+  double theta;          /* RoPE base */
+  long t0, y0, x0;       /* offsets added to every grid index */
+} oracle_grid;
+
+/* Exact widening of a bf16 bit pattern: bf16 is the top half of an IEEE
+ * binary32, so shifting the 16 bits up gives the same value as a float. */
+double gla_oracle_bf16_to_f64(uint16_t bits) {
+  uint32_t u = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+int gla_oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Pair counts of the (t, y, x) axis blocks for head dimension D. */
+void gla_oracle_axis_split(int D, int* Pt, int* Py, int* Px) {
+  int P = D / 2;
+  *Py = D / 6;
+  *Px = D / 6;
+  *Pt = P - 2 * (D / 6);
+}
+
+/* Rotation angle of pair p for a token at grid indices (t, y, x), offsets
+ * already included. */
+double gla_oracle_angle(int D, double theta, int p, long t, long y, long x) {
+  int Pt, Py, Px;
+  gla_oracle_axis_split(D, &Pt, &Py, &Px);
+  long pos;
+  int j, Pa;
+  if (p < Pt) {
+    pos = t; j = p; Pa = Pt;
+  } else if (p < Pt + Py) {
+    pos = y; j = p - Pt; Pa = Py;
+  } else {
+    pos = x; j = p - Pt - Py; Pa = Px;
+  }
+  double omega = pow(theta, -2.0 * (double)j / (2.0 * (double)Pa));
+  return (double)pos * omega;
+}
+
+/* Grid indices of token n (offsets included). */
+static void token_position(const oracle_grid* gr, long n, long* t, long* y, long* x) {
+  long HW = (long)gr->Hh * gr->W;
+  *t = n / HW + gr->t0;
+  *y = (n / gr->W) % gr->Hh + gr->y0;
+  *x = n % gr->W + gr->x0;
+}
+
+/* out = R_n u for token n; with rope == NULL the rotation is the identity. */
+static void rotate(int D, const oracle_grid* gr, long n, const double* u, double* out) {
+  if (gr == NULL) {
+    for (int d = 0; d < D; ++d) out[d] = u[d];
+    return;
+  }
+  long t, y, x;
+  token_position(gr, n, &t, &y, &x);
+  for (int p = 0; p < D / 2; ++p) {
+    double w = gla_oracle_angle(D, gr->theta, p, t, y, x);
+    double c = cos(w), s = sin(w);
+    double a = u[2 * p], b = u[2 * p + 1];
+    out[2 * p] = a * c - b * s;
+    out[2 * p + 1] = a * s + b * c;
+  }
+}
+
+/* Public wrapper of the rotation, so tests can check it in isolation:
+ * u and out hold D doubles for token n of the grid. */
+int gla_oracle_rotate(int D, int T, int Hh, int W, double theta, long t0, long y0, long x0,
+                      long n, const double* u, double* out) {
+  if (D <= 0 || (D & 1) || T <= 0 || Hh <= 0 || W <= 0) return ORACLE_ERR_ARG;
+  oracle_grid gr = {T, Hh, W, theta, t0, y0, x0};
+  rotate(D, &gr, n, u, out);
+  return ORACLE_OK;
+}
+
+static double relu(double u) { return u > 0.0 ? u : 0.0; }
+
+static double sigmoid(double u) { return 1.0 / (1.0 + exp(-u)); }
+
+/* Widen the D-vector of token n, head (b, h) from a [B, N, H, D] bf16 array. */
+static void load_row(const uint16_t* a, int N, int H, int D, int b, int h, long n, double* out) {
+  const uint16_t* p = a + (((long)b * N + n) * H + h) * (long)D;
+  for (int d = 0; d < D; ++d) out[d] = gla_oracle_bf16_to_f64(p[d]);
+}
+
+static int check_args(int B, int N, int H, int D, const oracle_grid* gr) {
+  if (B < 0 || N < 0 || H < 0 || D <= 0 || (D & 1)) return ORACLE_ERR_ARG;
+  if (gr != NULL) {
+    if (gr->T <= 0 || gr->Hh <= 0 || gr->W <= 0) return ORACLE_ERR_GRID;
+    if ((long)gr->T * gr->Hh * gr->W != (long)N) return ORACLE_ERR_GRID;
+  }
+  return ORACLE_OK;
+}
+
+/* First pass for head (b, h): S[d*D + e] = sum_n (R_n phi(k_n))[d] v_n[e],
+ * z[d] = sum_n phi(k_n)[d].  Sums run over n = 0 .. N-1 in order. */
+static int head_state(const uint16_t* k, const uint16_t* v, int N, int H, int D,
+                      const oracle_grid* gr, int b, int h, double* S, double* z) {
+  double* fk = malloc(sizeof(double) * D);
+  double* rk = malloc(sizeof(double) * D);
+  double* vr = malloc(sizeof(double) * D);
+  if (!fk || !rk || !vr) {
+    free(fk); free(rk); free(vr);
+    return ORACLE_ERR_ALLOC;
+  }
+  memset(S, 0, sizeof(double) * D * D);
+  memset(z, 0, sizeof(double) * D);
+  for (long n = 0; n < N; ++n) {
+    load_row(k, N, H, D, b, h, n, fk);
+    load_row(v, N, H, D, b, h, n, vr);
+    for (int d = 0; d < D; ++d) fk[d] = relu(fk[d]);
+    rotate(D, gr, n, fk, rk);
+    for (int d = 0; d < D; ++d) {
+      z[d] += fk[d];
+      for (int e = 0; e < D; ++e) S[(long)d * D + e] += rk[d] * vr[e];
+    }
+  }
+  free(fk); free(rk); free(vr);
+  return ORACLE_OK;
+}
+
+/* Second pass for one token n of head (b, h), given that head's S and z. */
+static void head_row(const uint16_t* q, const uint16_t* g, int N, int H, int D,
+                     const oracle_grid* gr, int b, int h, const double* S, const double* z,
+                     double eps, long n, double* fq, double* rq, double* gr_row, double* out) {
+  load_row(q, N, H, D, b, h, n, fq);
+  load_row(g, N, H, D, b, h, n, gr_row);
+  for (int d = 0; d < D; ++d) fq[d] = relu(fq[d]);
+  rotate(D, gr, n, fq, rq);
+  double den = 0.0;
+  for (int d = 0; d < D; ++d) den += fq[d] * z[d];
+  den += eps;
+  for (int e = 0; e < D; ++e) {
+    double num = 0.0;
+    for (int d = 0; d < D; ++d) num += rq[d] * S[(long)d * D + e];
+    out[e] = sigmoid(gr_row[e]) * num / den;
+  }
+}
+
+static int make_grid(int rope, int T, int Hh, int W, double theta, long t0, long y0, long x0,
+                     oracle_grid* gr, const oracle_grid** out) {
+  if (!rope) {
+    *out = NULL;
+    return ORACLE_OK;
+  }
+  gr->T = T; gr->Hh = Hh; gr->W = W; gr->theta = theta;
+  gr->t0 = t0; gr->y0 = y0; gr->x0 = x0;
+  *out = gr;
+  return ORACLE_OK;
+}
+
+/* State (S, z) of every head.  S: [B, H, D, D], z: [B, H, D], doubles.
+ * rope == 0 switches RoPE off (T, Hh, W, theta and offsets are then ignored). */
+int gla_oracle_state(const uint16_t* k, const uint16_t* v, int B, int N, int H, int D,
+                     int rope, int T, int Hh, int W, double theta, long t0, long y0, long x0,
+                     double* S, double* z) {
+  oracle_grid g0;
+  const oracle_grid* gr;
+  make_grid(rope, T, Hh, W, theta, t0, y0, x0, &g0, &gr);
+  int rc = check_args(B, N, H, D, gr);
+  if (rc) return rc;
+  int err = ORACLE_OK;
+  long BH = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    int b = (int)(bh / H), h = (int)(bh % H);
+    int r = head_state(k, v, N, H, D, gr, b, h, S + bh * D * (long)D, z + bh * D);
+    if (r) {
+#pragma omp critical
+      err = r;
+    }
+  }
+  return err;
+}
+
+/* Outputs of selected tokens of one head (b, h), given that head's S and z
+ * (layout as gla_oracle_state writes for one head).  out: [nrows, D]. */
+int gla_oracle_rows(const uint16_t* q, const uint16_t* g, int B, int N, int H, int D,
+                    int rope, int T, int Hh, int W, double theta, long t0, long y0, long x0,
+                    int b, int h, const double* S, const double* z, double eps,
+                    const long* rows, long nrows, double* out) {
+  oracle_grid g0;
+  const oracle_grid* gr;
+  make_grid(rope, T, Hh, W, theta, t0, y0, x0, &g0, &gr);
+  int rc = check_args(B, N, H, D, gr);
+  if (rc) return rc;
+  if (b < 0 || b >= B || h < 0 || h >= H) return ORACLE_ERR_ARG;
+  for (long i = 0; i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= N) return ORACLE_ERR_ARG;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* fq = malloc(sizeof(double) * D);
+    double* rq = malloc(sizeof(double) * D);
+    double* gv = malloc(sizeof(double) * D);
+    if (!fq || !rq || !gv) {
+#pragma omp critical
+      err = ORACLE_ERR_ALLOC;
+    } else {
+#pragma omp for schedule(static)
+      for (long i = 0; i < nrows; ++i)
+        head_row(q, g, N, H, D, gr, b, h, S, z, eps, rows[i], fq, rq, gv, out + i * D);
+    }
+    free(fq); free(rq); free(gv);
+  }
+  return err;
+}
+
+/* Whole forward pass: out[B, N, H, D] (doubles) from bf16 q, k, v, g. */
+int gla_oracle_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                       int B, int N, int H, int D,
+                       int rope, int T, int Hh, int W, double theta, long t0, long y0, long x0,
+                       double eps, double* out) {
+  oracle_grid g0;
+  const oracle_grid* gr;
+  make_grid(rope, T, Hh, W, theta, t0, y0, x0, &g0, &gr);
+  int rc = check_args(B, N, H, D, gr);
+  if (rc) return rc;
+  int err = ORACLE_OK;
+  long BH = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    int b = (int)(bh / H), h = (int)(bh % H);
+    double* S = malloc(sizeof(double) * D * (long)D);
+    double* z = malloc(sizeof(double) * D);
+    double* fq = malloc(sizeof(double) * D);
+    double* rq = malloc(sizeof(double) * D);
+    double* gv = malloc(sizeof(double) * D);
+    double* row = malloc(sizeof(double) * D);
+    int r = (S && z && fq && rq && gv && row) ? ORACLE_OK : ORACLE_ERR_ALLOC;
+    if (!r) r = head_state(k, v, N, H, D, gr, b, h, S, z);
+    if (!r) {
+      for (long n = 0; n < N; ++n) {
+        head_row(q, g, N, H, D, gr, b, h, S, z, eps, n, fq, rq, gv, row);
+        double* dst = out + (((long)b * N + n) * H + h) * (long)D;
+        for (int e = 0; e < D; ++e) dst[e] = row[e];
+      }
+    }
+    free(S); free(z); free(fq); free(rq); free(gv); free(row);
+    if (r) {
+#pragma omp critical
+      err = r;
+    }
+  }
+  return err;
+}
