@@ -1,0 +1,158 @@
+"""Benchmark of the gated bidirectional linear-attention mixer on one MI355X.
+
+One step = one whole pass of the hot path over one batch: the state half
+(state kernel + cross-chunk reduction, reading k and v) and the output half
+(output kernel, reading q and g, writing out), launched through the C ABI on
+torch's current stream with inputs already resident in HBM.
+
+Prints ONE JSON line.  `value` is tokens/s per layer (B*N tokens per step).
+`roofline` reports the output kernel (the largest byte stream: q, g read and
+out written, 6*D bytes per (token, head)) from HIP events recorded around it
+in every timed step.  `cpu_baseline` times the fp64 oracle on a bounded
+sample of the same workload (a subset of heads, scaled to the whole layer).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "gated linear-attn tokens/s per layer (5B 720p shape); achieved HBM GB/s vs peak"
+PEAK_HBM_GBPS = 8000.0
+DEFAULT_WORKLOAD = "5b_720p_193f"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, q, k, v, g, target_heads=None):
+    """Times the oracle on `target_heads` (b=0) heads of the workload, scaled to B*H heads."""
+    import oracle
+    threads = oracle.num_threads()
+    hs = min(w.H, target_heads or max(1, 2 * threads))
+    sl = [t[0:1, :, 0:hs].contiguous() for t in (q, k, v, g)]
+    grid = oracle.Grid(w.T, w.Hh, w.W, w.theta)
+    t0 = time.perf_counter()
+    oracle.forward(*sl, grid)
+    dt = time.perf_counter() - t0
+    scale = (w.B * w.H) / hs
+    rate = (w.B * w.N) / (dt * scale)
+    return {
+        "value": rate,
+        "unit": "tokens/s",
+        "cores": min(threads, hs),
+        "kind": "oracle",
+        "sample": f"{hs} of {w.B * w.H} (b, h) heads at full N={w.N}, {dt:.2f} s, "
+                  f"scaled x{scale:.2f} to the whole layer",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the mixer's state is exchanged within one "
+              f"device; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_linear_attention_forward_amd as gla
+    from workloads import BY_NAME, make_inputs
+
+    w = BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: workload {w.name} B={w.B} N={w.N} H={w.H} D={w.D}; generating inputs")
+    q, k, v, g = make_inputs(w)
+    qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
+    out = torch.empty_like(qd)
+    rope = gla.gla_rope_create(w.T, w.Hh, w.W, w.D, w.theta)
+    ws = gla.alloc_workspace(w.B, w.N, w.H, w.D, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        gla.gla_state_ws(kd, vd, rope, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        gla.gla_output_ws(qd, gd, rope, out, ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    state_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    out_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ev_step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
+    units = w.B * w.N * w.H
+    out_bytes = 6 * w.D * units        # q, g read + out written, bf16
+    state_bytes = 4 * w.D * units      # k, v read, bf16
+    all_bytes = out_bytes + state_bytes
+    achieved = out_bytes / (out_ms * 1e-3) / 1e9
+    tokens = w.B * w.N
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "D": w.D,
+                   "grid": [w.T, w.Hh, w.W], "parallelism": "single-gpu"},
+        "hbm_gbps_effective": all_bytes / (ms_step * 1e-3) / 1e9,
+        "phases_ms": {"state": state_ms, "output": out_ms, "step_events": ev_step_ms},
+        "roofline": {
+            "kernel": "output_kernel",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": None,
+            "algorithmic_bytes": out_bytes,
+            "avg_ms": out_ms,
+        },
+    }
+    rope.close()
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle (cpu_baseline)")
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, g)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

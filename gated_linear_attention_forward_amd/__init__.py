@@ -1,0 +1,24 @@
+"""Gated bidirectional linear-attention token mixer for AMD MI355X (gfx950).
+
+The compute path is libgla.so (C ABI in include/gla.h, HIP kernels in
+csrc/); this package is its thin ctypes binding.
+"""
+from .gla import (  # noqa: F401
+    EXPORTS,
+    GlaError,
+    RopeTables,
+    alloc_workspace,
+    gla_forward,
+    gla_forward_check,
+    gla_forward_ws,
+    gla_output_ws,
+    gla_rope_create,
+    gla_rope_destroy,
+    gla_rope_fill_host,
+    gla_rope_table_floats,
+    gla_state,
+    gla_state_ws,
+    gla_strerror,
+    gla_workspace_bytes,
+    load_library,
+)

@@ -1,0 +1,412 @@
+// gla_api.cpp -- host side of the C ABI declared in include/gla.h:
+// argument validation (before any HIP call), the factorised 3D RoPE table
+// builder, the work plan, the per-(device, stream) workspace cache and the
+// kernel launches.
+#include "gla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "gla_internal.h"
+
+namespace gla {
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+// The state kernel wants a few blocks per compute unit in flight (256 CUs),
+// while every chunk adds one fp32 (D*D + D) partial per head.  The output
+// kernel reads only a bf16 copy of the state per block, so it takes more.
+Plan make_plan(int B, int N, int H, int D) {
+  Plan p{};
+  p.B = B; p.N = N; p.H = H; p.D = D;
+  p.BH = B * H;
+  if (p.BH == 0 || N == 0) return p;
+  const int tt = state_tile_tokens(D);
+  const int tiles = ceil_div(N, tt);
+  int C = ceil_div(512, p.BH);
+  if (C > tiles) C = tiles;
+  if (C > kMaxChunks) C = kMaxChunks;
+  if (C < 1) C = 1;
+  p.L = ceil_div(tiles, C) * tt;
+  p.C = ceil_div(N, p.L);
+
+  const int its = ceil_div(N, kOutputTileTokens);
+  int C2 = ceil_div(1024, p.BH);
+  if (C2 > its) C2 = its;
+  if (C2 < 1) C2 = 1;
+  p.L2 = ceil_div(its, C2) * kOutputTileTokens;
+  p.C2 = ceil_div(N, p.L2);
+
+  size_t off = 0;
+  p.off_part = off;
+  off = align_up(off + (size_t)p.BH * p.C * (size_t)(D * D + D) * sizeof(float), 256);
+  p.off_sl = off;
+  off = align_up(off + (size_t)p.BH * D * D * sizeof(uint16_t), 256);
+  p.off_z = off;
+  off = align_up(off + (size_t)p.BH * D * sizeof(float), 256);
+  p.ws_bytes = off;
+  return p;
+}
+
+}  // namespace gla
+
+using gla::Plan;
+using gla::RopeArgs;
+
+namespace {
+
+bool dim_ok(int D) { return D == 32 || D == 64 || D == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + abytes) and [b, b + bbytes) share a byte
+bool overlap2(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bbytes && y < x + abytes;
+}
+
+bool overlap(const void* a, const void* b, size_t bytes) { return overlap2(a, bytes, b, bytes); }
+
+// Shape checks shared by every entry point.  Returns GLA_OK and the tensor
+// size in bytes, or an error.
+int check_shape(int B, int N, int H, int D, size_t* bytes) {
+  if (B < 0 || N < 0 || H < 0) return GLA_ERR_DIM;
+  if (!dim_ok(D)) return GLA_ERR_DIM;
+  const long long bh = (long long)B * H;
+  if (bh > 65535) return GLA_ERR_DIM;  // heads go to grid.y
+  const long long elems = (long long)B * N * H * D;
+  if (elems > (1LL << 40)) return GLA_ERR_DIM;
+  *bytes = (size_t)elems * 2;
+  return GLA_OK;
+}
+
+int check_rope(const gla_rope_tables* rope, int N, int D) {
+  if (!rope) return GLA_OK;
+  if (!rope->cs) return GLA_ERR_NULL;
+  if (rope->D != D) return GLA_ERR_ROPE;
+  if ((long long)rope->T * rope->Hh * rope->W != (long long)N) return GLA_ERR_ROPE;
+  if (rope->Pt + rope->Py + rope->Px != D / 2) return GLA_ERR_ROPE;
+  if (rope->cs_floats != gla_rope_table_floats(rope->T, rope->Hh, rope->W, D)) return GLA_ERR_ROPE;
+  return GLA_OK;
+}
+
+int check_tensors(std::initializer_list<const void*> ins, const void* out, size_t bytes) {
+  for (const void* p : ins)
+    if (!p) return GLA_ERR_NULL;
+  if (out == nullptr) return GLA_ERR_NULL;
+  for (const void* p : ins)
+    if (!aligned16(p)) return GLA_ERR_ALIGN;
+  if (!aligned16(out)) return GLA_ERR_ALIGN;
+  for (const void* p : ins)
+    if (bytes && overlap(p, out, bytes)) return GLA_ERR_ALIAS;
+  return GLA_OK;
+}
+
+RopeArgs rope_args(const gla_rope_tables* r) {
+  RopeArgs a{};
+  if (!r) return a;
+  a.cs = reinterpret_cast<const float2*>(r->cs);
+  a.T = r->T; a.Hh = r->Hh; a.W = r->W;
+  a.Pt = r->Pt; a.Py = r->Py; a.Px = r->Px;
+  return a;
+}
+
+int rope_device_ok(const gla_rope_tables* rope) {
+  if (!rope) return GLA_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
+  return dev == rope->device ? GLA_OK : GLA_ERR_ROPE;
+}
+
+void axis_split(int D, int* Pt, int* Py, int* Px) {
+  *Py = D / 6;
+  *Px = D / 6;
+  *Pt = D / 2 - 2 * (D / 6);
+}
+
+// ---- library-owned workspace, one per (device, stream) -------------------
+struct WsKey {
+  int device;
+  void* stream;
+  bool operator<(const WsKey& o) const {
+    return device != o.device ? device < o.device : stream < o.stream;
+  }
+};
+struct WsBuf {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<WsKey, WsBuf>* g_ws = nullptr;  // never destroyed: process-lifetime cache
+
+int get_workspace(size_t bytes, void* stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (!g_ws) g_ws = new (std::nothrow) std::map<WsKey, WsBuf>();
+  if (!g_ws) return GLA_ERR_ALLOC;
+  WsBuf& b = (*g_ws)[WsKey{dev, stream}];
+  if (b.bytes < bytes) {
+    if (b.ptr) {
+      // earlier work on this stream may still read the old buffer
+      if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
+      (void)hipFree(b.ptr);
+      b.ptr = nullptr;
+      b.bytes = 0;
+    }
+    size_t want = bytes + bytes / 4;
+    if (hipMalloc(&b.ptr, want) != hipSuccess) {
+      (void)hipGetLastError();
+      b.ptr = nullptr;
+      return GLA_ERR_ALLOC;
+    }
+    b.bytes = want;
+  }
+  *out = b.ptr;
+  return GLA_OK;
+}
+
+int check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
+  if (!ws) return GLA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return GLA_ERR_WORKSPACE;
+  if (ws_bytes < p.ws_bytes) return GLA_ERR_WORKSPACE;
+  return GLA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? GLA_OK : GLA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gla_strerror(int status) {
+  switch (status) {
+    case GLA_OK: return "success";
+    case GLA_ERR_NULL: return "a required pointer is NULL";
+    case GLA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case GLA_ERR_DIM: return "bad shape: D must be 32, 64 or 128; B, N, H non-negative; B*H <= 65535";
+    case GLA_ERR_ROPE: return "RoPE tables do not match the call (grid, head dim or device)";
+    case GLA_ERR_ALLOC: return "device memory allocation failed";
+    case GLA_ERR_LAUNCH: return "kernel launch failed";
+    case GLA_ERR_ALIAS: return "out overlaps an input";
+    case GLA_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case GLA_ERR_HIP: return "HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+size_t gla_rope_table_floats(int T, int Hh, int W, int D) {
+  if (T < 1 || Hh < 1 || W < 1 || D < 2 || (D & 1)) return 0;
+  int Pt, Py, Px;
+  axis_split(D, &Pt, &Py, &Px);
+  return 2 * ((size_t)T * Pt + (size_t)Hh * Py + (size_t)W * Px);
+}
+
+int gla_rope_fill_host(int T, int Hh, int W, int D, double theta, int t0, int y0, int x0,
+                       float* cs, size_t cs_floats) {
+  if (!cs) return GLA_ERR_NULL;
+  const size_t need = gla_rope_table_floats(T, Hh, W, D);
+  if (need == 0) return GLA_ERR_DIM;
+  if (cs_floats < need) return GLA_ERR_ROPE;
+  if (!(theta > 0.0)) return GLA_ERR_ROPE;
+  int P[3];
+  axis_split(D, &P[0], &P[1], &P[2]);
+  const int len[3] = {T, Hh, W};
+  const int off[3] = {t0, y0, x0};
+  size_t at = 0;
+  for (int a = 0; a < 3; ++a) {
+    for (int pos = 0; pos < len[a]; ++pos) {
+      for (int j = 0; j < P[a]; ++j) {
+        // frequency theta^(-2j / (2 Pa)) of pair j within this axis block
+        double omega = std::exp(-std::log(theta) * (2.0 * j) / (2.0 * P[a]));
+        double ang = (double)(pos + off[a]) * omega;
+        cs[at++] = (float)std::cos(ang);
+        cs[at++] = (float)std::sin(ang);
+      }
+    }
+  }
+  return GLA_OK;
+}
+
+int gla_rope_create(int T, int Hh, int W, int D, double theta, int t0, int y0, int x0,
+                    void* stream, gla_rope_tables** out) {
+  if (!out) return GLA_ERR_NULL;
+  *out = nullptr;
+  if (!dim_ok(D)) return GLA_ERR_DIM;
+  const size_t nf = gla_rope_table_floats(T, Hh, W, D);
+  if (nf == 0) return GLA_ERR_DIM;
+  if ((long long)T * Hh * W > INT32_MAX) return GLA_ERR_DIM;
+  std::vector<float> host;
+  try {
+    host.resize(nf);
+  } catch (...) {
+    return GLA_ERR_ALLOC;
+  }
+  int rc = gla_rope_fill_host(T, Hh, W, D, theta, t0, y0, x0, host.data(), nf);
+  if (rc) return rc;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
+  auto* r = new (std::nothrow) gla_rope_tables();
+  if (!r) return GLA_ERR_ALLOC;
+  void* d = nullptr;
+  if (hipMalloc(&d, nf * sizeof(float)) != hipSuccess) {
+    (void)hipGetLastError();
+    delete r;
+    return GLA_ERR_ALLOC;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(d, host.data(), nf * sizeof(float), hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
+    (void)hipFree(d);
+    delete r;
+    return GLA_ERR_HIP;
+  }
+  r->T = T; r->Hh = Hh; r->W = W; r->D = D;
+  axis_split(D, &r->Pt, &r->Py, &r->Px);
+  r->t0 = t0; r->y0 = y0; r->x0 = x0;
+  r->theta = theta;
+  r->cs = static_cast<const float*>(d);
+  r->cs_floats = nf;
+  r->device = dev;
+  *out = r;
+  return GLA_OK;
+}
+
+int gla_rope_destroy(gla_rope_tables* tables) {
+  if (!tables) return GLA_OK;
+  int rc = GLA_OK;
+  if (tables->cs && hipFree(const_cast<float*>(tables->cs)) != hipSuccess) rc = GLA_ERR_HIP;
+  delete tables;
+  return rc;
+}
+
+size_t gla_workspace_bytes(int B, int N, int H, int D) {
+  size_t bytes = 0;
+  if (check_shape(B, N, H, D, &bytes) != GLA_OK) return 0;
+  if (bytes == 0) return 0;
+  return gla::make_plan(B, N, H, D).ws_bytes;
+}
+
+int gla_forward_check(const void* q, const void* k, const void* v, const void* g,
+                      const gla_rope_tables* rope, const void* out, int B, int N, int H, int D) {
+  size_t bytes = 0;
+  int rc = check_shape(B, N, H, D, &bytes);
+  if (rc) return rc;
+  if (bytes == 0) return GLA_OK;
+  if ((rc = check_rope(rope, N, D))) return rc;
+  return check_tensors({q, k, v, g}, out, bytes);
+}
+
+int gla_state_ws(const void* k, const void* v, const gla_rope_tables* rope, int B, int N, int H,
+                 int D, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t bytes = 0;
+  int rc = check_shape(B, N, H, D, &bytes);
+  if (rc) return rc;
+  if (bytes == 0) return GLA_OK;
+  if ((rc = check_rope(rope, N, D))) return rc;
+  if (!k || !v) return GLA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v)) return GLA_ERR_ALIGN;
+  Plan p = gla::make_plan(B, N, H, D);
+  if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  if ((rc = rope_device_ok(rope))) return rc;
+  return status_of(gla::launch_state(p, static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), rope_args(rope), workspace,
+                                     nullptr, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int gla_output_ws(const void* q, const void* g, const gla_rope_tables* rope, void* out, int B,
+                  int N, int H, int D, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t bytes = 0;
+  int rc = check_shape(B, N, H, D, &bytes);
+  if (rc) return rc;
+  if (bytes == 0) return GLA_OK;
+  if ((rc = check_rope(rope, N, D))) return rc;
+  if ((rc = check_tensors({q, g}, out, bytes))) return rc;
+  Plan p = gla::make_plan(B, N, H, D);
+  if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  if ((rc = rope_device_ok(rope))) return rc;
+  return status_of(gla::launch_output(p, static_cast<const uint16_t*>(q),
+                                      static_cast<const uint16_t*>(g), rope_args(rope), workspace,
+                                      static_cast<uint16_t*>(out),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
+                   const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = gla_forward_check(q, k, v, g, rope, out, B, N, H, D);
+  if (rc) return rc;
+  if ((long long)B * N * H == 0) return GLA_OK;
+  Plan p = gla::make_plan(B, N, H, D);
+  if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  if ((rc = rope_device_ok(rope))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RopeArgs ra = rope_args(rope);
+  rc = status_of(gla::launch_state(p, static_cast<const uint16_t*>(k),
+                                   static_cast<const uint16_t*>(v), ra, workspace, nullptr,
+                                   nullptr, s));
+  if (rc) return rc;
+  return status_of(gla::launch_output(p, static_cast<const uint16_t*>(q),
+                                      static_cast<const uint16_t*>(g), ra, workspace,
+                                      static_cast<uint16_t*>(out), s));
+}
+
+int gla_forward(const void* q, const void* k, const void* v, const void* g,
+                const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                void* stream) {
+  int rc = gla_forward_check(q, k, v, g, rope, out, B, N, H, D);
+  if (rc) return rc;
+  if ((long long)B * N * H == 0) return GLA_OK;
+  Plan p = gla::make_plan(B, N, H, D);
+  void* ws = nullptr;
+  if ((rc = get_workspace(p.ws_bytes, stream, &ws))) return rc;
+  return gla_forward_ws(q, k, v, g, rope, out, B, N, H, D, ws, p.ws_bytes, stream);
+}
+
+int gla_state(const void* k, const void* v, const gla_rope_tables* rope, float* S, float* z,
+              int B, int N, int H, int D, void* stream) {
+  size_t bytes = 0;
+  int rc = check_shape(B, N, H, D, &bytes);
+  if (rc) return rc;
+  if ((rc = check_rope(rope, N, D))) return rc;
+  if ((long long)B * H == 0) return GLA_OK;
+  if (!k || !v || !S || !z) return GLA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(z)) return GLA_ERR_ALIGN;
+  const size_t sbytes = (size_t)B * H * D * D * sizeof(float);
+  const size_t zbytes = (size_t)B * H * D * sizeof(float);
+  if (bytes && (overlap2(S, sbytes, k, bytes) || overlap2(S, sbytes, v, bytes) ||
+                overlap2(z, zbytes, k, bytes) || overlap2(z, zbytes, v, bytes)))
+    return GLA_ERR_ALIAS;
+  if (overlap2(S, sbytes, z, zbytes)) return GLA_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    // empty sequence: S = 0, z = 0
+    if (hipMemsetAsync(S, 0, sbytes, s) != hipSuccess) return GLA_ERR_HIP;
+    if (hipMemsetAsync(z, 0, zbytes, s) != hipSuccess) return GLA_ERR_HIP;
+    return GLA_OK;
+  }
+  Plan p = gla::make_plan(B, N, H, D);
+  void* ws = nullptr;
+  if ((rc = get_workspace(p.ws_bytes, stream, &ws))) return rc;
+  if ((rc = rope_device_ok(rope))) return rc;
+  return status_of(gla::launch_state(p, static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), rope_args(rope), ws, S, z,
+                                     s));
+}
+
+}  // extern "C"

@@ -1,0 +1,281 @@
+"""Python binding of libgla.so (include/gla.h): argument marshalling only.
+
+Every step of the mixer runs in the library's HIP kernels; PyTorch only
+provides device memory and the current stream.  The functions carry the C
+names.  If the library has not been built the first call raises -- there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgla.so")
+
+GLA_OK = 0
+GLA_ERR_NULL = -1
+GLA_ERR_ALIGN = -2
+GLA_ERR_DIM = -3
+GLA_ERR_ROPE = -4
+GLA_ERR_ALLOC = -5
+GLA_ERR_LAUNCH = -6
+GLA_ERR_ALIAS = -7
+GLA_ERR_WORKSPACE = -8
+GLA_ERR_HIP = -9
+
+EXPORTS = (
+    "gla_strerror", "gla_rope_table_floats", "gla_rope_fill_host", "gla_rope_create",
+    "gla_rope_destroy", "gla_workspace_bytes", "gla_forward", "gla_forward_ws",
+    "gla_forward_check", "gla_state_ws", "gla_output_ws", "gla_state",
+)
+
+
+class GlaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {gla_strerror(code)} (status {code})")
+
+
+class gla_rope_tables(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32), ("Hh", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("Pt", ctypes.c_int32), ("Py", ctypes.c_int32), ("Px", ctypes.c_int32),
+        ("t0", ctypes.c_int32), ("y0", ctypes.c_int32), ("x0", ctypes.c_int32),
+        ("theta", ctypes.c_double),
+        ("cs", ctypes.c_void_p),
+        ("cs_floats", ctypes.c_size_t),
+        ("device", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library():
+    """Loads libgla.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -m gated_linear_attention_forward_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+    rp = ctypes.POINTER(gla_rope_tables)
+    sig = {
+        "gla_strerror": ([i32], ctypes.c_char_p),
+        "gla_rope_table_floats": ([i32] * 4, sz),
+        "gla_rope_fill_host": ([i32] * 4 + [dbl] + [i32] * 3 + [vp, sz], i32),
+        "gla_rope_create": ([i32] * 4 + [dbl] + [i32] * 3 + [vp, ctypes.POINTER(rp)], i32),
+        "gla_rope_destroy": ([rp], i32),
+        "gla_workspace_bytes": ([i32] * 4, sz),
+        "gla_forward": ([vp] * 4 + [rp, vp] + [i32] * 4 + [vp], i32),
+        "gla_forward_ws": ([vp] * 4 + [rp, vp] + [i32] * 4 + [vp, sz, vp], i32),
+        "gla_forward_check": ([vp] * 4 + [rp, vp] + [i32] * 4, i32),
+        "gla_state_ws": ([vp, vp, rp] + [i32] * 4 + [vp, sz, vp], i32),
+        "gla_output_ws": ([vp, vp, rp, vp] + [i32] * 4 + [vp, sz, vp], i32),
+        "gla_state": ([vp, vp, rp, vp, vp] + [i32] * 4 + [vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def _ok(code: int, where: str):
+    if code != GLA_OK:
+        raise GlaError(code, where)
+
+
+def gla_strerror(code: int) -> str:
+    return load_library().gla_strerror(int(code)).decode()
+
+
+# ---------------------------------------------------------------------------
+# RoPE tables
+
+
+class RopeTables:
+    """Owner of a library-built gla_rope_tables descriptor (device memory)."""
+
+    def __init__(self, ptr):
+        self._ptr = ptr
+
+    @property
+    def ptr(self):
+        if self._ptr is None:
+            raise ValueError("RoPE tables already destroyed")
+        return self._ptr
+
+    @property
+    def desc(self) -> gla_rope_tables:
+        return self.ptr.contents
+
+    def close(self):
+        if self._ptr is not None and _lib is not None:
+            _ok(_lib.gla_rope_destroy(self._ptr), "gla_rope_destroy")
+        self._ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _stream_handle(stream, device=None):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def gla_rope_table_floats(T: int, Hh: int, W: int, D: int) -> int:
+    return load_library().gla_rope_table_floats(T, Hh, W, D)
+
+
+def gla_rope_fill_host(T, Hh, W, D, theta=10000.0, t0=0, y0=0, x0=0) -> np.ndarray:
+    """The (cos, sin) table as the library builds it, on the host (no GPU)."""
+    n = gla_rope_table_floats(T, Hh, W, D)
+    if n == 0:
+        raise GlaError(GLA_ERR_DIM, "gla_rope_fill_host")
+    buf = np.empty(n, np.float32)
+    _ok(load_library().gla_rope_fill_host(T, Hh, W, D, float(theta), t0, y0, x0,
+                                          buf.ctypes.data_as(ctypes.c_void_p), n),
+        "gla_rope_fill_host")
+    return buf
+
+
+def gla_rope_create(T, Hh, W, D, theta=10000.0, t0=0, y0=0, x0=0, stream=None) -> RopeTables:
+    ptr = ctypes.POINTER(gla_rope_tables)()
+    _ok(load_library().gla_rope_create(T, Hh, W, D, float(theta), t0, y0, x0,
+                                       _stream_handle(stream), ctypes.byref(ptr)),
+        "gla_rope_create")
+    return RopeTables(ptr)
+
+
+def gla_rope_destroy(tables: RopeTables):
+    tables.close()
+
+
+# ---------------------------------------------------------------------------
+# forward pass
+
+
+def _check_bf16(name, t, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, N, H, D], got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _rope_ptr(rope):
+    """RopeTables, a raw ctypes pointer to gla_rope_tables, or None (RoPE off)."""
+    if rope is None:
+        return None
+    if isinstance(rope, RopeTables):
+        return rope.ptr
+    return rope
+
+
+def gla_workspace_bytes(B: int, N: int, H: int, D: int) -> int:
+    return load_library().gla_workspace_bytes(B, N, H, D)
+
+
+def alloc_workspace(B: int, N: int, H: int, D: int, device=None) -> torch.Tensor:
+    """A torch-owned uint8 device buffer large enough for gla_forward_ws."""
+    return torch.empty(max(gla_workspace_bytes(B, N, H, D), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def gla_forward_check(q, k, v, g, rope, out, B, N, H, D) -> int:
+    """Status the library's own argument validation gives (no GPU needed).
+    Pointers are passed as plain integers here."""
+    return load_library().gla_forward_check(q, k, v, g, _rope_ptr(rope), out, B, N, H, D)
+
+
+def gla_forward(q, k, v, g, rope=None, out=None, stream=None) -> torch.Tensor:
+    """out = sigmoid(g) * (R phi(q))^T S / (phi(q).z + eps) per head; bf16 [B, N, H, D]."""
+    _check_bf16("q", q)
+    for name, t in (("k", k), ("v", v), ("g", g)):
+        _check_bf16(name, t, q.shape)
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bf16("out", out, q.shape)
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                       _rope_ptr(rope), out.data_ptr(), B, N, H, D,
+                                       _stream_handle(stream, q.device)),
+            "gla_forward")
+    return out
+
+
+def gla_forward_ws(q, k, v, g, rope, out, ws: torch.Tensor, stream=None) -> torch.Tensor:
+    _check_bf16("q", q)
+    for name, t in (("k", k), ("v", v), ("g", g), ("out", out)):
+        _check_bf16(name, t, q.shape)
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_forward_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          g.data_ptr(), _rope_ptr(rope), out.data_ptr(),
+                                          B, N, H, D, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                          _stream_handle(stream, q.device)),
+            "gla_forward_ws")
+    return out
+
+
+def gla_state_ws(k, v, rope, ws: torch.Tensor, stream=None):
+    _check_bf16("k", k)
+    _check_bf16("v", v, k.shape)
+    B, N, H, D = k.shape
+    with torch.cuda.device(k.device):
+        _ok(load_library().gla_state_ws(k.data_ptr(), v.data_ptr(), _rope_ptr(rope), B, N, H, D,
+                                        ws.data_ptr(), ws.numel() * ws.element_size(),
+                                        _stream_handle(stream, k.device)),
+            "gla_state_ws")
+
+
+def gla_output_ws(q, g, rope, out, ws: torch.Tensor, stream=None) -> torch.Tensor:
+    _check_bf16("q", q)
+    _check_bf16("g", g, q.shape)
+    _check_bf16("out", out, q.shape)
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_output_ws(q.data_ptr(), g.data_ptr(), _rope_ptr(rope),
+                                         out.data_ptr(), B, N, H, D, ws.data_ptr(),
+                                         ws.numel() * ws.element_size(),
+                                         _stream_handle(stream, q.device)),
+            "gla_output_ws")
+    return out
+
+
+def gla_state(k, v, rope=None, stream=None):
+    """(S [B, H, D, D] fp32 with S[d, e], z [B, H, D] fp32) from the state kernels."""
+    _check_bf16("k", k)
+    _check_bf16("v", v, k.shape)
+    B, N, H, D = k.shape
+    S = torch.empty((B, H, D, D), dtype=torch.float32, device=k.device)
+    z = torch.empty((B, H, D), dtype=torch.float32, device=k.device)
+    with torch.cuda.device(k.device):
+        _ok(load_library().gla_state(k.data_ptr(), v.data_ptr(), _rope_ptr(rope), S.data_ptr(),
+                                     z.data_ptr(), B, N, H, D, _stream_handle(stream, k.device)),
+            "gla_state")
+    return S, z

@@ -1,0 +1,159 @@
+/*
+ * gla.h -- C ABI of the gated bidirectional linear-attention token mixer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("SANA-Video 2.0", NVlabs Sana docs, section Architecture:
+ * gated bidirectional linear-attention layers with Wan 3D rotary position
+ * embeddings, BF16 inference per section Model zoo; "SANA-Video 2.0: Hybrid
+ * Linear Attention with Attention Residuals ..." (mlsanity index), Abstract:
+ * gated linear attention for the O(N) token mixing), per batch b and head h:
+ *
+ *     phi(u) = max(u, 0)
+ *     S      = sum_n (R_n phi(k_n)) v_n^T        D x D, no causal mask
+ *     z      = sum_n phi(k_n)                    D
+ *     o_n    = sigmoid(g_n) * ((R_n phi(q_n))^T S) / (phi(q_n) . z + 1e-6)
+ *
+ * R_n is the 3D RoPE rotation of token n at latent-grid position (t, y, x):
+ * the D/2 interleaved pairs (2i, 2i+1) are split into axis blocks t, y, x of
+ * Pt = D/2 - 2*floor(D/6), Py = Px = floor(D/6) pairs; pair j of an axis
+ * block with Pa pairs turns by (index + offset) * theta^(-2j / (2 Pa)).
+ * Tokens are ordered n = (t*Hh + y)*W + x.  RoPE acts on the numerator only.
+ *
+ * Tensors.  q, k, v, g and out are device pointers to bf16 arrays of shape
+ * [B, N, H, D], contiguous (element (b, n, h, d) at ((b*N + n)*H + h)*D + d),
+ * each 16-byte aligned.  D must be 32, 64 or 128.  out must not overlap any
+ * input.  The caller owns every tensor; the library never frees them.
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream) on the
+ * current HIP device; every pointer must belong to that device.  Calls only
+ * enqueue work and return without a host synchronisation, except where a
+ * library-owned buffer has to grow (noted below).  Results are bitwise
+ * reproducible for the same inputs, shape and device.
+ *
+ * Errors.  Every entry point returns an int status (GLA_OK or a negative
+ * gla_status).  Arguments are validated before any HIP call, so a rejected
+ * call has no side effect.  Faults inside a kernel surface at the caller's
+ * next synchronisation, as with any HIP launch.  No C++ exception crosses
+ * this interface.
+ */
+#ifndef GLA_H_
+#define GLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gla_status {
+  GLA_OK = 0,
+  GLA_ERR_NULL = -1,      /* a required pointer is NULL */
+  GLA_ERR_ALIGN = -2,     /* a tensor pointer is not 16-byte aligned */
+  GLA_ERR_DIM = -3,       /* D not in {32, 64, 128}; B, N or H negative; size overflow */
+  GLA_ERR_ROPE = -4,      /* RoPE tables do not fit (T*Hh*W != N, other D, other device) */
+  GLA_ERR_ALLOC = -5,     /* device memory allocation failed */
+  GLA_ERR_LAUNCH = -6,    /* a kernel launch failed */
+  GLA_ERR_ALIAS = -7,     /* out overlaps an input */
+  GLA_ERR_WORKSPACE = -8, /* caller workspace too small or not 256-byte aligned */
+  GLA_ERR_HIP = -9        /* another HIP runtime call failed */
+};
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* gla_strerror(int status);
+
+/* ---------------------------------------------------------------------
+ * 3D RoPE tables.
+ *
+ * The rotation factors are stored factorised per axis: (cos, sin) float
+ * pairs of (index + offset) * omega_j for every grid index of each axis,
+ * laid out as [T][Pt] | [Hh][Py] | [W][Px] pairs (t block first).  They are
+ * computed in double precision on the host and rounded to float.  For the
+ * 5B 720p/60s grid (181 x 22 x 40, D = 128) this is 42 KB, against 81.5 MB
+ * for a dense per-token table.
+ */
+typedef struct gla_rope_tables {
+  int32_t T, Hh, W;      /* latent grid: frames, rows, columns */
+  int32_t D;             /* head dimension the tables were built for */
+  int32_t Pt, Py, Px;    /* rotation pairs per axis; Pt + Py + Px = D/2 */
+  int32_t t0, y0, x0;    /* index offsets added to every position */
+  double theta;          /* RoPE base (10000 in the Wan convention) */
+  const float* cs;       /* device pointer: the (cos, sin) pairs above */
+  size_t cs_floats;      /* number of floats behind cs */
+  int32_t device;        /* HIP device that holds cs */
+} gla_rope_tables;
+
+/* Number of floats the (cos, sin) table of a grid takes, 0 for bad sizes. */
+size_t gla_rope_table_floats(int T, int Hh, int W, int D);
+
+/* Fills a HOST buffer of `cs_floats` floats with the table described above
+ * (no GPU needed).  D must be even and >= 2; T, Hh, W >= 1. */
+int gla_rope_fill_host(int T, int Hh, int W, int D, double theta, int t0, int y0, int x0,
+                       float* cs, size_t cs_floats);
+
+/* Builds the table on the host, copies it to the current device (enqueued on
+ * `stream`, then synchronised so the host copy can be released) and returns
+ * a library-owned descriptor in *out.  D must be 32, 64 or 128. */
+int gla_rope_create(int T, int Hh, int W, int D, double theta, int t0, int y0, int x0,
+                    void* stream, gla_rope_tables** out);
+
+/* Releases a descriptor from gla_rope_create (NULL is a no-op).  The caller
+ * must make sure no enqueued gla_forward still reads it. */
+int gla_rope_destroy(gla_rope_tables* tables);
+
+/* ---------------------------------------------------------------------
+ * Forward pass.
+ */
+
+/* Bytes of device workspace gla_forward_ws needs for this shape (per-chunk
+ * partial states, the reduced state and the normaliser).  0 for N*B*H == 0. */
+size_t gla_workspace_bytes(int B, int N, int H, int D);
+
+/* Runs the mixer: out = o as defined above, bf16, round-to-nearest-even.
+ * rope == NULL switches RoPE off (identical to all angles being zero).
+ * Uses a library-owned workspace cached per (device, stream); growing it
+ * calls hipMalloc, which may synchronise.  Calls that share one stream are
+ * ordered by it; do not run two calls on the same stream from two host
+ * threads at once.  B*N*H == 0 is a no-op that returns GLA_OK. */
+int gla_forward(const void* q, const void* k, const void* v, const void* g,
+                const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                void* stream);
+
+/* Same as gla_forward with a caller-owned device workspace (>= the size
+ * gla_workspace_bytes returns, 256-byte aligned).  The workspace must not be
+ * used by other work while this call's kernels run.  Never allocates. */
+int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
+                   const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Argument validation of gla_forward alone: returns the status gla_forward
+ * would return before touching the GPU (GLA_OK if the arguments are valid).
+ * Makes no HIP call, so it runs on hosts without a GPU. */
+int gla_forward_check(const void* q, const void* k, const void* v, const void* g,
+                      const gla_rope_tables* rope, const void* out, int B, int N, int H, int D);
+
+/* The two halves of gla_forward_ws, for callers that schedule them apart
+ * (timing each half, or exchanging the state between them).  gla_state_ws
+ * reads k and v and leaves the reduced state of every head in `workspace`;
+ * gla_output_ws reads q and g and that state and writes out.  Calling both
+ * in order on one stream with one workspace equals gla_forward_ws.  The
+ * workspace contents between the two calls are private to the library. */
+int gla_state_ws(const void* k, const void* v, const gla_rope_tables* rope,
+                 int B, int N, int H, int D, void* workspace, size_t workspace_bytes,
+                 void* stream);
+int gla_output_ws(const void* q, const void* g, const gla_rope_tables* rope, void* out,
+                  int B, int N, int H, int D, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* The state half of the pass: S (fp32 [B, H, D, D], S[d][e]) and z (fp32
+ * [B, H, D]) into caller device buffers (16-byte aligned, not overlapping
+ * k or v), with the same kernels and reduction order gla_forward uses.
+ * k, v, rope as for gla_forward.  Uses the library-owned workspace. */
+int gla_state(const void* k, const void* v, const gla_rope_tables* rope, float* S, float* z,
+              int B, int N, int H, int D, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H_ */

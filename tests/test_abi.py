@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gla.h declares, validates arguments before any HIP call, and builds
+RoPE tables that agree with the oracle's fp64 rotation angles."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gated_linear_attention_forward_amd as gla
+import oracle
+from gated_linear_attention_forward_amd import gla as glamod
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = gla.load_library()
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gla.h but not exported"
+    assert set(names) == set(gla.EXPORTS)
+
+
+def test_strerror_covers_codes():
+    for code in range(0, -10, -1):
+        s = gla.gla_strerror(code)
+        assert s and s != "unknown status"
+    assert gla.gla_strerror(17) == "unknown status"
+
+
+A = 1 << 20  # fake, 16-byte aligned "device" addresses: validation never dereferences them
+
+
+def check(q=A, k=2 * A, v=3 * A, g=4 * A, rope=None, out=5 * A, B=1, N=64, H=2, D=128):
+    return gla.gla_forward_check(q, k, v, g, rope, out, B, N, H, D)
+
+
+def test_valid_arguments_pass_validation():
+    assert check() == 0
+    assert check(D=32) == 0 and check(D=64) == 0
+
+
+@pytest.mark.parametrize("D", [0, 16, 48, 96, 127, 256])
+def test_bad_head_dim(D):
+    assert check(D=D) == glamod.GLA_ERR_DIM
+
+
+def test_negative_and_oversized_shapes():
+    assert check(B=-1) == glamod.GLA_ERR_DIM
+    assert check(N=-5) == glamod.GLA_ERR_DIM
+    assert check(H=-2) == glamod.GLA_ERR_DIM
+    assert check(B=2, H=40000) == glamod.GLA_ERR_DIM  # B*H beyond the grid limit
+
+
+def test_empty_calls_are_noops():
+    assert check(N=0) == 0
+    assert check(B=0) == 0
+    assert check(H=0, q=0, k=0) == 0  # nothing to touch: pointers are not needed
+
+
+def test_null_and_alignment():
+    assert check(q=0) == glamod.GLA_ERR_NULL
+    assert check(out=0) == glamod.GLA_ERR_NULL
+    assert check(v=3 * A + 8) == glamod.GLA_ERR_ALIGN
+    assert check(out=5 * A + 2) == glamod.GLA_ERR_ALIGN
+
+
+def test_alias_detection():
+    nbytes = 1 * 64 * 2 * 128 * 2
+    assert check(out=A) == glamod.GLA_ERR_ALIAS
+    assert check(out=4 * A + nbytes - 16) == glamod.GLA_ERR_ALIAS
+    assert check(out=4 * A + nbytes) == 0
+
+
+def _host_rope(T, Hh, W, D, cs=A):
+    r = glamod.gla_rope_tables()
+    r.T, r.Hh, r.W, r.D = T, Hh, W, D
+    py = D // 6
+    r.Pt, r.Py, r.Px = D // 2 - 2 * py, py, py
+    r.theta = 1e4
+    r.cs = cs
+    r.cs_floats = gla.gla_rope_table_floats(T, Hh, W, D)
+    r.device = 0
+    return ctypes.pointer(r)
+
+
+def test_rope_mismatch_rejected():
+    assert check(N=64, rope=_host_rope(4, 4, 4, 128)) == 0
+    assert check(N=64, rope=_host_rope(4, 4, 5, 128)) == glamod.GLA_ERR_ROPE
+    assert check(N=64, D=64, rope=_host_rope(4, 4, 4, 128)) == glamod.GLA_ERR_ROPE
+    assert check(N=64, rope=_host_rope(4, 4, 4, 128, cs=0)) == glamod.GLA_ERR_NULL
+
+
+def test_workspace_size_formula():
+    # partials (C chunks x (D*D + D) fp32) + bf16 state + fp32 z, each 256-byte aligned
+    for (B, N, H, D) in ((1, 256, 2, 32), (2, 22000, 20, 128), (1, 159280, 20, 128)):
+        ws = gla.gla_workspace_bytes(B, N, H, D)
+        bh = B * H
+        assert ws >= bh * (D * D + D) * 4 + bh * D * D * 2 + bh * D * 4
+        assert ws % 256 == 0
+    assert gla.gla_workspace_bytes(0, 10, 2, 128) == 0
+    assert gla.gla_workspace_bytes(1, 10, 2, 100) == 0
+
+
+@pytest.mark.parametrize("D,grid,off", [(32, (4, 8, 8), (0, 0, 0)), (64, (3, 5, 7), (1, 2, 3)),
+                                        (128, (25, 22, 40), (0, 0, 0)),
+                                        (128, (181, 22, 40), (5, -3, 7))])
+def test_rope_table_matches_oracle_angles(D, grid, off):
+    """Every (cos, sin) entry equals the oracle's fp64 angle's cos/sin within 1e-6."""
+    T, Hh, W = grid
+    cs = gla.gla_rope_fill_host(T, Hh, W, D, 1e4, *off).astype(np.float64)
+    pt, py, px = oracle.axis_split(D)
+    assert cs.size == 2 * (T * pt + Hh * py + W * px)
+    at = 0
+    for axis, (n, pa, first) in enumerate(((T, pt, 0), (Hh, py, pt), (W, px, pt + py))):
+        for pos in range(n):
+            idx = [0, 0, 0]
+            idx[axis] = pos + off[axis]
+            ang = np.array([oracle.angle(D, 1e4, first + j, *idx) for j in range(pa)])
+            got = cs[at:at + 2 * pa]
+            assert np.max(np.abs(got[0::2] - np.cos(ang))) <= 1e-6
+            assert np.max(np.abs(got[1::2] - np.sin(ang))) <= 1e-6
+            at += 2 * pa
+    assert at == cs.size
+
+
+def test_rope_fill_rejects_bad_args():
+    with pytest.raises(gla.GlaError):
+        gla.gla_rope_fill_host(0, 1, 1, 128)
+    with pytest.raises(gla.GlaError):
+        gla.gla_rope_fill_host(2, 2, 2, 127)
