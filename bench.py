@@ -8,8 +8,8 @@ torch's current stream with inputs already resident in HBM.
 Prints ONE JSON line.  `value` is tokens/s per layer (B*N tokens per step).
 `roofline` reports the output kernel (the largest byte stream: q, g read and
 out written, 6*D bytes per (token, head)) from HIP events recorded around it
-in every timed step.  `cpu_baseline` times the fp64 oracle on a bounded
-sample of the same workload (a subset of heads, scaled to the whole layer).
+in every timed step.  `cpu_baseline` times the fp64 oracle on the same
+workload, repeated for about ten seconds of CPU work.
 """
 from __future__ import annotations
 
@@ -32,26 +32,41 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, q, k, v, g, target_heads=None):
-    """Times the oracle on `target_heads` (b=0) heads of the workload, scaled to B*H heads."""
+def cpu_baseline(w, q, k, v, g, min_seconds=10.0, max_reps=20):
+    """Times the fp64 oracle on the whole workload, repeated until about
+    `min_seconds` of CPU work (or `max_reps` passes) have run."""
     import oracle
-    threads = oracle.num_threads()
-    hs = min(w.H, target_heads or max(1, 2 * threads))
-    sl = [t[0:1, :, 0:hs].contiguous() for t in (q, k, v, g)]
     grid = oracle.Grid(w.T, w.Hh, w.W, w.theta)
+    threads = oracle.num_threads()
+    reps = 0
     t0 = time.perf_counter()
-    oracle.forward(*sl, grid)
-    dt = time.perf_counter() - t0
-    scale = (w.B * w.H) / hs
-    rate = (w.B * w.N) / (dt * scale)
+    while True:
+        oracle.forward(q, k, v, g, grid)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
+    per = dt / reps
     return {
-        "value": rate,
+        "value": (w.B * w.N) / per,
         "unit": "tokens/s",
-        "cores": min(threads, hs),
+        "cores": min(threads, w.B * w.H),
         "kind": "oracle",
-        "sample": f"{hs} of {w.B * w.H} (b, h) heads at full N={w.N}, {dt:.2f} s, "
-                  f"scaled x{scale:.2f} to the whole layer",
+        "sample": f"whole workload ({w.B * w.H} heads x N={w.N}), {reps} passes in {dt:.1f} s, "
+                  f"{per:.2f} s per pass",
     }
+
+
+def copy_calibration(dev, nbytes=1 << 30):
+    """One plain device-to-device copy of known size, so hardware byte counters
+    (FETCH_SIZE, WRITE_SIZE) read in the same run can be scaled to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"bench: calibration copy of {nbytes} bytes done")
+    del src, dst
 
 
 def main():
@@ -61,6 +76,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device copy first (for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -83,6 +100,8 @@ def main():
     rope = gla.gla_rope_create(w.T, w.Hh, w.W, w.D, w.theta)
     ws = gla.alloc_workspace(w.B, w.N, w.H, w.D, dev)
     stream = torch.cuda.current_stream(dev)
+    if args.calibrate_copy:
+        copy_calibration(dev)
 
     def step(ev=None):
         if ev is not None:

@@ -28,6 +28,16 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
 
+DivMagic make_div_magic(uint32_t d) {
+  DivMagic r{};
+  int l = 0;
+  while (l < 32 && (1ull << l) < d) ++l;  // l = ceil(log2 d)
+  r.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  r.s1 = l < 1 ? l : 1;
+  r.s2 = l > 1 ? l - 1 : 0;
+  return r;
+}
+
 // The state kernel wants a few blocks per compute unit in flight (256 CUs),
 // while every chunk adds one fp32 (D*D + D) partial per head.  The output
 // kernel reads only a bf16 copy of the state per block, so it takes more.
@@ -36,17 +46,18 @@ Plan make_plan(int B, int N, int H, int D) {
   p.B = B; p.N = N; p.H = H; p.D = D;
   p.BH = B * H;
   if (p.BH == 0 || N == 0) return p;
-  const int tt = state_tile_tokens(D);
-  const int tiles = ceil_div(N, tt);
-  int C = ceil_div(512, p.BH);
-  if (C > tiles) C = tiles;
+  // state chunks: whole 16-token tiles, about state_blocks(D) blocks in total
+  const int tiles = ceil_div(N, 16);
+  int C = state_blocks(D) / p.BH;
+  const int cmax = ceil_div(tiles, 4 * kStateMinTilesPerWave);
+  if (C > cmax) C = cmax;
   if (C > kMaxChunks) C = kMaxChunks;
   if (C < 1) C = 1;
-  p.L = ceil_div(tiles, C) * tt;
+  p.L = ceil_div(tiles, C) * 16;
   p.C = ceil_div(N, p.L);
 
   const int its = ceil_div(N, kOutputTileTokens);
-  int C2 = ceil_div(1024, p.BH);
+  int C2 = ceil_div(kOutputBlocks, p.BH);
   if (C2 > its) C2 = its;
   if (C2 < 1) C2 = 1;
   p.L2 = ceil_div(its, C2) * kOutputTileTokens;
@@ -56,7 +67,7 @@ Plan make_plan(int B, int N, int H, int D) {
   p.off_part = off;
   off = align_up(off + (size_t)p.BH * p.C * (size_t)(D * D + D) * sizeof(float), 256);
   p.off_sl = off;
-  off = align_up(off + (size_t)p.BH * D * D * sizeof(uint16_t), 256);
+  off = align_up(off + (size_t)p.BH * (D + 16) * D * sizeof(uint16_t), 256);
   p.off_z = off;
   off = align_up(off + (size_t)p.BH * D * sizeof(float), 256);
   p.ws_bytes = off;
@@ -66,7 +77,6 @@ Plan make_plan(int B, int N, int H, int D) {
 }  // namespace gla
 
 using gla::Plan;
-using gla::RopeArgs;
 
 namespace {
 
@@ -90,7 +100,8 @@ int check_shape(int B, int N, int H, int D, size_t* bytes) {
   const long long bh = (long long)B * H;
   if (bh > 65535) return GLA_ERR_DIM;  // heads go to grid.y
   const long long elems = (long long)B * N * H * D;
-  if (elems > (1LL << 40)) return GLA_ERR_DIM;
+  // each batch element's [N, H, D] slab is addressed with 31-bit byte offsets
+  if ((long long)N * H * D * 2 >= (1LL << 31)) return GLA_ERR_DIM;
   *bytes = (size_t)elems * 2;
   return GLA_OK;
 }
@@ -100,7 +111,8 @@ int check_rope(const gla_rope_tables* rope, int N, int D) {
   if (!rope->cs) return GLA_ERR_NULL;
   if (rope->D != D) return GLA_ERR_ROPE;
   if ((long long)rope->T * rope->Hh * rope->W != (long long)N) return GLA_ERR_ROPE;
-  if (rope->Pt + rope->Py + rope->Px != D / 2) return GLA_ERR_ROPE;
+  // the kernels fix the axis split for each D (as gla_rope_create builds it)
+  if (rope->Py != D / 6 || rope->Px != D / 6 || rope->Pt != D / 2 - 2 * (D / 6)) return GLA_ERR_ROPE;
   if (rope->cs_floats != gla_rope_table_floats(rope->T, rope->Hh, rope->W, D)) return GLA_ERR_ROPE;
   return GLA_OK;
 }
@@ -117,12 +129,30 @@ int check_tensors(std::initializer_list<const void*> ins, const void* out, size_
   return GLA_OK;
 }
 
-RopeArgs rope_args(const gla_rope_tables* r) {
-  RopeArgs a{};
-  if (!r) return a;
-  a.cs = reinterpret_cast<const float2*>(r->cs);
-  a.T = r->T; a.Hh = r->Hh; a.W = r->W;
-  a.Pt = r->Pt; a.Py = r->Py; a.Px = r->Px;
+// Kernel arguments of one call.  L is the block token range of the kernel the
+// arguments are for (it sets how many t-rows of the table a block stages).
+gla::KArgs kernel_args(const Plan& p, const gla_rope_tables* r, int L, void* ws) {
+  gla::KArgs a{};
+  a.N = p.N;
+  a.H = p.H;
+  a.slab_bytes = (uint32_t)((size_t)p.N * p.H * p.D * 2);
+  a.L = L;
+  a.C = p.C;
+  if (r) {
+    a.cs = reinterpret_cast<const float2*>(r->cs);
+    a.T = r->T; a.Hh = r->Hh; a.W = r->W;
+    a.Pt = r->Pt; a.Py = r->Py; a.Px = r->Px;
+    const uint32_t hw = (uint32_t)r->Hh * (uint32_t)r->W;
+    a.div_hw = gla::make_div_magic(hw);
+    a.div_w = gla::make_div_magic((uint32_t)r->W);
+    // a range of L consecutive tokens touches at most this many t-rows
+    long long nt = ((long long)L + hw - 2) / hw + 1;
+    a.nt = (int)(nt < r->T ? nt : r->T);
+  }
+  char* w = static_cast<char*>(ws);
+  a.part = reinterpret_cast<float*>(w + p.off_part);
+  a.sl = reinterpret_cast<uint16_t*>(w + p.off_sl);
+  a.zf = reinterpret_cast<float*>(w + p.off_z);
   return a;
 }
 
@@ -189,6 +219,25 @@ int check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? GLA_OK : GLA_ERR_LAUNCH; }
+
+int run_state(const Plan& p, const void* k, const void* v, const gla_rope_tables* rope, void* ws,
+              float* S, float* z, void* stream) {
+  gla::KArgs a = kernel_args(p, rope, p.L, ws);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.S_out = S;
+  a.z_out = z;
+  return status_of(gla::launch_state(p, a, static_cast<hipStream_t>(stream)));
+}
+
+int run_output(const Plan& p, const void* q, const void* g, const gla_rope_tables* rope,
+               void* out, void* ws, void* stream) {
+  gla::KArgs a = kernel_args(p, rope, p.L2, ws);
+  a.q = static_cast<const uint16_t*>(q);
+  a.g = static_cast<const uint16_t*>(g);
+  a.out = static_cast<uint16_t*>(out);
+  return status_of(gla::launch_output(p, a, static_cast<hipStream_t>(stream)));
+}
 
 }  // namespace
 
@@ -324,9 +373,7 @@ int gla_state_ws(const void* k, const void* v, const gla_rope_tables* rope, int 
   Plan p = gla::make_plan(B, N, H, D);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   if ((rc = rope_device_ok(rope))) return rc;
-  return status_of(gla::launch_state(p, static_cast<const uint16_t*>(k),
-                                     static_cast<const uint16_t*>(v), rope_args(rope), workspace,
-                                     nullptr, nullptr, static_cast<hipStream_t>(stream)));
+  return run_state(p, k, v, rope, workspace, nullptr, nullptr, stream);
 }
 
 int gla_output_ws(const void* q, const void* g, const gla_rope_tables* rope, void* out, int B,
@@ -340,10 +387,7 @@ int gla_output_ws(const void* q, const void* g, const gla_rope_tables* rope, voi
   Plan p = gla::make_plan(B, N, H, D);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   if ((rc = rope_device_ok(rope))) return rc;
-  return status_of(gla::launch_output(p, static_cast<const uint16_t*>(q),
-                                      static_cast<const uint16_t*>(g), rope_args(rope), workspace,
-                                      static_cast<uint16_t*>(out),
-                                      static_cast<hipStream_t>(stream)));
+  return run_output(p, q, g, rope, out, workspace, stream);
 }
 
 int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
@@ -355,15 +399,9 @@ int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
   Plan p = gla::make_plan(B, N, H, D);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   if ((rc = rope_device_ok(rope))) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  RopeArgs ra = rope_args(rope);
-  rc = status_of(gla::launch_state(p, static_cast<const uint16_t*>(k),
-                                   static_cast<const uint16_t*>(v), ra, workspace, nullptr,
-                                   nullptr, s));
+  rc = run_state(p, k, v, rope, workspace, nullptr, nullptr, stream);
   if (rc) return rc;
-  return status_of(gla::launch_output(p, static_cast<const uint16_t*>(q),
-                                      static_cast<const uint16_t*>(g), ra, workspace,
-                                      static_cast<uint16_t*>(out), s));
+  return run_output(p, q, g, rope, out, workspace, stream);
 }
 
 int gla_forward(const void* q, const void* k, const void* v, const void* g,
@@ -385,8 +423,12 @@ int gla_state(const void* k, const void* v, const gla_rope_tables* rope, float* 
   if (rc) return rc;
   if ((rc = check_rope(rope, N, D))) return rc;
   if ((long long)B * H == 0) return GLA_OK;
-  if (!k || !v || !S || !z) return GLA_ERR_NULL;
-  if (!aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(z)) return GLA_ERR_ALIGN;
+  if (!S || !z) return GLA_ERR_NULL;
+  if (!aligned16(S) || !aligned16(z)) return GLA_ERR_ALIGN;
+  if (N > 0) {
+    if (!k || !v) return GLA_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v)) return GLA_ERR_ALIGN;
+  }
   const size_t sbytes = (size_t)B * H * D * D * sizeof(float);
   const size_t zbytes = (size_t)B * H * D * sizeof(float);
   if (bytes && (overlap2(S, sbytes, k, bytes) || overlap2(S, sbytes, v, bytes) ||
@@ -404,9 +446,7 @@ int gla_state(const void* k, const void* v, const gla_rope_tables* rope, float* 
   void* ws = nullptr;
   if ((rc = get_workspace(p.ws_bytes, stream, &ws))) return rc;
   if ((rc = rope_device_ok(rope))) return rc;
-  return status_of(gla::launch_state(p, static_cast<const uint16_t*>(k),
-                                     static_cast<const uint16_t*>(v), rope_args(rope), ws, S, z,
-                                     s));
+  return run_state(p, k, v, rope, ws, S, z, stream);
 }
 
 }  // extern "C"

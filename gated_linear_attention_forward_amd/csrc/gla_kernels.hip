@@ -10,14 +10,21 @@
 //   state kernel   each block reduces one chunk of one head's tokens into an
 //                  fp32 partial (S_c, z_c) on bf16 MFMA (32x32x16);
 //   reduce kernel  sums the chunk partials of a head in a fixed pairwise tree
-//                  and stores S as bf16 in the output kernel's operand layout;
+//                  and stores S (bf16) and z (as a bf16 hi/lo pair) in the
+//                  output kernel's operand layout;
 //   output kernel  streams q and g, contracts R phi(q) with the LDS-resident S
-//                  on bf16 MFMA (16x16x32), applies normaliser and gate, and
-//                  writes bf16 out.
-// All tensors are bf16 [B, N, H, D]; a head's D-vector of a token is 2D
-// contiguous bytes, consecutive tokens are H*D*2 bytes apart.
+//                  and phi(q) with z on bf16 MFMA (16x16x32), applies the
+//                  normaliser and the gate, and writes bf16 out.
+// All tensors are bf16 [B, N, H, D].  A head's D-vector of a token is 2D
+// contiguous bytes; consecutive tokens are H*D*2 bytes apart.  Global
+// traffic goes through buffer instructions with 32-bit offsets from each
+// batch element's slab; a lane whose token lies outside its block's range
+// uses an offset past the end of the buffer, which the hardware turns into
+// zero loads and dropped stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "gla_internal.h"
 
@@ -27,474 +34,667 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kEps = 1e-6f;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr uint32_t kOob = 0x80000000u;  // offset past every slab (slabs are < 2 GiB)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Round two floats to bf16 (nearest-even) and pack them, a in the low half.
+// ReLU of two bf16 in one dword: as int16 a bf16 is negative exactly when its
+// sign bit is set, so a packed signed max with 0 zeroes the negative halves
+// (and -0) and keeps the rest bit for bit.
+__device__ __forceinline__ uint32_t relu2(uint32_t w) {
+  s16x2 x = __builtin_bit_cast(s16x2, w);
+  x = __builtin_elementwise_max(x, (s16x2){0, 0});
+  return __builtin_bit_cast(uint32_t, x);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round two floats to bf16 (nearest-even) and pack them, a in the low half
+// (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  __bf16 x = (__bf16)a;
-  __bf16 y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  const bf16x2 y = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, y);
 }
 
-// (cos, sin) of rotation pair p for a token whose per-axis row offsets into
-// the factorised table are ot, oy, ox (each already minus its axis's first pair).
-__device__ __forceinline__ float2 rope_cs(const RopeArgs& r, int p, int ot, int oy, int ox) {
-  int idx = (p < r.Pt) ? ot + p : ((p < r.Pt + r.Py) ? oy + p : ox + p);
-  return r.cs[idx];
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, DivMagic d) {
+  uint32_t t = __umulhi(n, d.m);
+  return (t + ((n - t) >> d.s1)) >> d.s2;
 }
 
-__device__ __forceinline__ void rope_rows(const RopeArgs& r, unsigned n, int& ot, int& oy, int& ox) {
-  unsigned HW = (unsigned)(r.Hh * r.W);
-  unsigned t = n / HW;
-  unsigned rem = n - t * HW;
-  unsigned y = rem / (unsigned)r.W;
-  unsigned x = rem - y * (unsigned)r.W;
-  ot = (int)t * r.Pt;
-  oy = r.T * r.Pt + (int)y * r.Py - r.Pt;
-  ox = r.T * r.Pt + r.Hh * r.Py + (int)x * r.Px - r.Pt - r.Py;
+// Compile-time loop: calls f(std::integral_constant<int, i>) for i in [0, N).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<0, N>(f);
+}
+
+// Pairs per RoPE axis for head dimension D: y and x get floor(D/6) pairs each,
+// t the rest (the split the host-side table builder uses).
+template <int D>
+struct Axes {
+  static constexpr int Py = D / 6;
+  static constexpr int Px = D / 6;
+  static constexpr int Pt = D / 2 - 2 * (D / 6);
+};
+
+// Where a block reads its RoPE factors: the factorised table, either staged
+// in LDS (t-rows of the block's own token range plus the y and x tables) or
+// straight from global memory.
+struct TabView {
+  const float2* tab;
+  int tbase;   // first t-row present
+  int ntr;     // t-rows present
+  int t_last;  // last t of the block's tokens (positions past the range clamp to it)
+};
+
+// Copies the table rows a block needs into LDS.  Caller synchronises.
+template <int D>
+__device__ __forceinline__ TabView stage_table(const KArgs& a, float2* ltab, bool in_lds,
+                                               int n_begin, int n_end) {
+  using X = Axes<D>;
+  TabView tv;
+  const int t_first = (int)fast_div((uint32_t)n_begin, a.div_hw);
+  tv.t_last = (int)fast_div((uint32_t)(n_end - 1), a.div_hw);
+  if (in_lds) {
+    const int nt_blk = tv.t_last - t_first + 1;
+    const float2* src_t = a.cs + (size_t)t_first * X::Pt;
+    for (int i = threadIdx.x; i < nt_blk * X::Pt; i += 256) ltab[i] = src_t[i];
+    const float2* src_yx = a.cs + (size_t)a.T * X::Pt;
+    const int nyx = a.Hh * X::Py + a.W * X::Px;
+    for (int i = threadIdx.x; i < nyx; i += 256) ltab[a.nt * X::Pt + i] = src_yx[i];
+    tv.tab = ltab;
+    tv.tbase = t_first;
+    tv.ntr = a.nt;
+  } else {
+    tv.tab = a.cs;
+    tv.tbase = 0;
+    tv.ntr = a.T;
+  }
+  return tv;
+}
+
+// Per-axis row offsets (in pairs, each minus its axis's first pair index) of
+// grid position (t, y, x) in a TabView.
+struct RowOff {
+  int ot, oy, ox;
+};
+
+template <int D>
+__device__ __forceinline__ RowOff row_offsets(const KArgs& a, const TabView& tv, int t, int y,
+                                              int x) {
+  using X = Axes<D>;
+  RowOff r;
+  t = min(t, tv.t_last);
+  r.ot = (t - tv.tbase) * X::Pt;
+  r.oy = tv.ntr * X::Pt + y * X::Py - X::Pt;
+  r.ox = tv.ntr * X::Pt + a.Hh * X::Py + x * X::Px - X::Pt - X::Py;
+  return r;
+}
+
+// Grid position of token n (row-major t, y, x).
+__device__ __forceinline__ void grid_pos(const KArgs& a, uint32_t n, int& t, int& y, int& x) {
+  t = (int)fast_div(n, a.div_hw);
+  const uint32_t rem = n - (uint32_t)t * (uint32_t)(a.Hh * a.W);
+  y = (int)fast_div(rem, a.div_w);
+  x = (int)(rem - (uint32_t)y * (uint32_t)a.W);
+}
+
+// (cos, sin) of pair p, where p is known to lie in [PMIN, PMAX]: when that
+// range sits inside one axis block the table row is chosen at compile time,
+// otherwise by masks (no branches).
+template <int D, int PMIN, int PMAX>
+__device__ __forceinline__ float2 rope_factor(const TabView& tv, const RowOff& r, int p) {
+  using X = Axes<D>;
+  int base;
+  if constexpr (PMAX < X::Pt) {
+    base = r.ot;
+  } else if constexpr (PMIN >= X::Pt && PMAX < X::Pt + X::Py) {
+    base = r.oy;
+  } else if constexpr (PMIN >= X::Pt + X::Py) {
+    base = r.ox;
+  } else {
+    const int my = -(int)(p >= X::Pt && p < X::Pt + X::Py);
+    const int mx = -(int)(p >= X::Pt + X::Py);
+    base = r.ot + ((r.oy - r.ot) & my) + ((r.ox - r.ot) & mx);
+  }
+  return tv.tab[base + p];
+}
+
+// RoPE factors of the 4 pairs of one 16-byte chunk: chunk index c = 4 S + m
+// with S compile-time and m in [0, 3].
+template <int D, int S>
+__device__ __forceinline__ void rope_factors(const TabView& tv, const RowOff& ro, int m,
+                                             float2 (&cs)[4]) {
+  static_for<4>([&](auto U) {
+    constexpr int u = decltype(U)::value;
+    cs[u] = rope_factor<D, 16 * S + u, 16 * S + 12 + u>(tv, ro, 4 * (4 * S + m) + u);
+  });
+}
+
+// Rotates the 4 pairs of one 16-byte chunk (8 features, ReLU already
+// applied, as packed bf16) and returns them as packed bf16.
+__device__ __forceinline__ u32x4 rotate_chunk(const u32x4 fq, const float2 (&cs)[4]) {
+  u32x4 pk;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float a0 = bf_lo(fq[u]);
+    const float a1 = bf_hi(fq[u]);
+    pk[u] = pack_bf16(a0 * cs[u].x - a1 * cs[u].y, a0 * cs[u].y + a1 * cs[u].x);
+  }
+  return pk;
+}
+
+template <int D, int S>
+__device__ __forceinline__ u32x4 rope_chunk(const u32x4 fq, const TabView& tv, const RowOff& ro,
+                                            int m) {
+  float2 cs[4];
+  rope_factors<D, S>(tv, ro, m, cs);
+  return rotate_chunk(fq, cs);
 }
 
 // ---------------------------------------------------------------------------
 // State kernel.
 //
-// Block = 256 threads, one (chunk, head).  A tile holds TT = 8192/D tokens,
-// so every thread loads 4 tokens x 16 bytes of k and of v per tile (thread t
-// takes 16-byte chunk t % (D/8) of tokens 4*(t / (D/8)) + 0..3).  ReLU and
-// RoPE are applied in fp32 registers, z accumulates the unrotated ReLU
-// features, and R phi(k) (rounded to bf16) and v are written to LDS
-// transposed -- one row per feature, tokens contiguous -- because both MFMA
-// operands of S = sum_n rk_n v_n^T contract over tokens.  Rows are padded by
-// 16 bytes and the 16-byte token units XOR-swizzled by (256/D)*(row/16) mod 8,
-// which keeps both the transposed 8-byte writes and the 16-byte MFMA operand
-// reads free of LDS bank conflicts.  The next tile's global loads are issued
-// before the MFMA phase of the current one.
+// Block = 4 waves, one (chunk, head); the waves are independent until the
+// block's end.  Each wave owns a full D x D fp32 accumulator (for D = 128,
+// 256 accumulation registers per lane, one wave per SIMD) and streams the
+// 16-token tiles w, w + 4, w + 8, ... of its block's chunk.  In a tile, lane
+// l takes token l % 16 and the 16-byte chunks 4s + l/16 (s < D/32) of that
+// token's k and v (one grid position per lane and tile; half of the RoPE
+// pair slots resolve their table row at compile time).  ReLU and RoPE are
+// applied to k in fp32 registers, z accumulates the unrotated features, and
+// R phi(k) (bf16) and v are written to the wave's LDS tile in their natural
+// token-major layout.  The MFMA operands of S += sum_n rk_n v_n^T contract
+// over tokens, so they are read back with ds_read_b64_tr_b16: within each
+// 16-lane group, source lane a + 4r points at 4 features of token r and
+// destination lane 4a + b receives feature b of tokens 0..3; two such reads
+// give a lane the 8 tokens of one feature that v_mfma_f32_32x32x16_bf16
+// takes.  Row pitches are padded to 2D + 32 bytes so the four rows a 16-lane
+// group touches fall on distinct banks.
+//
+// The loop is software-pipelined: step i issues the MFMAs of tile i - 1,
+// whose operands were read from LDS in step i - 1, while it prepares tile i
+// (ReLU, RoPE, LDS staging into the other of two tile buffers, operand
+// reads); the global loads run PF tiles ahead in a register ring.  A tile
+// past the wave's last one loads zeros (offsets outside the buffer) and adds
+// exactly nothing.  At the end the four accumulators are added in wave
+// order through LDS.
 template <int D>
 struct StateCfg {
-  static constexpr int NC = D / 8;                 // 16-byte chunks per token vector
-  static constexpr int TT = 8192 / D;              // tokens per tile
-  static constexpr int ROWB = TT * 2 + 16;         // LDS row pitch, bytes
-  static constexpr int UW = 256 / D;               // swizzle step
-  static constexpr int RT = D / 32;                // 32x32 output tiles per dimension
-  static constexpr int KSPLIT = (RT * RT >= 4) ? 1 : 4 / (RT * RT);
-  static constexpr int WR = (RT >= 2) ? 2 : 1;     // wave grid over output tiles
-  static constexpr int WC = (RT >= 2) ? 2 : 1;
-  static constexpr int TR = RT / WR;               // output tiles per wave (rows, cols)
-  static constexpr int TC = RT / WC;
-  static constexpr int KSTEPS = TT / 16;
-  static constexpr int NG = 256 / NC;              // token groups of 4 per tile
-  static_assert(WR * WC * KSPLIT == 4, "four waves per block");
-  static_assert(TT / 8 >= 8, "swizzle needs >= 8 token units per row");
+  static constexpr int KS = D / 32;         // 16-byte chunks per lane and token
+  static constexpr int TW = 16;             // tokens per wave tile
+  static constexpr int RT = D / 32;         // 32x32 accumulator tiles per dimension
+  static constexpr int RP = 2 * D + 32;     // LDS row pitch, bytes
+  static constexpr int BUF_BYTES = 2 * TW * RP;      // k and v tiles
+  static constexpr int WAVE_BYTES = 2 * BUF_BYTES;   // double-buffered
+  static constexpr int TILE_BYTES = 4 * WAVE_BYTES;
+  static constexpr int PF = 2;              // tiles in flight per wave
+  // block-end reduction: 32x32 accumulator tiles added per round (each takes
+  // 4 KB per wave), followed by the four waves' z vectors
+  static constexpr int RED_FIT = (TILE_BYTES - 16 * D) / (4 * 4096);
+  static constexpr int RED_TILES = RED_FIT < 1 ? 1 : (RED_FIT > RT * RT ? RT * RT : RED_FIT);
+  static constexpr int ZW_OFF = 4 * RED_TILES * 4096;
+  static constexpr int LDS_BYTES = TILE_BYTES > ZW_OFF + 16 * D ? TILE_BYTES : ZW_OFF + 16 * D;
 };
 
-template <int D>
-__device__ __forceinline__ int lds_off(int row, int tok) {
-  using Cf = StateCfg<D>;
-  int f = (Cf::UW * (row >> 4)) & 7;
-  return row * Cf::ROWB + ((((tok >> 3) ^ f)) << 4) + ((tok & 7) << 1);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA operand of features [32 i, 32 i + 32) over the 16 tokens of a
+// token-major LDS tile (see the state kernel's description).
+__device__ __forceinline__ bf16x8 frag_tr(const unsigned char* tile, int pitch, int i, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int f = 32 * i + 16 * (g & 1) + 4 * (s & 3);
+  const int tok = 8 * (g >> 1) + (s >> 2);
+  const unsigned char* p0 = tile + tok * pitch + 2 * f;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * pitch));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 template <int D, bool ROPE>
-__global__ __launch_bounds__(256) void state_kernel(const uint16_t* __restrict__ k,
-                                                    const uint16_t* __restrict__ v, int N, int H,
-                                                    int L, int C, RopeArgs rope,
-                                                    float* __restrict__ part) {
+struct StateWave {
   using Cf = StateCfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k[D * Cf::ROWB];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v[D * Cf::ROWB];
-  __shared__ float zred[Cf::NG * D];
+  static constexpr int KS = Cf::KS;
+  const KArgs& a;
+  const TabView& tv;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t tokstride, headoff;
+  int n_begin, n_end, wave, nit, lane, m, col;
+  unsigned char* buf;  // this wave's two tile buffers
+  u32x4 kr[Cf::PF][KS], vr[Cf::PF][KS];
+  bf16x8 A[2][Cf::RT], Bv[2][Cf::RT];
+  float2 cs[KS][4];    // RoPE factors of the tile being prepared
+  float zacc[KS][8];
+  f32x16 acc[Cf::RT][Cf::RT];
+
+  __device__ __forceinline__ int token(int it) const {
+    return n_begin + Cf::TW * (wave + 4 * it) + col;
+  }
+
+  __device__ __forceinline__ void issue(int st, int it) {
+    const int n = token(it);
+    const uint32_t off = (it < nit && n < n_end) ? (uint32_t)n * tokstride + headoff : kOob;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      kr[st][s2] = load16(rk, off + 64u * s2);
+      vr[st][s2] = load16(rv, off + 64u * s2);
+    }
+  }
+
+  // LDS reads of tile `it`'s RoPE factors (they complete while the step
+  // issues its operand reads and MFMAs)
+  __device__ __forceinline__ void load_factors(int it) {
+    if (!ROPE) return;
+    int t, y, x;
+    grid_pos(a, (uint32_t)min(token(it), n_end - 1), t, y, x);
+    const RowOff ro = row_offsets<D>(a, tv, t, y, x);
+    static_for<KS>([&](auto S2) {
+      constexpr int s2 = decltype(S2)::value;
+      rope_factors<D, s2>(tv, ro, m, cs[s2]);
+    });
+  }
+
+  // ReLU, z and RoPE of tile `it` (ring slot ST), staged into tile buffer PB;
+  // then the loads of tile it + PF go into the freed ring slot
+  template <int ST, int PB>
+  __device__ __forceinline__ void stage(int it) {
+    unsigned char* ktile = buf + PB * Cf::BUF_BYTES;
+    unsigned char* vtile = ktile + Cf::TW * Cf::RP;
+    u32x4 rkw[KS];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      u32x4 fq;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        fq[u] = relu2(kr[ST][s2][u]);
+        zacc[s2][2 * u] += bf_lo(fq[u]);
+        zacc[s2][2 * u + 1] += bf_hi(fq[u]);
+      }
+      rkw[s2] = ROPE ? rotate_chunk(fq, cs[s2]) : fq;
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      *reinterpret_cast<u32x4*>(ktile + col * Cf::RP + 16 * (4 * s2 + m)) = rkw[s2];
+      *reinterpret_cast<u32x4*>(vtile + col * Cf::RP + 16 * (4 * s2 + m)) = vr[ST][s2];
+    }
+    issue(ST, it + Cf::PF);
+  }
+
+  // MFMA operands of the tile staged in buffer PB.  The LDS executes one
+  // wave's instructions in order, so these reads see that wave's staging
+  // writes of an earlier step without a wait; the compiler barrier keeps
+  // the program order.
+  template <int PB>
+  __device__ __forceinline__ void read_operands() {
+    asm volatile("" ::: "memory");
+    const unsigned char* ktile = buf + PB * Cf::BUF_BYTES;
+    const unsigned char* vtile = ktile + Cf::TW * Cf::RP;
+#pragma unroll
+    for (int i = 0; i < Cf::RT; ++i) A[PB][i] = frag_tr(ktile, Cf::RP, i, lane);
+#pragma unroll
+    for (int j = 0; j < Cf::RT; ++j) Bv[PB][j] = frag_tr(vtile, Cf::RP, j, lane);
+  }
+
+  template <int PB>
+  __device__ __forceinline__ void contract() {
+#pragma unroll
+    for (int i = 0; i < Cf::RT; ++i)
+#pragma unroll
+      for (int j = 0; j < Cf::RT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[PB][i], Bv[PB][j], acc[i][j], 0, 0, 0);
+  }
+
+  // step `it` (parity P = it % 2): factors of tile it, operands of tile
+  // it - 1, MFMAs of tile it - 2, staging of tile it
+  template <int P>
+  __device__ __forceinline__ void step(int it) {
+    load_factors(it);
+    read_operands<1 - P>();
+    contract<P>();
+    asm volatile("" ::: "memory");
+    stage<P, P>(it);
+  }
+
+  __device__ __forceinline__ void run() {
+#pragma unroll
+    for (int i = 0; i < Cf::RT; ++i)
+#pragma unroll
+      for (int j = 0; j < Cf::RT; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) zacc[s2][j] = 0.f;
+    static_assert(Cf::PF == 2, "the ring, the buffers and the operand sets alternate together");
+    issue(0, 0);
+    issue(1, 1);
+    load_factors(0);
+    stage<0, 0>(0);
+    load_factors(1);
+    read_operands<0>();
+    asm volatile("" ::: "memory");
+    stage<1, 1>(1);
+    // tile j is contracted in step j + 2; tiles past the wave's last are
+    // zero, so the loop runs whole pairs of steps up to step nit + 1
+    for (int it = 2; it < nit + 2; it += 2) {
+      step<0>(it);
+      step<1>(it + 1);
+    }
+  }
+};
+
+template <int D, bool ROPE, bool TLDS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void state_kernel(KArgs a) {
+  using Cf = StateCfg<D>;
+  constexpr int KS = Cf::KS;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float2* ltab = reinterpret_cast<float2*>(smem + Cf::LDS_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int m = lane >> 4;
+  const int col = lane & 15;
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
-  const int b = bh / H, h = bh - (bh / H) * H;
-  const int n_begin = c * L;
-  const int n_end = min(N, n_begin + L);
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int n_begin = c * a.L;
+  const int n_end = min(a.N, n_begin + a.L);
 
-  const size_t tok_stride = (size_t)H * D;
-  const size_t head_base = ((size_t)b * N * H + h) * D;
-  const uint16_t* kb = k + head_base;
-  const uint16_t* vb = v + head_base;
+  TabView tv{};
+  if (ROPE) tv = stage_table<D>(a, ltab, TLDS, n_begin, n_end);
+  __syncthreads();
 
-  const int c8 = tid % Cf::NC;     // 16-byte chunk of the token vector
-  const int grp = tid / Cf::NC;    // token group (4 tokens)
+  const size_t boff = (size_t)b * a.N * a.H * D;
+  const int ntile = (n_end - n_begin + Cf::TW - 1) / Cf::TW;
+  StateWave<D, ROPE> w{a,
+                       tv,
+                       make_rsrc(a.k + boff, a.slab_bytes),
+                       make_rsrc(a.v + boff, a.slab_bytes),
+                       (uint32_t)a.H * D * 2,
+                       (uint32_t)h * D * 2 + 16u * m,
+                       n_begin,
+                       n_end,
+                       wave,
+                       (ntile - wave + 3) / 4,
+                       lane,
+                       m,
+                       col,
+                       smem + wave * Cf::WAVE_BYTES};
+  w.run();
 
-  // MFMA work split
-  const int wk = wave % Cf::KSPLIT;
-  const int wt = wave / Cf::KSPLIT;
-  const int wr = wt / Cf::WC, wc = wt % Cf::WC;
+  // z of this wave: the 16 lanes of a lane group hold the same features
+#pragma unroll
+  for (int msk = 1; msk < 16; msk *= 2)
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w.zacc[s2][j] += __shfl_xor(w.zacc[s2][j], msk);
 
-  f32x16 acc[Cf::TR][Cf::TC];
+  __syncthreads();  // every wave is done with its tiles; they become scratch
+  float* red = reinterpret_cast<float*>(smem);
+  float* dst = a.part + ((size_t)bh * a.C + c) * (size_t)(D * D + D);
+  float* zw = reinterpret_cast<float*>(smem + Cf::ZW_OFF);
+  if (col == 0) {
 #pragma unroll
-  for (int a = 0; a < Cf::TR; ++a)
+    for (int s2 = 0; s2 < KS; ++s2)
 #pragma unroll
-    for (int bb = 0; bb < Cf::TC; ++bb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][bb][r] = 0.f;
-
-  float zacc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) zacc[j] = 0.f;
-
-  uint4 kr[4], vr[4];
-  auto load_tile = [&](int n0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int n = n0 + 4 * grp + i;
-      if (n < n_end) {
-        kr[i] = *reinterpret_cast<const uint4*>(kb + (size_t)n * tok_stride + 8 * c8);
-        vr[i] = *reinterpret_cast<const uint4*>(vb + (size_t)n * tok_stride + 8 * c8);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  if (n_begin < n_end) load_tile(n_begin);
-
-  for (int n0 = n_begin; n0 < n_end; n0 += Cf::TT) {
-    // features of this thread's 4 tokens: rk[i][j] (bf16 bits), 8 features each
-    uint16_t rkb[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-      float f[8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        f[2 * u] = fmaxf(bf_lo(w[u]), 0.f);
-        f[2 * u + 1] = fmaxf(bf_hi(w[u]), 0.f);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) zacc[j] += f[j];
-      if (ROPE) {
-        int n = n0 + 4 * grp + i;
-        unsigned np = (unsigned)((n < n_end) ? n : n_begin);
-        int ot, oy, ox;
-        rope_rows(rope, np, ot, oy, ox);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float2 cs = rope_cs(rope, 4 * c8 + u, ot, oy, ox);
-          float a0 = f[2 * u], a1 = f[2 * u + 1];
-          f[2 * u] = a0 * cs.x - a1 * cs.y;
-          f[2 * u + 1] = a0 * cs.y + a1 * cs.x;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint32_t p = pack_bf16(f[2 * u], f[2 * u + 1]);
-        rkb[i][2 * u] = (uint16_t)(p & 0xffffu);
-        rkb[i][2 * u + 1] = (uint16_t)(p >> 16);
-      }
-    }
-
-    __syncthreads();  // previous tile's MFMA reads are done
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 8 * c8 + j;
-      const int off = lds_off<D>(row, 4 * grp);
-      uint2 wk2, wv2;
-      wk2.x = (uint32_t)rkb[0][j] | ((uint32_t)rkb[1][j] << 16);
-      wk2.y = (uint32_t)rkb[2][j] | ((uint32_t)rkb[3][j] << 16);
-      uint32_t vw[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vw[i][0] = vr[i].x; vw[i][1] = vr[i].y; vw[i][2] = vr[i].z; vw[i][3] = vr[i].w;
-      }
-      uint16_t v0 = (uint16_t)((j & 1) ? (vw[0][j >> 1] >> 16) : (vw[0][j >> 1] & 0xffffu));
-      uint16_t v1 = (uint16_t)((j & 1) ? (vw[1][j >> 1] >> 16) : (vw[1][j >> 1] & 0xffffu));
-      uint16_t v2 = (uint16_t)((j & 1) ? (vw[2][j >> 1] >> 16) : (vw[2][j >> 1] & 0xffffu));
-      uint16_t v3 = (uint16_t)((j & 1) ? (vw[3][j >> 1] >> 16) : (vw[3][j >> 1] & 0xffffu));
-      wv2.x = (uint32_t)v0 | ((uint32_t)v1 << 16);
-      wv2.y = (uint32_t)v2 | ((uint32_t)v3 << 16);
-      *reinterpret_cast<uint2*>(lds_k + off) = wk2;
-      *reinterpret_cast<uint2*>(lds_v + off) = wv2;
-    }
-
-    if (n0 + Cf::TT < n_end) load_tile(n0 + Cf::TT);
-    __syncthreads();
-
-#pragma unroll
-    for (int ks = wk; ks < Cf::KSTEPS; ks += Cf::KSPLIT) {
-      const int tok = 16 * ks + 8 * (lane >> 5);
-      bf16x8 A[Cf::TR], Bv[Cf::TC];
-#pragma unroll
-      for (int a = 0; a < Cf::TR; ++a) {
-        int row = 32 * (wr * Cf::TR + a) + (lane & 31);
-        A[a] = *reinterpret_cast<const bf16x8*>(lds_k + lds_off<D>(row, tok));
-      }
-#pragma unroll
-      for (int bb = 0; bb < Cf::TC; ++bb) {
-        int row = 32 * (wc * Cf::TC + bb) + (lane & 31);
-        Bv[bb] = *reinterpret_cast<const bf16x8*>(lds_v + lds_off<D>(row, tok));
-      }
-#pragma unroll
-      for (int a = 0; a < Cf::TR; ++a)
-#pragma unroll
-        for (int bb = 0; bb < Cf::TC; ++bb)
-          acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a], Bv[bb], acc[a][bb], 0, 0, 0);
-    }
+      for (int j = 0; j < 8; ++j) zw[wave * D + 8 * (4 * s2 + m) + j] = w.zacc[s2][j];
   }
+  __syncthreads();
+  if (tid < D) dst[D * D + tid] = ((zw[tid] + zw[D + tid]) + zw[2 * D + tid]) + zw[3 * D + tid];
+  __syncthreads();
 
-  // z partial: sum the token groups in a fixed order
+  // S: add the four waves' accumulators, RED_TILES 32x32 tiles per round
+  constexpr int NT = Cf::RT * Cf::RT;
+  constexpr int WSTRIDE = Cf::RED_TILES * 1024;  // floats per wave per round
 #pragma unroll
-  for (int j = 0; j < 8; ++j) zred[grp * D + 8 * c8 + j] = zacc[j];
-
-  float* dst = part + ((size_t)bh * C + c) * (size_t)(D * D + D);
-  if (Cf::KSPLIT == 1) {
+  for (int t0 = 0; t0 < NT; t0 += Cf::RED_TILES) {
 #pragma unroll
-    for (int a = 0; a < Cf::TR; ++a)
+    for (int q = 0; q < Cf::RED_TILES; ++q) {
+      if (t0 + q < NT) {
+        const int ti = (t0 + q) / Cf::RT, tj = (t0 + q) % Cf::RT;
 #pragma unroll
-      for (int bb = 0; bb < Cf::TC; ++bb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int d = 32 * (wr * Cf::TR + a) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          int e = 32 * (wc * Cf::TC + bb) + (lane & 31);
-          dst[d * D + e] = acc[a][bb][r];
-        }
-    __syncthreads();
-  } else {
-    // the waves split the token steps of one 32x32 tile; add their results in wave order
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(lds_k);  // 4 waves x 16 x 64 floats = 16 KB
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[0][0][r];
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = red[r * 64 + lane];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) s += red[(w * 16 + r) * 64 + lane];
-        int d = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        int e = lane & 31;
-        dst[d * D + e] = s;
+        for (int r = 0; r < 16; ++r)
+          red[wave * WSTRIDE + (q * 16 + r) * 64 + lane] = w.acc[ti][tj][r];
       }
     }
-  }
-  if (tid < D) {
-    float s = 0.f;
-    for (int gi = 0; gi < Cf::NG; ++gi) s += zred[gi * D + tid];
-    dst[D * D + tid] = s;
+    __syncthreads();
+    for (int idx = tid; idx < WSTRIDE; idx += 256) {
+      const int q = idx / 1024, r = (idx / 64) % 16, l = idx % 64;
+      if (t0 + q < NT) {
+        const int ti = (t0 + q) / Cf::RT, tj = (t0 + q) % Cf::RT;
+        const float sum = ((red[idx] + red[WSTRIDE + idx]) + red[2 * WSTRIDE + idx]) +
+                          red[3 * WSTRIDE + idx];
+        const int d = 32 * ti + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        const int e = 32 * tj + (l & 31);
+        dst[d * D + e] = sum;
+      }
+    }
+    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
 // Reduce kernel: per head, S = sum_c S_c and z = sum_c z_c over the C chunk
-// partials in a fixed pairwise tree (a binary counter merges equal-sized
-// partial sums, older operand on the left), so the result does not depend on
-// which block finished first.  S is stored as bf16 rows in the output
-// kernel's operand order (row R(e) holds S[0..D)[e]); optional fp32 copies of
+// partials.  Each thread loads the P (a power of two >= C, at most 64) chunk
+// values of its element at once -- loads past the head's C partials fall
+// outside the buffer and read as zero -- and adds them in a fixed pairwise
+// tree, so the result does not depend on which block finished first.  More
+// than 64 chunks are summed 64 at a time, groups in order.
+// Outputs per head, in the output kernel's operand layout (D + 16 rows of D
+// bf16): row R(e) holds S[0..D)[e]; row D holds bf16(z), row D + 1 holds
+// bf16(z - bf16(z)); rows D + 2 .. D + 15 are zero.  Optional fp32 copies of
 // S and z go to the caller.
 
-constexpr int kTreeLevels = 9;  // handles C <= 256 = kMaxChunks
-
-struct TreeSum {
-  float st[kTreeLevels];
-  int cnt;
-  __device__ __forceinline__ TreeSum() : cnt(0) {
-#pragma unroll
-    for (int l = 0; l < kTreeLevels; ++l) st[l] = 0.f;
-  }
-  __device__ __forceinline__ void push(float x) {
-#pragma unroll
-    for (int l = 0; l < kTreeLevels; ++l) {
-      if ((cnt >> l) & 1) {
-        x = st[l] + x;
-      } else {
-        st[l] = x;
-        break;
-      }
-    }
-    ++cnt;
-  }
-  __device__ __forceinline__ float total() const {
-    float s = 0.f;
-    bool any = false;
-#pragma unroll
-    for (int l = 0; l < kTreeLevels; ++l) {
-      if ((cnt >> l) & 1) {
-        s = any ? st[l] + s : st[l];
-        any = true;
-      }
-    }
-    return s;
-  }
-};
-
 // Output-kernel operand row of value column e (see output_kernel).
-template <int D>
 __device__ __forceinline__ int out_row_of(int e) {
-  int j = 2 * (e >> 5) + ((e & 7) >> 2);
-  int r = 4 * ((e & 31) >> 3) + (e & 3);
+  const int j = 2 * (e >> 5) + ((e & 7) >> 2);
+  const int r = 4 * ((e & 31) >> 3) + (e & 3);
   return 16 * j + r;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, int C,
-                                                     uint16_t* __restrict__ sl,
-                                                     float* __restrict__ zf,
-                                                     float* __restrict__ S_out,
-                                                     float* __restrict__ z_out) {
+template <int P, int R>
+__device__ __forceinline__ void tree_sum(__amdgpu_buffer_rsrc_t rs, uint32_t off0, uint32_t cstride,
+                                         uint32_t rstride, int C, float (&out)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) out[r] = 0.f;
+  for (int g0 = 0; g0 < C; g0 += P) {
+    float x[R][P];
+#pragma unroll
+    for (int cc = 0; cc < P; ++cc)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        x[r][cc] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rs, off0 + (uint32_t)(g0 + cc) * cstride + r * rstride, 0, 0));
+#pragma unroll
+    for (int w = P / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int cc = 0; cc < w; ++cc)
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r][cc] = x[r][2 * cc] + x[r][2 * cc + 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) out[r] = (g0 == 0) ? x[r][0] : out[r] + x[r][0];
+  }
+}
+
+template <int D, int P>
+__global__ __launch_bounds__(256) void reduce_kernel(KArgs a) {
+  constexpr int NS = D * D / 2;  // threads on S: column e, feature pair (2i, 2i + 1)
   const int bh = blockIdx.y;
   const int gid = blockIdx.x * 256 + threadIdx.x;
-  const size_t pstride = (size_t)(D * D + D);
-  const float* pb = part + (size_t)bh * C * pstride;
-  constexpr int NS = D * D / 8;
+  const uint32_t pstride = (uint32_t)(D * D + D) * 4u;  // bytes per chunk partial
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(a.part + (size_t)bh * a.C * (D * D + D), (uint32_t)a.C * pstride);
+  uint16_t* slh = a.sl + (size_t)bh * (D + 16) * D;
   if (gid < NS) {
     const int e = gid % D;
-    const int d8 = gid / D;
-    TreeSum ts[8];
-    for (int cc = 0; cc < C; ++cc) {
-      const float* src = pb + cc * pstride + (size_t)(8 * d8) * D + e;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ts[j].push(src[j * D]);
-    }
-    float s[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s[j] = ts[j].total();
-    uint4 w;
-    w.x = pack_bf16(s[0], s[1]);
-    w.y = pack_bf16(s[2], s[3]);
-    w.z = pack_bf16(s[4], s[5]);
-    w.w = pack_bf16(s[6], s[7]);
-    *reinterpret_cast<uint4*>(sl + (size_t)bh * D * D + (size_t)out_row_of<D>(e) * D + 8 * d8) = w;
-    if (S_out) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) S_out[(size_t)bh * D * D + (size_t)(8 * d8 + j) * D + e] = s[j];
+    const int d = 2 * (gid / D);
+    float s[2];
+    tree_sum<P, 2>(rs, (uint32_t)(d * D + e) * 4u, pstride, (uint32_t)D * 4u, a.C, s);
+    *reinterpret_cast<uint32_t*>(slh + (size_t)out_row_of(e) * D + d) = pack_bf16(s[0], s[1]);
+    if (a.S_out) {
+      a.S_out[(size_t)bh * D * D + (size_t)d * D + e] = s[0];
+      a.S_out[(size_t)bh * D * D + (size_t)(d + 1) * D + e] = s[1];
     }
   } else if (gid < NS + D) {
     const int d = gid - NS;
-    TreeSum ts;
-    for (int cc = 0; cc < C; ++cc) ts.push(pb[cc * pstride + D * D + d]);
-    float s = ts.total();
-    zf[(size_t)bh * D + d] = s;
-    if (z_out) z_out[(size_t)bh * D + d] = s;
+    float s[1];
+    tree_sum<P, 1>(rs, (uint32_t)(D * D + d) * 4u, pstride, 0u, a.C, s);
+    a.zf[(size_t)bh * D + d] = s[0];
+    if (a.z_out) a.z_out[(size_t)bh * D + d] = s[0];
+    const __bf16 zh = (__bf16)s[0];
+    const __bf16 zl = (__bf16)(s[0] - (float)zh);
+    slh[(size_t)D * D + d] = __builtin_bit_cast(uint16_t, zh);
+    slh[(size_t)(D + 1) * D + d] = __builtin_bit_cast(uint16_t, zl);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) slh[(size_t)(D + r) * D + d] = 0;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Output kernel.
 //
-// Block = 256 threads (4 waves), one (token chunk, head).  The head's S (bf16,
-// D x D) is staged in LDS once per block with rows padded by 16 bytes.  Each
-// wave handles 16 tokens per step as the B operand of v_mfma_f32_16x16x32_bf16
-// computing num^T = S^T (R phi(q))^T: lane l holds token l % 16 and, for
-// k-step s, the 16-byte chunk 4s + l/16 of that token's q -- a direct 16-byte
-// global load, no LDS round trip.  The accumulator then holds, for the same
-// token, value columns E(j, m, i) = 32*(j/2) + 8m + 4*(j%2) + i (m = l/16),
-// which for each pair of m-blocks is again the 16-byte chunk 4t + m: g is read
-// and out written with the same 16-byte per-lane pattern as q.  The
-// denominator phi(q).z (unrotated features) is a per-lane partial dot product
-// summed over the four lanes of a token with two xor shuffles.
-template <int D, bool ROPE>
-__global__ __launch_bounds__(256) void output_kernel(const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ g,
-                                                     const uint16_t* __restrict__ sl,
-                                                     const float* __restrict__ zf, int N, int H,
-                                                     int L2, RopeArgs rope,
-                                                     uint16_t* __restrict__ out) {
+// Block = 256 threads (4 waves), one (token range, head).  The head's S (bf16,
+// D x D) and the two z rows are staged in LDS once per block with rows padded
+// by 16 bytes.  Each wave handles 16 tokens per step as the B operand of
+// v_mfma_f32_16x16x32_bf16 computing num^T = S^T (R phi(q))^T: lane l holds
+// token l % 16 and, for k-step s, the 16-byte chunk 4s + l/16 of that token's
+// q -- a direct 16-byte global load, no LDS round trip.  The accumulator then
+// holds, for the same token, value columns E(j, m, i) = 32*(j/2) + 8m +
+// 4*(j%2) + i (m = l/16), which for each pair of 16-row blocks is again the
+// 16-byte chunk 4t + m: g is read and out written with the same 16-byte
+// per-lane pattern as q.  The denominator phi(q).z uses the unrotated
+// features, which are exact in bf16: one more 16-row block holds z as a bf16
+// hi/lo pair, so phi(q).z comes out of the same MFMA pipe in fp32.
+template <int D, bool ROPE, bool TLDS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void output_kernel(KArgs a) {
   constexpr int KS = D / 32;       // k-steps of 32 features
   constexpr int MB = D / 16;       // 16-row blocks of S^T
   constexpr int PITCH = D * 2 + 16;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_s[D * PITCH];
+  constexpr int ROWS = D + 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* sS = smem;
+  float2* ltab = reinterpret_cast<float2*>(smem + ROWS * PITCH);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int m = lane >> 4;
   const int col = lane & 15;
   const int bh = blockIdx.y;
-  const int b = bh / H, h = bh - (bh / H) * H;
-  const int n_begin = blockIdx.x * L2;
-  const int n_end = min(N, n_begin + L2);
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int n_begin = blockIdx.x * a.L;
+  const int n_end = min(a.N, n_begin + a.L);
 
-  // stage S^T rows
-  const uint4* src = reinterpret_cast<const uint4*>(sl + (size_t)bh * D * D);
-  for (int i = tid; i < D * D / 8; i += 256) {
-    int row = i / (D / 8), u = i % (D / 8);
-    *reinterpret_cast<uint4*>(lds_s + row * PITCH + 16 * u) = src[i];
+  // stage S^T rows and the z rows
+  const uint4* src = reinterpret_cast<const uint4*>(a.sl + (size_t)bh * ROWS * D);
+  for (int i = tid; i < ROWS * D / 8; i += 256) {
+    const int row = i / (D / 8), u = i % (D / 8);
+    *reinterpret_cast<uint4*>(sS + row * PITCH + 16 * u) = src[i];
   }
-  float zr[KS][8];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const float4* zp = reinterpret_cast<const float4*>(zf + (size_t)bh * D + 8 * (4 * s + m));
-    float4 z0 = zp[0], z1 = zp[1];
-    zr[s][0] = z0.x; zr[s][1] = z0.y; zr[s][2] = z0.z; zr[s][3] = z0.w;
-    zr[s][4] = z1.x; zr[s][5] = z1.y; zr[s][6] = z1.z; zr[s][7] = z1.w;
-  }
+  TabView tv{};
+  if (ROPE) tv = stage_table<D>(a, ltab, TLDS, n_begin, n_end);
   __syncthreads();
 
-  const size_t tok_stride = (size_t)H * D;
-  const size_t head_base = ((size_t)b * N * H + h) * D;
+  const size_t boff = (size_t)b * a.N * a.H * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + boff, a.slab_bytes);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + boff, a.slab_bytes);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out + boff, a.slab_bytes);
+  const uint32_t tokstride = (uint32_t)a.H * D * 2;
+  const uint32_t headoff = (uint32_t)h * D * 2 + 16u * m;
 
-  for (int base = n_begin + 16 * wave; base < n_end; base += 64) {
+  auto offset_of = [&](int base) -> uint32_t {
     const int n = base + col;
-    const bool valid = n < n_end;
-    uint4 qv[KS], gv[KS];
+    return (n < n_end) ? (uint32_t)n * tokstride + headoff : kOob;
+  };
+  auto load_qg = [&](int base, u32x4 (&qv)[KS], u32x4 (&gv)[KS]) {
+    const uint32_t toff = offset_of(base);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      size_t off = head_base + (size_t)n * tok_stride + 8 * (4 * s + m);
-      if (valid) {
-        qv[s] = *reinterpret_cast<const uint4*>(q + off);
-        gv[s] = *reinterpret_cast<const uint4*>(g + off);
-      } else {
-        qv[s] = make_uint4(0, 0, 0, 0);
-        gv[s] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    int ot = 0, oy = 0, ox = 0;
-    if (ROPE) rope_rows(rope, (unsigned)(valid ? n : n_begin), ot, oy, ox);
+    for (int s2 = 0; s2 < KS; ++s2) qv[s2] = load16(rq, toff + 64u * s2);
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) gv[s2] = load16(rg, toff + 64u * s2);
+  };
 
-    float den = 0.f;
-    bf16x8 Bq[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint32_t w[4] = {qv[s].x, qv[s].y, qv[s].z, qv[s].w};
-      uint32_t pk[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float a0 = fmaxf(bf_lo(w[u]), 0.f);
-        float a1 = fmaxf(bf_hi(w[u]), 0.f);
-        den += a0 * zr[s][2 * u] + a1 * zr[s][2 * u + 1];
-        if (ROPE) {
-          float2 cs = rope_cs(rope, 4 * (4 * s + m) + u, ot, oy, ox);
-          float r0 = a0 * cs.x - a1 * cs.y;
-          float r1 = a0 * cs.y + a1 * cs.x;
-          a0 = r0;
-          a1 = r1;
-        }
-        pk[u] = pack_bf16(a0, a1);
-      }
-      uint4 pv = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      Bq[s] = __builtin_bit_cast(bf16x8, pv);
+  // one 16-token step of this wave: tokens base .. base + 15
+  auto step = [&](int base, const u32x4 (&qv)[KS], const u32x4 (&gv)[KS]) {
+    // keep the S fragments in LDS: reading them inside the loop costs LDS
+    // bandwidth but leaves registers for more waves in flight
+    asm volatile("" ::: "memory");
+    const uint32_t toff = offset_of(base);
+    RowOff rof{};
+    if (ROPE) {
+      int t, y, x;
+      grid_pos(a, (uint32_t)min(base + col, n_end - 1), t, y, x);
+      rof = row_offsets<D>(a, tv, t, y, x);
     }
+    bf16x8 Bd[KS], Bq[KS];
+    static_for<KS>([&](auto S2) {
+      constexpr int s2 = decltype(S2)::value;
+      u32x4 fq;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fq[u] = relu2(qv[s2][u]);
+      Bd[s2] = __builtin_bit_cast(bf16x8, fq);
+      Bq[s2] = __builtin_bit_cast(bf16x8, ROPE ? rope_chunk<D, s2>(fq, tv, rof, m) : fq);
+    });
 
+    f32x4 accd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const bf16x8 A = *reinterpret_cast<const bf16x8*>(sS + (D + col) * PITCH + 16 * (4 * s2 + m));
+      accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bd[s2], accd, 0, 0, 0);
+    }
     f32x4 acc[MB];
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
       acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        bf16x8 A = *reinterpret_cast<const bf16x8*>(lds_s + (16 * j + col) * PITCH +
-                                                    16 * (4 * s + m));
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bq[s], acc[j], 0, 0, 0);
+      for (int s2 = 0; s2 < KS; ++s2) {
+        const bf16x8 A =
+            *reinterpret_cast<const bf16x8*>(sS + (16 * j + col) * PITCH + 16 * (4 * s2 + m));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bq[s2], acc[j], 0, 0, 0);
       }
     }
 
-    den += __shfl_xor(den, 16);
-    den += __shfl_xor(den, 32);
-    const float inv = __builtin_amdgcn_rcpf(den + kEps);
+    // rows 0 and 1 of the z block (lanes 0..15) hold phi(q).z_hi and phi(q).z_lo
+    const float dpart = accd[0] + accd[1];
+    const float den = __shfl(dpart, col) + kEps;
 
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
-      uint32_t gw[4] = {gv[t].x, gv[t].y, gv[t].z, gv[t].w};
-      uint32_t ow[4];
+      u32x4 ow;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         float o2[2];
@@ -502,80 +702,125 @@ __global__ __launch_bounds__(256) void output_kernel(const uint16_t* __restrict_
         for (int hlf = 0; hlf < 2; ++hlf) {
           const int jj = 2 * u + hlf;            // element of the 16-byte chunk
           const int j = 2 * t + (jj >> 2);       // accumulator block
-          const int r = jj & 3;
-          float gval = hlf ? bf_hi(gw[u]) : bf_lo(gw[u]);
-          float sig = __builtin_amdgcn_rcpf(1.f + __expf(-gval));
-          o2[hlf] = acc[j][r] * inv * sig;
+          const float gval = hlf ? bf_hi(gv[t][u]) : bf_lo(gv[t][u]);
+          // sigmoid(g) / den = 1 / (den * (1 + exp(-g)))
+          const float e = __expf(-gval);
+          o2[hlf] = acc[j][jj & 3] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
         }
         ow[u] = pack_bf16(o2[0], o2[1]);
       }
-      if (valid) {
-        size_t off = head_base + (size_t)n * tok_stride + 8 * (4 * t + m);
-        *reinterpret_cast<uint4*>(out + off) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-      }
+      store16(ro, toff + 64u * t, ow);
     }
+  };
+
+  // two register sets: the next step's q and g are in flight during a step
+  u32x4 qa[KS], ga[KS], qb[KS], gb[KS];
+  int base = n_begin + 16 * wave;
+  if (base < n_end) load_qg(base, qa, ga);
+  for (; base < n_end; base += 128) {
+    load_qg(base + 64, qb, gb);
+    step(base, qa, ga);
+    if (base + 64 >= n_end) break;
+    load_qg(base + 128, qa, ga);
+    step(base + 64, qb, gb);
   }
 }
 
 template <int D>
-hipError_t launch_state_d(const Plan& p, const uint16_t* k, const uint16_t* v,
-                          const RopeArgs& rope, void* ws, float* S_out, float* z_out,
-                          hipStream_t stream) {
-  char* w = static_cast<char*>(ws);
-  float* part = reinterpret_cast<float*>(w + p.off_part);
-  uint16_t* sl = reinterpret_cast<uint16_t*>(w + p.off_sl);
-  float* zf = reinterpret_cast<float*>(w + p.off_z);
-  dim3 g1(p.C, p.BH);
-  if (rope.cs)
-    hipLaunchKernelGGL((state_kernel<D, true>), g1, dim3(256), 0, stream, k, v, p.N, p.H, p.L,
-                       p.C, rope, part);
-  else
-    hipLaunchKernelGGL((state_kernel<D, false>), g1, dim3(256), 0, stream, k, v, p.N, p.H, p.L,
-                       p.C, rope, part);
-  hipError_t e = hipGetLastError();
+constexpr int state_lds_bytes() {
+  return StateCfg<D>::LDS_BYTES;
+}
+template <int D>
+constexpr int output_lds_bytes() {
+  return (D + 16) * (D * 2 + 16);
+}
+
+int table_lds_bytes(const KArgs& a) {
+  return 8 * (a.nt * a.Pt + a.Hh * a.Py + a.W * a.Px);
+}
+
+
+template <int D, int P>
+void launch_reduce(const Plan& p, const KArgs& a, hipStream_t stream) {
+  const dim3 g2((D * D / 2 + D + 255) / 256, p.BH);
+  hipLaunchKernelGGL((reduce_kernel<D, P>), g2, dim3(256), 0, stream, a);
+}
+
+// Kernels that take more than 64 KB of dynamic LDS say so once per process.
+template <class K>
+hipError_t allow_lds(K kernel, size_t bytes) {
+  static size_t granted = 0;
+  if (bytes <= 65536 || bytes <= granted) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) granted = bytes;
+  return e;
+}
+
+template <int D, bool ROPE, bool TLDS>
+hipError_t launch_state_k(const Plan& p, const KArgs& a, size_t lds, hipStream_t stream) {
+  const dim3 g1(p.C, p.BH);
+  hipError_t e = allow_lds(state_kernel<D, ROPE, TLDS>, lds);
   if (e != hipSuccess) return e;
-  dim3 g2((D * D / 8 + D + 255) / 256, p.BH);
-  hipLaunchKernelGGL((reduce_kernel<D>), g2, dim3(256), 0, stream, part, p.C, sl, zf, S_out,
-                     z_out);
+  hipLaunchKernelGGL((state_kernel<D, ROPE, TLDS>), g1, dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_output_d(const Plan& p, const uint16_t* q, const uint16_t* g,
-                           const RopeArgs& rope, const void* ws, uint16_t* out,
-                           hipStream_t stream) {
-  const char* w = static_cast<const char*>(ws);
-  const uint16_t* sl = reinterpret_cast<const uint16_t*>(w + p.off_sl);
-  const float* zf = reinterpret_cast<const float*>(w + p.off_z);
-  dim3 g3(p.C2, p.BH);
-  if (rope.cs)
-    hipLaunchKernelGGL((output_kernel<D, true>), g3, dim3(256), 0, stream, q, g, sl, zf, p.N,
-                       p.H, p.L2, rope, out);
+hipError_t launch_state_d(const Plan& p, KArgs a, hipStream_t stream) {
+  const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;
+  const size_t lds = state_lds_bytes<D>() + (tl ? table_lds_bytes(a) : 0);
+  hipError_t e0;
+  if (!a.cs)
+    e0 = launch_state_k<D, false, false>(p, a, lds, stream);
+  else if (tl)
+    e0 = launch_state_k<D, true, true>(p, a, lds, stream);
   else
-    hipLaunchKernelGGL((output_kernel<D, false>), g3, dim3(256), 0, stream, q, g, sl, zf, p.N,
-                       p.H, p.L2, rope, out);
+    e0 = launch_state_k<D, true, false>(p, a, lds, stream);
+  if (e0 != hipSuccess) return e0;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.C <= 8)
+    launch_reduce<D, 8>(p, a, stream);
+  else if (p.C <= 16)
+    launch_reduce<D, 16>(p, a, stream);
+  else if (p.C <= 32)
+    launch_reduce<D, 32>(p, a, stream);
+  else
+    launch_reduce<D, 64>(p, a, stream);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream) {
+  const dim3 g3(p.C2, p.BH);
+  const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;
+  const size_t lds = output_lds_bytes<D>() + (tl ? table_lds_bytes(a) : 0);
+  if (!a.cs)
+    hipLaunchKernelGGL((output_kernel<D, false, false>), g3, dim3(256), lds, stream, a);
+  else if (tl)
+    hipLaunchKernelGGL((output_kernel<D, true, true>), g3, dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL((output_kernel<D, true, false>), g3, dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_state(const Plan& p, const uint16_t* k, const uint16_t* v, const RopeArgs& rope,
-                        void* ws, float* S_out, float* z_out, hipStream_t stream) {
+hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream) {
   switch (p.D) {
-    case 32: return launch_state_d<32>(p, k, v, rope, ws, S_out, z_out, stream);
-    case 64: return launch_state_d<64>(p, k, v, rope, ws, S_out, z_out, stream);
-    case 128: return launch_state_d<128>(p, k, v, rope, ws, S_out, z_out, stream);
+    case 32: return launch_state_d<32>(p, a, stream);
+    case 64: return launch_state_d<64>(p, a, stream);
+    case 128: return launch_state_d<128>(p, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_output(const Plan& p, const uint16_t* q, const uint16_t* g,
-                         const RopeArgs& rope, const void* ws, uint16_t* out,
-                         hipStream_t stream) {
+hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream) {
   switch (p.D) {
-    case 32: return launch_output_d<32>(p, q, g, rope, ws, out, stream);
-    case 64: return launch_output_d<64>(p, q, g, rope, ws, out, stream);
-    case 128: return launch_output_d<128>(p, q, g, rope, ws, out, stream);
+    case 32: return launch_output_d<32>(p, a, stream);
+    case 64: return launch_output_d<64>(p, a, stream);
+    case 128: return launch_output_d<128>(p, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -148,7 +148,8 @@ int gla_output_ws(const void* q, const void* g, const gla_rope_tables* rope, voi
 /* The state half of the pass: S (fp32 [B, H, D, D], S[d][e]) and z (fp32
  * [B, H, D]) into caller device buffers (16-byte aligned, not overlapping
  * k or v), with the same kernels and reduction order gla_forward uses.
- * k, v, rope as for gla_forward.  Uses the library-owned workspace. */
+ * k, v, rope as for gla_forward (k and v may be NULL when N == 0; S and z
+ * are then set to zero).  Uses the library-owned workspace. */
 int gla_state(const void* k, const void* v, const gla_rope_tables* rope, float* S, float* z,
               int B, int N, int H, int D, void* stream);
 
