@@ -50,8 +50,13 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
-__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+// Stores of the output stream carry the non-temporal hint (cache policy bit
+// nt): nothing reads them back, and without the hint their write-back lands
+// in the next pass's state kernel instead of this one.
+constexpr int kCpolNt = 2;
+
+__device__ __forceinline__ void store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNt);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -113,8 +118,9 @@ struct TabView {
   int t_last;  // last t of the block's tokens (positions past the range clamp to it)
 };
 
-// Copies the table rows a block needs into LDS.  Caller synchronises.
-template <int D>
+// Copies the table rows a block of NT threads needs into LDS.  Caller
+// synchronises.
+template <int D, int NT = 256>
 __device__ __forceinline__ TabView stage_table(const KArgs& a, float2* ltab, bool in_lds,
                                                int n_begin, int n_end) {
   using X = Axes<D>;
@@ -124,10 +130,10 @@ __device__ __forceinline__ TabView stage_table(const KArgs& a, float2* ltab, boo
   if (in_lds) {
     const int nt_blk = tv.t_last - t_first + 1;
     const float2* src_t = a.cs + (size_t)t_first * X::Pt;
-    for (int i = threadIdx.x; i < nt_blk * X::Pt; i += 256) ltab[i] = src_t[i];
+    for (int i = threadIdx.x; i < nt_blk * X::Pt; i += NT) ltab[i] = src_t[i];
     const float2* src_yx = a.cs + (size_t)a.T * X::Pt;
     const int nyx = a.Hh * X::Py + a.W * X::Px;
-    for (int i = threadIdx.x; i < nyx; i += 256) ltab[a.nt * X::Pt + i] = src_yx[i];
+    for (int i = threadIdx.x; i < nyx; i += NT) ltab[a.nt * X::Pt + i] = src_yx[i];
     tv.tab = ltab;
     tv.tbase = t_first;
     tv.ntr = a.nt;
@@ -507,6 +513,292 @@ void state_kernel(KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Half-state kernel (D = 64, 128).
+//
+// A full D x D accumulator per wave allows one wave per SIMD at D = 128, and
+// one wave alone leaves the SIMD idle while it waits on its own loads, LDS
+// round trips and MFMA results.  Here a block has 8 waves in 4 pairs; both
+// waves of pair p work on the pair's 16-token tiles p, p + 4, p + 8, ... and
+// wave half hf accumulates rows [hf D/2, hf D/2 + D/2) of S (D = 128: 128
+// accumulation registers, two waves per SIMD).  Each wave loads its half of
+// the features of k and of v, so every byte is fetched once: ReLU, z and
+// RoPE of its k half go to its own LDS tile (its A operand), its v half to
+// the pair's shared v tile (both waves' B operand), and one barrier per
+// step publishes the v tile.  The v tile alternates between two slots, so
+// the writes of step i + 1 never meet the reads of step i.  Lane l takes
+// token l / 4 and the 16-byte chunks 4s + l % 4 of its half.  Row pitches
+// are 16 or 48 (mod 64) dwords: the four rows one 16-lane group of a
+// transposing read touches then start 16 banks apart, and the two token rows
+// eight lanes write together never share a bank.  At the block's end the
+// four pairs' accumulators are added in pair order through LDS.
+constexpr int tile_pitch(int row_bytes) {
+  int dw = row_bytes / 4;
+  while (dw % 64 != 16 && dw % 64 != 48) ++dw;
+  return 4 * dw;
+}
+
+template <int D>
+struct HalfCfg {
+  static constexpr int HALF = D / 2;          // rows of S per wave
+  static constexpr int CH = HALF / 8;         // 16-byte chunks in a half row
+  static constexpr int KC = D / 64;           // k (and v) chunks per lane and tile
+  static constexpr int TW = 16;               // tokens per tile
+  static constexpr int RA = D / 64;           // 32-row blocks of a wave's S rows
+  static constexpr int RB = D / 32;           // 32-column blocks
+  static constexpr int KP = tile_pitch(HALF * 2);
+  static constexpr int VP = tile_pitch(D * 2);
+  static constexpr int KTILE = TW * KP;       // per wave
+  static constexpr int VTILE = TW * VP;       // per pair and slot
+  static constexpr int V_OFF = 8 * KTILE;
+  static constexpr int TILE_BYTES = V_OFF + 4 * 2 * VTILE;
+  static constexpr int PF = 2;                // tiles in flight per wave
+  // block-end reduction: per round each wave stores RED 32x32 tiles (4 KB)
+  static constexpr int NT = RA * RB;
+  static constexpr int RED_FIT = TILE_BYTES / (8 * 4096);
+  static constexpr int RED = RED_FIT < 1 ? 1 : (RED_FIT > NT ? NT : RED_FIT);
+  static constexpr int ZW_OFF = 8 * RED * 4096;
+  static constexpr int LDS_BYTES = TILE_BYTES > ZW_OFF + 16 * D ? TILE_BYTES : ZW_OFF + 16 * D;
+  static_assert(KC >= 1 && RA >= 1, "half-state layout needs D >= 64");
+};
+
+template <int D, bool ROPE, int HF>
+struct HalfWave {
+  using Cf = HalfCfg<D>;
+  static constexpr int KC = Cf::KC, RA = Cf::RA, RB = Cf::RB, PF = Cf::PF;
+  const KArgs& a;
+  const TabView& tv;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t tokstride, hoff;
+  int n_begin, n_end, pair, nit, lane, m, col;
+  unsigned char* kbuf;  // this wave's R phi(k) tile, TW rows of KP bytes
+  unsigned char* vbuf;  // the pair's two v tile slots, TW rows of VP bytes each
+  u32x4 kr[PF][KC], vr[PF][KC];
+  bf16x8 A[RA], Bv[RB];
+  float2 cs[KC][4];
+  float zacc[KC][8];
+  f32x16 acc[RA][RB];
+
+  __device__ __forceinline__ int token(int it) const {
+    return n_begin + Cf::TW * (pair + 4 * it) + col;
+  }
+
+  __device__ __forceinline__ void issue(int st, int it) {
+    const int n = token(it);
+    const uint32_t off = (it < nit && n < n_end) ? (uint32_t)n * tokstride + hoff : kOob;
+#pragma unroll
+    for (int s2 = 0; s2 < KC; ++s2) {
+      kr[st][s2] = load16(rk, off + 64u * s2);
+      vr[st][s2] = load16(rv, off + 64u * s2);
+    }
+  }
+
+  // (cos, sin) of the lane's k pairs in tile `it`: chunk 4 s + m of this
+  // half is chunk CH HF + 4 s + m of the row, pairs 4 times that plus u
+  __device__ __forceinline__ void load_factors(int it) {
+    if (!ROPE) return;
+    int t, y, x;
+    grid_pos(a, (uint32_t)min(token(it), n_end - 1), t, y, x);
+    const RowOff ro = row_offsets<D>(a, tv, t, y, x);
+    static_for<KC>([&](auto S2) {
+      constexpr int s2 = decltype(S2)::value;
+      static_for<4>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        constexpr int pmin = 4 * (Cf::CH * HF + 4 * s2) + u;
+        cs[s2][u] = rope_factor<D, pmin, pmin + 12>(tv, ro, pmin + 4 * m);
+      });
+    });
+  }
+
+  template <int ST>
+  __device__ __forceinline__ void stage(int it) {
+    asm volatile("" ::: "memory");
+    unsigned char* vt = vbuf + ST * Cf::VTILE + col * Cf::VP + Cf::HALF * 2 * HF;
+#pragma unroll
+    for (int s2 = 0; s2 < KC; ++s2) {
+      u32x4 fq;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        fq[u] = relu2(kr[ST][s2][u]);
+        zacc[s2][2 * u] += bf_lo(fq[u]);
+        zacc[s2][2 * u + 1] += bf_hi(fq[u]);
+      }
+      const u32x4 w = ROPE ? rotate_chunk(fq, cs[s2]) : fq;
+      *reinterpret_cast<u32x4*>(kbuf + col * Cf::KP + 16 * (4 * s2 + m)) = w;
+      *reinterpret_cast<u32x4*>(vt + 16 * (4 * s2 + m)) = vr[ST][s2];
+    }
+    issue(ST, it + PF);
+  }
+
+  // After the barrier: the wave's own k tile (the LDS executes one wave's
+  // instructions in order, so its own writes need no wait) and the pair's v
+  // slot ST.
+  template <int ST>
+  __device__ __forceinline__ void contract() {
+#pragma unroll
+    for (int i = 0; i < RA; ++i) A[i] = frag_tr(kbuf, Cf::KP, i, lane);
+#pragma unroll
+    for (int j = 0; j < RB; ++j) Bv[j] = frag_tr(vbuf + ST * Cf::VTILE, Cf::VP, j, lane);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < RA; ++i)
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], Bv[j], acc[i][j], 0, 0, 0);
+  }
+
+  // Every wave's LDS writes of this step are complete before any wave passes
+  // (no wait on the global loads in flight).
+  __device__ __forceinline__ void publish() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+
+  // Steps are kept apart in the schedule: overlapping one step's factor
+  // reads with the previous step's operands would overflow the register
+  // budget of two waves per SIMD, and a spill reload (a memory load like the
+  // prefetches) would make the loop wait for every load in flight.
+  template <int ST>
+  __device__ __forceinline__ void step(int it) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_factors(it);
+    stage<ST>(it);
+    publish();
+    contract<ST>();
+  }
+
+  // nsteps: the block's common step count (even, >= every pair's tiles);
+  // steps past a pair's last tile load and add zeros
+  __device__ __forceinline__ void run(int nsteps) {
+#pragma unroll
+    for (int i = 0; i < RA; ++i)
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < KC; ++s2)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) zacc[s2][j] = 0.f;
+    static_assert(PF == 2, "the load ring and the v slots alternate together");
+    // Loads return in issue order and the loop waits for slot 0 while slot 1
+    // is still in flight; the entry must issue the slots in the same order as
+    // the loop body, or the wait at the loop head becomes a wait for all.
+    issue(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int it = 0; it < nsteps; it += 2) {
+      step<0>(it);
+      step<1>(it + 1);
+    }
+  }
+};
+
+// Runs one half's waves and the block-end reduction.  Both halves execute the
+// same sequence of barriers.
+template <int D, bool ROPE, int HF>
+__device__ __forceinline__ void half_main(const KArgs& a, const TabView& tv, unsigned char* smem,
+                                          int tid, int wave, int pair, int lane, int b, int h,
+                                          int bh, int c, int n_begin, int n_end) {
+  using Cf = HalfCfg<D>;
+  const int m = lane & 3, col = lane >> 2;
+  const size_t boff = (size_t)b * a.N * a.H * D;
+  const int ntile = (n_end - n_begin + Cf::TW - 1) / Cf::TW;
+  const int nsteps = 2 * ((ntile + 7) / 8);  // pair 0's tiles, rounded up to even
+  HalfWave<D, ROPE, HF> w{a,
+                          tv,
+                          make_rsrc(a.k + boff, a.slab_bytes),
+                          make_rsrc(a.v + boff, a.slab_bytes),
+                          (uint32_t)a.H * D * 2,
+                          (uint32_t)h * D * 2 + (uint32_t)(Cf::HALF * 2 * HF) + 16u * m,
+                          n_begin,
+                          n_end,
+                          pair,
+                          (ntile - pair + 3) / 4,
+                          lane,
+                          m,
+                          col,
+                          smem + wave * Cf::KTILE,
+                          smem + Cf::V_OFF + pair * 2 * Cf::VTILE};
+  w.run(nsteps);
+
+  // z of this wave: lanes with the same l % 4 hold the same features
+#pragma unroll
+  for (int msk = 4; msk < 64; msk *= 2)
+#pragma unroll
+    for (int s2 = 0; s2 < Cf::KC; ++s2)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w.zacc[s2][j] += __shfl_xor(w.zacc[s2][j], msk);
+
+  __syncthreads();  // every wave is done with its tiles; they become scratch
+  float* red = reinterpret_cast<float*>(smem);
+  float* dst = a.part + ((size_t)bh * a.C + c) * (size_t)(D * D + D);
+  float* zw = reinterpret_cast<float*>(smem + Cf::ZW_OFF);
+  if (col == 0) {
+#pragma unroll
+    for (int s2 = 0; s2 < Cf::KC; ++s2)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        zw[pair * D + Cf::HALF * HF + 8 * (4 * s2 + m) + j] = w.zacc[s2][j];
+  }
+  __syncthreads();
+  if (tid < D) dst[D * D + tid] = ((zw[tid] + zw[D + tid]) + zw[2 * D + tid]) + zw[3 * D + tid];
+
+  // S: add the four pairs' accumulators, RED 32x32 tiles per wave per round
+  constexpr int WSTRIDE = Cf::RED * 1024;  // floats per wave per round
+#pragma unroll
+  for (int t0 = 0; t0 < Cf::NT; t0 += Cf::RED) {
+#pragma unroll
+    for (int q = 0; q < Cf::RED; ++q) {
+      if (t0 + q < Cf::NT) {
+        const int ti = (t0 + q) / Cf::RB, tj = (t0 + q) % Cf::RB;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          red[wave * WSTRIDE + (q * 16 + r) * 64 + lane] = w.acc[ti][tj][r];
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 2 * WSTRIDE; idx += 512) {
+      const int hf = idx / WSTRIDE, rem = idx - hf * WSTRIDE;
+      const int q = rem / 1024, r = (rem / 64) % 16, l = rem % 64;
+      if (t0 + q < Cf::NT) {
+        const int ti = (t0 + q) / Cf::RB, tj = (t0 + q) % Cf::RB;
+        const float* src = red + 4 * hf * WSTRIDE + rem;
+        const float sum = ((src[0] + src[WSTRIDE]) + src[2 * WSTRIDE]) + src[3 * WSTRIDE];
+        const int d = Cf::HALF * hf + 32 * ti + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        const int e = 32 * tj + (l & 31);
+        dst[d * D + e] = sum;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, bool ROPE, bool TLDS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void state_half_kernel(KArgs a) {
+  using Cf = HalfCfg<D>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float2* ltab = reinterpret_cast<float2*>(smem + Cf::LDS_BYTES);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int pair = wave & 3, hf = wave >> 2;
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int n_begin = c * a.L;
+  const int n_end = min(a.N, n_begin + a.L);
+
+  TabView tv{};
+  if (ROPE) tv = stage_table<D, 512>(a, ltab, TLDS, n_begin, n_end);
+  __syncthreads();
+  if (hf == 0)
+    half_main<D, ROPE, 0>(a, tv, smem, tid, wave, pair, lane, b, h, bh, c, n_begin, n_end);
+  else
+    half_main<D, ROPE, 1>(a, tv, smem, tid, wave, pair, lane, b, h, bh, c, n_begin, n_end);
+}
+
+// ---------------------------------------------------------------------------
 // Reduce kernel: per head, S = sum_c S_c and z = sum_c z_c over the C chunk
 // partials.  Each thread loads the P (a power of two >= C, at most 64) chunk
 // values of its element at once -- loads past the head's C partials fall
@@ -709,7 +1001,7 @@ void output_kernel(KArgs a) {
         }
         ow[u] = pack_bf16(o2[0], o2[1]);
       }
-      store16(ro, toff + 64u * t, ow);
+      store16_nt(ro, toff + 64u * t, ow);
     }
   };
 
@@ -726,9 +1018,18 @@ void output_kernel(KArgs a) {
   }
 }
 
+// D = 32 keeps the one-wave-per-tile kernel (its accumulator is small);
+// D = 64 and 128 use the half-state kernel.
+template <int D>
+constexpr bool use_half() {
+  return D >= 64;
+}
 template <int D>
 constexpr int state_lds_bytes() {
-  return StateCfg<D>::LDS_BYTES;
+  if constexpr (use_half<D>())
+    return HalfCfg<D>::LDS_BYTES;
+  else
+    return StateCfg<D>::LDS_BYTES;
 }
 template <int D>
 constexpr int output_lds_bytes() {
@@ -746,12 +1047,13 @@ void launch_reduce(const Plan& p, const KArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((reduce_kernel<D, P>), g2, dim3(256), 0, stream, a);
 }
 
-// Kernels that take more than 64 KB of dynamic LDS say so once per process.
-template <class K>
-hipError_t allow_lds(K kernel, size_t bytes) {
+// A kernel that takes more than 64 KB of dynamic LDS raises its limit to the
+// largest size asked for so far (one record per kernel).
+template <auto K>
+hipError_t allow_lds(size_t bytes) {
   static size_t granted = 0;
   if (bytes <= 65536 || bytes <= granted) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(K),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e == hipSuccess) granted = bytes;
   return e;
@@ -760,9 +1062,15 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 template <int D, bool ROPE, bool TLDS>
 hipError_t launch_state_k(const Plan& p, const KArgs& a, size_t lds, hipStream_t stream) {
   const dim3 g1(p.C, p.BH);
-  hipError_t e = allow_lds(state_kernel<D, ROPE, TLDS>, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((state_kernel<D, ROPE, TLDS>), g1, dim3(256), lds, stream, a);
+  if constexpr (use_half<D>()) {
+    hipError_t e = allow_lds<state_half_kernel<D, ROPE, TLDS>>(lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((state_half_kernel<D, ROPE, TLDS>), g1, dim3(512), lds, stream, a);
+  } else {
+    hipError_t e = allow_lds<state_kernel<D, ROPE, TLDS>>(lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((state_kernel<D, ROPE, TLDS>), g1, dim3(256), lds, stream, a);
+  }
   return hipGetLastError();
 }
 
