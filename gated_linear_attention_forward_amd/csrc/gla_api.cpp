@@ -67,7 +67,7 @@ Plan make_plan(int B, int N, int H, int D) {
   p.off_part = off;
   off = align_up(off + (size_t)p.BH * p.C * (size_t)(D * D + D) * sizeof(float), 256);
   p.off_sl = off;
-  off = align_up(off + (size_t)p.BH * (D + 16) * D * sizeof(uint16_t), 256);
+  off = align_up(off + (size_t)p.BH * (D + 2) * D * sizeof(uint16_t), 256);
   p.off_z = off;
   off = align_up(off + (size_t)p.BH * D * sizeof(float), 256);
   p.ws_bytes = off;

@@ -38,7 +38,7 @@ struct KArgs {
   int nt;                // t-rows of the table staged per block (when staged in LDS)
   // workspace
   float* part;           // [BH][C][D*D + D] fp32 chunk partials
-  uint16_t* sl;          // [BH][D + 16][D] bf16: S^T rows in output order, then z rows
+  uint16_t* sl;          // [BH][D + 2][D] bf16: S^T rows in output order, then z hi/lo rows
   float* zf;             // [BH][D] fp32 z
   float* S_out;          // optional fp32 S [BH][D][D]
   float* z_out;          // optional fp32 z [BH][D]

@@ -805,16 +805,18 @@ void state_half_kernel(KArgs a) {
 // outside the buffer and read as zero -- and adds them in a fixed pairwise
 // tree, so the result does not depend on which block finished first.  More
 // than 64 chunks are summed 64 at a time, groups in order.
-// Outputs per head, in the output kernel's operand layout (D + 16 rows of D
-// bf16): row R(e) holds S[0..D)[e]; row D holds bf16(z), row D + 1 holds
-// bf16(z - bf16(z)); rows D + 2 .. D + 15 are zero.  Optional fp32 copies of
-// S and z go to the caller.
+// Outputs per head, in the output kernel's operand layout (D + 2 rows of D
+// bf16): row R(e) holds S[0..D)[e] (see out_row_of); row D holds bf16(z),
+// row D + 1 holds bf16(z - bf16(z)).  Optional fp32 copies of S and z go to
+// the caller.
 
-// Output-kernel operand row of value column e (see output_kernel).
+// Output-kernel operand row of value column e: with MB = D/16 column blocks,
+// row 16 j + c holds column MB c + j, so that lane column c of block j owns
+// the MB contiguous columns MB c .. MB c + MB - 1 across the blocks.
+template <int D>
 __device__ __forceinline__ int out_row_of(int e) {
-  const int j = 2 * (e >> 5) + ((e & 7) >> 2);
-  const int r = 4 * ((e & 31) >> 3) + (e & 3);
-  return 16 * j + r;
+  constexpr int MB = D / 16;
+  return 16 * (e % MB) + e / MB;
 }
 
 template <int P, int R>
@@ -849,13 +851,13 @@ __global__ __launch_bounds__(256) void reduce_kernel(KArgs a) {
   const uint32_t pstride = (uint32_t)(D * D + D) * 4u;  // bytes per chunk partial
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(a.part + (size_t)bh * a.C * (D * D + D), (uint32_t)a.C * pstride);
-  uint16_t* slh = a.sl + (size_t)bh * (D + 16) * D;
+  uint16_t* slh = a.sl + (size_t)bh * (D + 2) * D;
   if (gid < NS) {
     const int e = gid % D;
     const int d = 2 * (gid / D);
     float s[2];
     tree_sum<P, 2>(rs, (uint32_t)(d * D + e) * 4u, pstride, (uint32_t)D * 4u, a.C, s);
-    *reinterpret_cast<uint32_t*>(slh + (size_t)out_row_of(e) * D + d) = pack_bf16(s[0], s[1]);
+    *reinterpret_cast<uint32_t*>(slh + (size_t)out_row_of<D>(e) * D + d) = pack_bf16(s[0], s[1]);
     if (a.S_out) {
       a.S_out[(size_t)bh * D * D + (size_t)d * D + e] = s[0];
       a.S_out[(size_t)bh * D * D + (size_t)(d + 1) * D + e] = s[1];
@@ -870,33 +872,75 @@ __global__ __launch_bounds__(256) void reduce_kernel(KArgs a) {
     const __bf16 zl = (__bf16)(s[0] - (float)zh);
     slh[(size_t)D * D + d] = __builtin_bit_cast(uint16_t, zh);
     slh[(size_t)(D + 1) * D + d] = __builtin_bit_cast(uint16_t, zl);
-#pragma unroll
-    for (int r = 2; r < 16; ++r) slh[(size_t)(D + r) * D + d] = 0;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Output kernel.
 //
-// Block = 256 threads (4 waves), one (token range, head).  The head's S (bf16,
-// D x D) and the two z rows are staged in LDS once per block with rows padded
-// by 16 bytes.  Each wave handles 16 tokens per step as the B operand of
-// v_mfma_f32_16x16x32_bf16 computing num^T = S^T (R phi(q))^T: lane l holds
-// token l % 16 and, for k-step s, the 16-byte chunk 4s + l/16 of that token's
-// q -- a direct 16-byte global load, no LDS round trip.  The accumulator then
-// holds, for the same token, value columns E(j, m, i) = 32*(j/2) + 8m +
-// 4*(j%2) + i (m = l/16), which for each pair of 16-row blocks is again the
-// 16-byte chunk 4t + m: g is read and out written with the same 16-byte
-// per-lane pattern as q.  The denominator phi(q).z uses the unrotated
-// features, which are exact in bf16: one more 16-row block holds z as a bf16
-// hi/lo pair, so phi(q).z comes out of the same MFMA pipe in fp32.
+// Block = 256 threads (4 waves), one (token range, head).  The head's S^T
+// (bf16, D rows of D) and the two z rows are staged in LDS once per block,
+// rows padded by 16 bytes.  Each wave computes 16 tokens per step as
+// num = (R phi(q)) S on v_mfma_f32_16x16x32_bf16 with the tokens as the A
+// operand: lane l holds token l % 16 and, for k-step s, features
+// 32 s + 8 (l / 16) .. + 7 of it (one 16-byte global load).  The B operand
+// of column block j is LDS row 16 j + c for lane column c, which holds value
+// column MB c + j (MB = D / 16 blocks).  The accumulator of block j then
+// holds, in lane l, tokens 4 (l / 16) + i (i < 4) at value column
+// MB (l % 16) + j: across the MB blocks a lane owns MB contiguous columns of
+// four tokens (16 bytes at D = 128).  g is read and out written in that
+// layout, so one instruction covers four whole token rows.  The denominator
+// phi(q).z uses the unrotated features, exact in bf16, against B columns
+// that alternate bf16(z) and bf16(z - bf16(z)); adding the neighbouring
+// lane's value gives phi(q).z in fp32 for the same four tokens.
+template <int OB>
+struct Chunk;
+template <>
+struct Chunk<16> {
+  typedef u32x4 T;
+};
+template <>
+struct Chunk<8> {
+  typedef uint32_t T __attribute__((ext_vector_type(2)));
+};
+template <>
+struct Chunk<4> {
+  typedef uint32_t T __attribute__((ext_vector_type(1)));
+};
+
+template <int OB>
+__device__ __forceinline__ typename Chunk<OB>::T load_chunk(__amdgpu_buffer_rsrc_t r,
+                                                            uint32_t off) {
+  using T = typename Chunk<OB>::T;
+  if constexpr (OB == 16)
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  else if constexpr (OB == 8)
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  else
+    return T{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)};
+}
+
+template <int OB>
+__device__ __forceinline__ void store_chunk_nt(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               typename Chunk<OB>::T v) {
+  if constexpr (OB == 16)
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNt);
+  else if constexpr (OB == 8)
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolNt);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(v[0], r, off, 0, kCpolNt);
+}
+
 template <int D, bool ROPE, bool TLDS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void output_kernel(KArgs a) {
   constexpr int KS = D / 32;       // k-steps of 32 features
-  constexpr int MB = D / 16;       // 16-row blocks of S^T
+  constexpr int MB = D / 16;       // 16-column blocks of the value dimension
+  constexpr int OB = 2 * MB;       // output bytes per lane and token
+  constexpr int OW = OB / 4;       // ... in dwords
   constexpr int PITCH = D * 2 + 16;
-  constexpr int ROWS = D + 16;
+  constexpr int ROWS = D + 2;
+  using OChunk = typename Chunk<OB>::T;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char* sS = smem;
   float2* ltab = reinterpret_cast<float2*>(smem + ROWS * PITCH);
@@ -911,7 +955,7 @@ void output_kernel(KArgs a) {
   const int n_begin = blockIdx.x * a.L;
   const int n_end = min(a.N, n_begin + a.L);
 
-  // stage S^T rows and the z rows
+  // stage the S^T rows and the z rows
   const uint4* src = reinterpret_cast<const uint4*>(a.sl + (size_t)bh * ROWS * D);
   for (int i = tid; i < ROWS * D / 8; i += 256) {
     const int row = i / (D / 8), u = i % (D / 8);
@@ -926,87 +970,104 @@ void output_kernel(KArgs a) {
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + boff, a.slab_bytes);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out + boff, a.slab_bytes);
   const uint32_t tokstride = (uint32_t)a.H * D * 2;
-  const uint32_t headoff = (uint32_t)h * D * 2 + 16u * m;
+  const uint32_t qoff = (uint32_t)h * D * 2 + 16u * m;     // A operand chunk of q
+  const uint32_t goff = (uint32_t)h * D * 2 + (uint32_t)OB * col;  // owned output columns
 
-  auto offset_of = [&](int base) -> uint32_t {
+  // q: token base + col; g and out: token base + 4 m + i
+  auto q_offset = [&](int base) -> uint32_t {
     const int n = base + col;
-    return (n < n_end) ? (uint32_t)n * tokstride + headoff : kOob;
+    return (n < n_end) ? (uint32_t)n * tokstride + qoff : kOob;
   };
-  auto load_qg = [&](int base, u32x4 (&qv)[KS], u32x4 (&gv)[KS]) {
-    const uint32_t toff = offset_of(base);
+  auto g_offset = [&](int base, int i) -> uint32_t {
+    const int n = base + 4 * m + i;
+    return (n < n_end) ? (uint32_t)n * tokstride + goff : kOob;
+  };
+  auto load_qg = [&](int base, u32x4 (&qv)[KS], OChunk (&gv)[4]) {
+    const uint32_t toff = q_offset(base);
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) qv[s2] = load16(rq, toff + 64u * s2);
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) gv[s2] = load16(rg, toff + 64u * s2);
+    for (int i = 0; i < 4; ++i) gv[i] = load_chunk<OB>(rg, g_offset(base, i));
   };
 
   // one 16-token step of this wave: tokens base .. base + 15
-  auto step = [&](int base, const u32x4 (&qv)[KS], const u32x4 (&gv)[KS]) {
-    // keep the S fragments in LDS: reading them inside the loop costs LDS
+  auto step = [&](int base, const u32x4 (&qv)[KS], const OChunk (&gv)[4]) {
+    // the S fragments stay in LDS: reading them in the loop costs LDS
     // bandwidth but leaves registers for more waves in flight
     asm volatile("" ::: "memory");
-    const uint32_t toff = offset_of(base);
     RowOff rof{};
     if (ROPE) {
       int t, y, x;
       grid_pos(a, (uint32_t)min(base + col, n_end - 1), t, y, x);
       rof = row_offsets<D>(a, tv, t, y, x);
     }
-    bf16x8 Bd[KS], Bq[KS];
-    static_for<KS>([&](auto S2) {
-      constexpr int s2 = decltype(S2)::value;
-      u32x4 fq;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) fq[u] = relu2(qv[s2][u]);
-      Bd[s2] = __builtin_bit_cast(bf16x8, fq);
-      Bq[s2] = __builtin_bit_cast(bf16x8, ROPE ? rope_chunk<D, s2>(fq, tv, rof, m) : fq);
-    });
-
+    // phi(q) first, against z: phi(q).z_hi in even lane columns, phi(q).z_lo
+    // in odd ones; the rotated operand is built afterwards from the same
+    // registers, so the two copies are never live together
+    u32x4 fq[KS];
     f32x4 accd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-      const bf16x8 A = *reinterpret_cast<const bf16x8*>(sS + (D + col) * PITCH + 16 * (4 * s2 + m));
-      accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bd[s2], accd, 0, 0, 0);
-    }
-    f32x4 acc[MB];
 #pragma unroll
-    for (int j = 0; j < MB; ++j) {
+      for (int u = 0; u < 4; ++u) fq[s2][u] = relu2(qv[s2][u]);
+      const bf16x8 Bz =
+          *reinterpret_cast<const bf16x8*>(sS + (D + (col & 1)) * PITCH + 16 * (4 * s2 + m));
+      accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fq[s2]), Bz, accd,
+                                                    0, 0, 0);
+    }
+    bf16x8 Aq[KS];
+    static_for<KS>([&](auto S2) {
+      constexpr int s2 = decltype(S2)::value;
+      Aq[s2] = __builtin_bit_cast(bf16x8, ROPE ? rope_chunk<D, s2>(fq[s2], tv, rof, m) : fq[s2]);
+    });
+    // S fragments of column block j + 1 are read while block j multiplies;
+    // the fences keep the compiler from reading further ahead (each block
+    // is KS fragments of 4 registers)
+    f32x4 acc[MB];
+    bf16x8 Bf[2][KS];
+    auto read_b = [&](int j, bf16x8 (&dst)[KS]) {
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        dst[s2] = *reinterpret_cast<const bf16x8*>(sS + (16 * j + col) * PITCH + 16 * (4 * s2 + m));
+    };
+    read_b(0, Bf[0]);
+    static_for<MB>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j + 1 < MB) read_b(j + 1, Bf[(j + 1) & 1]);
+      asm volatile("" ::: "memory");
       acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) {
-        const bf16x8 A =
-            *reinterpret_cast<const bf16x8*>(sS + (16 * j + col) * PITCH + 16 * (4 * s2 + m));
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bq[s2], acc[j], 0, 0, 0);
-      }
-    }
-
-    // rows 0 and 1 of the z block (lanes 0..15) hold phi(q).z_hi and phi(q).z_lo
-    const float dpart = accd[0] + accd[1];
-    const float den = __shfl(dpart, col) + kEps;
+      for (int s2 = 0; s2 < KS; ++s2)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[s2], Bf[j & 1][s2], acc[j], 0, 0, 0);
+    });
 
 #pragma unroll
-    for (int t = 0; t < KS; ++t) {
-      u32x4 ow;
+    for (int i = 0; i < 4; ++i) {
+      // quad_perm [1, 0, 3, 2]: the neighbouring lane column's term
+      const float other = __int_as_float(
+          __builtin_amdgcn_mov_dpp(__float_as_int(accd[i]), 0xB1, 0xF, 0xF, false));
+      const float den = (accd[i] + other) + kEps;
+      OChunk ow;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int w = 0; w < OW; ++w) {
         float o2[2];
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
-          const int jj = 2 * u + hlf;            // element of the 16-byte chunk
-          const int j = 2 * t + (jj >> 2);       // accumulator block
-          const float gval = hlf ? bf_hi(gv[t][u]) : bf_lo(gv[t][u]);
+          const int j = 2 * w + hlf;  // column block = element of the owned chunk
+          const float gval = hlf ? bf_hi(gv[i][w]) : bf_lo(gv[i][w]);
           // sigmoid(g) / den = 1 / (den * (1 + exp(-g)))
           const float e = __expf(-gval);
-          o2[hlf] = acc[j][jj & 3] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
+          o2[hlf] = acc[j][i] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
         }
-        ow[u] = pack_bf16(o2[0], o2[1]);
+        ow[w] = pack_bf16(o2[0], o2[1]);
       }
-      store16_nt(ro, toff + 64u * t, ow);
+      store_chunk_nt<OB>(ro, g_offset(base, i), ow);
     }
   };
 
   // two register sets: the next step's q and g are in flight during a step
-  u32x4 qa[KS], ga[KS], qb[KS], gb[KS];
+  u32x4 qa[KS], qb[KS];
+  OChunk ga[4], gb[4];
   int base = n_begin + 16 * wave;
   if (base < n_end) load_qg(base, qa, ga);
   for (; base < n_end; base += 128) {
@@ -1033,7 +1094,7 @@ constexpr int state_lds_bytes() {
 }
 template <int D>
 constexpr int output_lds_bytes() {
-  return (D + 16) * (D * 2 + 16);
+  return (D + 2) * (D * 2 + 16);
 }
 
 int table_lds_bytes(const KArgs& a) {
