@@ -8,12 +8,16 @@ torch's current stream with inputs already resident in HBM.
 Prints ONE JSON line.  `value` is tokens/s per layer (B*N tokens per step).
 `roofline` reports the output kernel (the largest byte stream: q, g read and
 out written, 6*D bytes per (token, head)) from HIP events recorded around it
-in every timed step.  `cpu_baseline` times the fp64 oracle on the same
-workload, repeated for about ten seconds of CPU work.
+in every timed step on the stream it runs on; `traffic` is its HBM bytes per
+launch from the committed rocprofv3 byte counters (profiles/), or null when
+the kernel source differs from the one those counters were taken on.
+`cpu_baseline` times the fp64 oracle on a sample of the workload's heads
+(about ten seconds of CPU work) and scales to the whole workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,29 +36,56 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, q, k, v, g, min_seconds=10.0, max_reps=20):
-    """Times the fp64 oracle on the whole workload, repeated until about
-    `min_seconds` of CPU work (or `max_reps` passes) have run."""
+def cpu_baseline(w, q, k, v, g, min_seconds=10.0):
+    """Times the fp64 oracle on the first `hs` heads of batch element 0 (one
+    head per oracle thread), repeated until about `min_seconds` of CPU work,
+    and scales the per-head time to the whole workload (heads are
+    independent and cost the same)."""
     import oracle
     grid = oracle.Grid(w.T, w.Hh, w.W, w.theta)
     threads = oracle.num_threads()
+    hs = max(1, min(w.H, threads))
+    qs, ks, vs, gs = (t[:1, :, :hs].contiguous() for t in (q, k, v, g))
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.forward(q, k, v, g, grid)
+        oracle.forward(qs, ks, vs, gs, grid)
         reps += 1
         dt = time.perf_counter() - t0
-        if dt >= min_seconds or reps >= max_reps:
+        if dt >= min_seconds:
             break
-    per = dt / reps
+    per_head = dt / (reps * hs)
+    whole = per_head * w.B * w.H
     return {
-        "value": (w.B * w.N) / per,
+        "value": (w.B * w.N) / whole,
         "unit": "tokens/s",
-        "cores": min(threads, w.B * w.H),
+        "cores": hs,
         "kind": "oracle",
-        "sample": f"whole workload ({w.B * w.H} heads x N={w.N}), {reps} passes in {dt:.1f} s, "
-                  f"{per:.2f} s per pass",
+        "sample": f"{hs} of {w.B * w.H} heads (batch 0, all N={w.N} tokens), {reps} passes in "
+                  f"{dt:.1f} s; {per_head:.3f} s per head, scaled to {w.B * w.H} heads",
     }
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "counters_5b_720p_193f.md")
+KERNEL_SOURCE = os.path.join(ROOT, "gated_linear_attention_forward_amd", "csrc", "gla_kernels.hip")
+
+
+def counter_traffic(workload_name):
+    """HBM bytes per launch of the output kernel from the committed counters,
+    if they were taken on this workload and on the current kernel source."""
+    if workload_name != "5b_720p_193f" or not os.path.exists(COUNTERS):
+        return None, "no counters for this workload"
+    fields = {}
+    with open(COUNTERS) as f:
+        for line in f:
+            key, sep, val = line.partition(":")
+            if sep and key.strip() in ("kernel_source_sha256", "output_kernel_traffic_bytes"):
+                fields[key.strip()] = val.strip()
+    with open(KERNEL_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest:
+        return None, "kernel source changed since the counters were taken"
+    return float(fields["output_kernel_traffic_bytes"]), os.path.relpath(COUNTERS, ROOT)
 
 
 def copy_calibration(dev, nbytes=1 << 30):
@@ -137,6 +168,7 @@ def main():
     all_bytes = out_bytes + state_bytes
     achieved = out_bytes / (out_ms * 1e-3) / 1e9
     tokens = w.B * w.N
+    traffic, traffic_src = counter_traffic(w.name)
     result = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -161,9 +193,21 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS,
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_source": traffic_src,
+            "traffic_over_algorithmic": traffic / out_bytes if traffic else None,
             "algorithmic_bytes": out_bytes,
             "avg_ms": out_ms,
+        },
+        "state_roofline": {
+            "kernels": "state + reduce",
+            "bound": "hbm",
+            "achieved": state_bytes / (state_ms * 1e-3) / 1e9,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": state_bytes / (state_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "algorithmic_bytes": state_bytes,
+            "avg_ms": state_ms,
         },
     }
     rope.close()
