@@ -71,7 +71,7 @@ constexpr int kMaxChunks = 256;
 constexpr int state_blocks(int D) { return D > 0 ? 256 : 256; }
 // Each wave of a state block should see at least this many 16-token tiles.
 constexpr int kStateMinTilesPerWave = 2;
-constexpr int kOutputBlocks = 1024;
+constexpr int kOutputBlocks = 2048;
 // Largest RoPE table slice (bytes) a block stages in LDS; larger grids read
 // the table from global memory instead.
 constexpr int kMaxLdsTableBytes = 24 * 1024;

@@ -950,9 +950,12 @@ void output_kernel(KArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int m = lane >> 4;
   const int col = lane & 15;
-  const int bh = blockIdx.y;
+  // heads vary fastest over the grid: the blocks resident at once cover every
+  // head of a few token ranges (whole token rows are read together), and with
+  // a head count divisible by the 8 XCDs each head's blocks share one L2
+  const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int n_begin = blockIdx.x * a.L;
+  const int n_begin = blockIdx.y * a.L;
   const int n_end = min(a.N, n_begin + a.L);
 
   // stage the S^T rows and the z rows
@@ -1162,7 +1165,7 @@ hipError_t launch_state_d(const Plan& p, KArgs a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream) {
-  const dim3 g3(p.C2, p.BH);
+  const dim3 g3(p.BH, p.C2);
   const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;
   const size_t lds = output_lds_bytes<D>() + (tl ? table_lds_bytes(a) : 0);
   if (!a.cs)
