@@ -525,8 +525,10 @@ void state_kernel(KArgs a) {
 // RoPE of its k half go to its own LDS tile (its A operand), its v half to
 // the pair's shared v tile (both waves' B operand), and one barrier per
 // step publishes the v tile.  The v tile alternates between two slots, so
-// the writes of step i + 1 never meet the reads of step i.  Lane l takes
-// token l / 4 and the 16-byte chunks 4s + l % 4 of its half.  Row pitches
+// the writes of step i + 1 never meet the reads of step i.  With CH
+// 16-byte chunks in a half row, lane l takes chunk l % CH of tile rows
+// l / CH, l / CH + 64 / CH, ...: one load instruction covers 64 / CH whole
+// half rows, which streams faster than sixteen partial rows.  Row pitches
 // are 16 or 48 (mod 64) dwords: the four rows one 16-lane group of a
 // transposing read touches then start 16 banks apart, and the two token rows
 // eight lanes write together never share a bank.  At the block's end the
@@ -541,8 +543,9 @@ template <int D>
 struct HalfCfg {
   static constexpr int HALF = D / 2;          // rows of S per wave
   static constexpr int CH = HALF / 8;         // 16-byte chunks in a half row
-  static constexpr int KC = D / 64;           // k (and v) chunks per lane and tile
+  static constexpr int TPI = 64 / CH;         // tokens per load instruction
   static constexpr int TW = 16;               // tokens per tile
+  static constexpr int NI = TW / TPI;         // tokens per lane and tile (k and v each)
   static constexpr int RA = D / 64;           // 32-row blocks of a wave's S rows
   static constexpr int RB = D / 32;           // 32-column blocks
   static constexpr int KP = tile_pitch(HALF * 2);
@@ -558,73 +561,75 @@ struct HalfCfg {
   static constexpr int RED = RED_FIT < 1 ? 1 : (RED_FIT > NT ? NT : RED_FIT);
   static constexpr int ZW_OFF = 8 * RED * 4096;
   static constexpr int LDS_BYTES = TILE_BYTES > ZW_OFF + 16 * D ? TILE_BYTES : ZW_OFF + 16 * D;
-  static_assert(KC >= 1 && RA >= 1, "half-state layout needs D >= 64");
+  static_assert(CH >= 4 && NI >= 1 && RA >= 1, "half-state layout needs D >= 64");
 };
 
 template <int D, bool ROPE, int HF>
 struct HalfWave {
   using Cf = HalfCfg<D>;
-  static constexpr int KC = Cf::KC, RA = Cf::RA, RB = Cf::RB, PF = Cf::PF;
+  static constexpr int NI = Cf::NI, RA = Cf::RA, RB = Cf::RB, PF = Cf::PF, TPI = Cf::TPI;
   const KArgs& a;
   const TabView& tv;
   __amdgpu_buffer_rsrc_t rk, rv;
   uint32_t tokstride, hoff;
-  int n_begin, n_end, pair, nit, lane, m, col;
+  int n_begin, n_end, pair, nit, lane, cl, tl;
   unsigned char* kbuf;  // this wave's R phi(k) tile, TW rows of KP bytes
   unsigned char* vbuf;  // the pair's two v tile slots, TW rows of VP bytes each
-  u32x4 kr[PF][KC], vr[PF][KC];
+  u32x4 kr[PF][NI], vr[PF][NI];
   bf16x8 A[RA], Bv[RB];
-  float2 cs[KC][4];
-  float zacc[KC][8];
+  float2 cs[NI][4];
+  float zacc[8];
   f32x16 acc[RA][RB];
 
-  __device__ __forceinline__ int token(int it) const {
-    return n_begin + Cf::TW * (pair + 4 * it) + col;
+  // token of the lane's i-th row in tile `it`
+  __device__ __forceinline__ int token(int it, int i) const {
+    return n_begin + Cf::TW * (pair + 4 * it) + TPI * i + tl;
   }
 
   __device__ __forceinline__ void issue(int st, int it) {
-    const int n = token(it);
-    const uint32_t off = (it < nit && n < n_end) ? (uint32_t)n * tokstride + hoff : kOob;
 #pragma unroll
-    for (int s2 = 0; s2 < KC; ++s2) {
-      kr[st][s2] = load16(rk, off + 64u * s2);
-      vr[st][s2] = load16(rv, off + 64u * s2);
+    for (int i = 0; i < NI; ++i) {
+      const int n = token(it, i);
+      const uint32_t off = (it < nit && n < n_end) ? (uint32_t)n * tokstride + hoff : kOob;
+      kr[st][i] = load16(rk, off);
+      vr[st][i] = load16(rv, off);
     }
   }
 
-  // (cos, sin) of the lane's k pairs in tile `it`: chunk 4 s + m of this
-  // half is chunk CH HF + 4 s + m of the row, pairs 4 times that plus u
+  // (cos, sin) of the lane's 4 pairs for each of its tokens in tile `it`:
+  // chunk cl of this half is chunk CH HF + cl of the row
   __device__ __forceinline__ void load_factors(int it) {
     if (!ROPE) return;
-    int t, y, x;
-    grid_pos(a, (uint32_t)min(token(it), n_end - 1), t, y, x);
-    const RowOff ro = row_offsets<D>(a, tv, t, y, x);
-    static_for<KC>([&](auto S2) {
-      constexpr int s2 = decltype(S2)::value;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      int t, y, x;
+      grid_pos(a, (uint32_t)min(token(it, i), n_end - 1), t, y, x);
+      const RowOff ro = row_offsets<D>(a, tv, t, y, x);
       static_for<4>([&](auto U) {
         constexpr int u = decltype(U)::value;
-        constexpr int pmin = 4 * (Cf::CH * HF + 4 * s2) + u;
-        cs[s2][u] = rope_factor<D, pmin, pmin + 12>(tv, ro, pmin + 4 * m);
+        constexpr int pmin = 4 * Cf::CH * HF + u;
+        cs[i][u] = rope_factor<D, pmin, pmin + 4 * (Cf::CH - 1)>(tv, ro, pmin + 4 * cl);
       });
-    });
+    }
   }
 
   template <int ST>
   __device__ __forceinline__ void stage(int it) {
     asm volatile("" ::: "memory");
-    unsigned char* vt = vbuf + ST * Cf::VTILE + col * Cf::VP + Cf::HALF * 2 * HF;
+    unsigned char* vt = vbuf + ST * Cf::VTILE + Cf::HALF * 2 * HF + 16 * cl;
 #pragma unroll
-    for (int s2 = 0; s2 < KC; ++s2) {
+    for (int i = 0; i < NI; ++i) {
       u32x4 fq;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        fq[u] = relu2(kr[ST][s2][u]);
-        zacc[s2][2 * u] += bf_lo(fq[u]);
-        zacc[s2][2 * u + 1] += bf_hi(fq[u]);
+        fq[u] = relu2(kr[ST][i][u]);
+        zacc[2 * u] += bf_lo(fq[u]);
+        zacc[2 * u + 1] += bf_hi(fq[u]);
       }
-      const u32x4 w = ROPE ? rotate_chunk(fq, cs[s2]) : fq;
-      *reinterpret_cast<u32x4*>(kbuf + col * Cf::KP + 16 * (4 * s2 + m)) = w;
-      *reinterpret_cast<u32x4*>(vt + 16 * (4 * s2 + m)) = vr[ST][s2];
+      const u32x4 w = ROPE ? rotate_chunk(fq, cs[i]) : fq;
+      const int row = TPI * i + tl;
+      *reinterpret_cast<u32x4*>(kbuf + row * Cf::KP + 16 * cl) = w;
+      *reinterpret_cast<u32x4*>(vt + row * Cf::VP) = vr[ST][i];
     }
     issue(ST, it + PF);
   }
@@ -675,9 +680,7 @@ struct HalfWave {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < KC; ++s2)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) zacc[s2][j] = 0.f;
+    for (int j = 0; j < 8; ++j) zacc[j] = 0.f;
     static_assert(PF == 2, "the load ring and the v slots alternate together");
     // Loads return in issue order and the loop waits for slot 0 while slot 1
     // is still in flight; the entry must issue the slots in the same order as
@@ -700,7 +703,7 @@ __device__ __forceinline__ void half_main(const KArgs& a, const TabView& tv, uns
                                           int tid, int wave, int pair, int lane, int b, int h,
                                           int bh, int c, int n_begin, int n_end) {
   using Cf = HalfCfg<D>;
-  const int m = lane & 3, col = lane >> 2;
+  const int cl = lane % Cf::CH, tl = lane / Cf::CH;
   const size_t boff = (size_t)b * a.N * a.H * D;
   const int ntile = (n_end - n_begin + Cf::TW - 1) / Cf::TW;
   const int nsteps = 2 * ((ntile + 7) / 8);  // pair 0's tiles, rounded up to even
@@ -709,36 +712,31 @@ __device__ __forceinline__ void half_main(const KArgs& a, const TabView& tv, uns
                           make_rsrc(a.k + boff, a.slab_bytes),
                           make_rsrc(a.v + boff, a.slab_bytes),
                           (uint32_t)a.H * D * 2,
-                          (uint32_t)h * D * 2 + (uint32_t)(Cf::HALF * 2 * HF) + 16u * m,
+                          (uint32_t)h * D * 2 + (uint32_t)(Cf::HALF * 2 * HF) + 16u * cl,
                           n_begin,
                           n_end,
                           pair,
                           (ntile - pair + 3) / 4,
                           lane,
-                          m,
-                          col,
+                          cl,
+                          tl,
                           smem + wave * Cf::KTILE,
                           smem + Cf::V_OFF + pair * 2 * Cf::VTILE};
   w.run(nsteps);
 
-  // z of this wave: lanes with the same l % 4 hold the same features
+  // z of this wave: lanes with the same l % CH hold the same features
 #pragma unroll
-  for (int msk = 4; msk < 64; msk *= 2)
+  for (int msk = Cf::CH; msk < 64; msk *= 2)
 #pragma unroll
-    for (int s2 = 0; s2 < Cf::KC; ++s2)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w.zacc[s2][j] += __shfl_xor(w.zacc[s2][j], msk);
+    for (int j = 0; j < 8; ++j) w.zacc[j] += __shfl_xor(w.zacc[j], msk);
 
   __syncthreads();  // every wave is done with its tiles; they become scratch
   float* red = reinterpret_cast<float*>(smem);
   float* dst = a.part + ((size_t)bh * a.C + c) * (size_t)(D * D + D);
   float* zw = reinterpret_cast<float*>(smem + Cf::ZW_OFF);
-  if (col == 0) {
+  if (tl == 0) {
 #pragma unroll
-    for (int s2 = 0; s2 < Cf::KC; ++s2)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        zw[pair * D + Cf::HALF * HF + 8 * (4 * s2 + m) + j] = w.zacc[s2][j];
+    for (int j = 0; j < 8; ++j) zw[pair * D + Cf::HALF * HF + 8 * cl + j] = w.zacc[j];
   }
   __syncthreads();
   if (tid < D) dst[D * D + tid] = ((zw[tid] + zw[D + tid]) + zw[2 * D + tid]) + zw[3 * D + tid];
