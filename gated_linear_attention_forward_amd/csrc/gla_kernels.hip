@@ -798,11 +798,14 @@ void state_half_kernel(KArgs a) {
 
 // ---------------------------------------------------------------------------
 // Reduce kernel: per head, S = sum_c S_c and z = sum_c z_c over the C chunk
-// partials.  Each thread loads the P (a power of two >= C, at most 64) chunk
-// values of its element at once -- loads past the head's C partials fall
-// outside the buffer and read as zero -- and adds them in a fixed pairwise
-// tree, so the result does not depend on which block finished first.  More
-// than 64 chunks are summed 64 at a time, groups in order.
+// partials.  A block takes a tile of S (16 rows x 64 columns at D = 128);
+// each thread loads, for its 4 consecutive columns e of a row d, the P (a power of two
+// >= C, at most 32) chunk values at once -- loads past the head's C partials
+// fall outside the buffer and read as zero -- and adds them in a fixed
+// pairwise tree, so the result does not depend on which block finished
+// first.  More than 32 chunks are summed 32 at a time, groups in order.  The
+// tile is transposed through LDS so the bf16 operand rows go out in 16-byte
+// runs.  The first tile's block also reduces z.
 // Outputs per head, in the output kernel's operand layout (D + 2 rows of D
 // bf16): row R(e) holds S[0..D)[e] (see out_row_of); row D holds bf16(z),
 // row D + 1 holds bf16(z - bf16(z)).  Optional fp32 copies of S and z go to
@@ -817,19 +820,21 @@ __device__ __forceinline__ int out_row_of(int e) {
   return 16 * (e % MB) + e / MB;
 }
 
+// Fixed-order sum over chunks of R 16-byte vectors at off0 + r * rstride.
 template <int P, int R>
-__device__ __forceinline__ void tree_sum(__amdgpu_buffer_rsrc_t rs, uint32_t off0, uint32_t cstride,
-                                         uint32_t rstride, int C, float (&out)[R]) {
+__device__ __forceinline__ void tree_sum4(__amdgpu_buffer_rsrc_t rs, uint32_t off0,
+                                          uint32_t cstride, uint32_t rstride, int C,
+                                          f32x4 (&out)[R]) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) out[r] = 0.f;
+  for (int r = 0; r < R; ++r) out[r] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int g0 = 0; g0 < C; g0 += P) {
-    float x[R][P];
+    f32x4 x[R][P];
 #pragma unroll
     for (int cc = 0; cc < P; ++cc)
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        x[r][cc] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            rs, off0 + (uint32_t)(g0 + cc) * cstride + r * rstride, 0, 0));
+        x[r][cc] = __builtin_bit_cast(
+            f32x4, load16(rs, off0 + (uint32_t)(g0 + cc) * cstride + r * rstride));
 #pragma unroll
     for (int w = P / 2; w >= 1; w /= 2)
 #pragma unroll
@@ -841,35 +846,68 @@ __device__ __forceinline__ void tree_sum(__amdgpu_buffer_rsrc_t rs, uint32_t off
   }
 }
 
+template <int D>
+struct RedCfg {
+  static constexpr int TE = D < 64 ? D : 64;   // tile columns (e)
+  static constexpr int EQ = TE / 4;            // threads per tile row (4 columns each)
+  static constexpr int TR = 256 / EQ < D ? 256 / EQ : D;  // tile rows (d), one per thread group
+  static constexpr int NTE = D / TE;           // tiles across e
+  static constexpr int NTILE = NTE * (D / TR); // tiles per head
+  static constexpr int TP = TR + 1;            // LDS pitch (floats) of the transposed tile
+  static_assert(EQ * TR == 256 && TR % 8 == 0, "one tile element group per thread");
+};
+
 template <int D, int P>
 __global__ __launch_bounds__(256) void reduce_kernel(KArgs a) {
-  constexpr int NS = D * D / 2;  // threads on S: column e, feature pair (2i, 2i + 1)
+  using Rc = RedCfg<D>;
+  __shared__ float tile[Rc::TE * Rc::TP];     // [e][d]
   const int bh = blockIdx.y;
-  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int t = threadIdx.x;
+  const int d0 = Rc::TR * (blockIdx.x / Rc::NTE), e0 = Rc::TE * (blockIdx.x % Rc::NTE);
   const uint32_t pstride = (uint32_t)(D * D + D) * 4u;  // bytes per chunk partial
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(a.part + (size_t)bh * a.C * (D * D + D), (uint32_t)a.C * pstride);
   uint16_t* slh = a.sl + (size_t)bh * (D + 2) * D;
-  if (gid < NS) {
-    const int e = gid % D;
-    const int d = 2 * (gid / D);
-    float s[2];
-    tree_sum<P, 2>(rs, (uint32_t)(d * D + e) * 4u, pstride, (uint32_t)D * 4u, a.C, s);
-    *reinterpret_cast<uint32_t*>(slh + (size_t)out_row_of<D>(e) * D + d) = pack_bf16(s[0], s[1]);
-    if (a.S_out) {
-      a.S_out[(size_t)bh * D * D + (size_t)d * D + e] = s[0];
-      a.S_out[(size_t)bh * D * D + (size_t)(d + 1) * D + e] = s[1];
+
+  // row d0 + t / EQ, columns e0 + 4 (t % EQ) .. + 3
+  const int dl = t / Rc::EQ, el = 4 * (t % Rc::EQ);
+  f32x4 s4[1];
+  tree_sum4<P, 1>(rs, (uint32_t)((d0 + dl) * D + e0 + el) * 4u, pstride, 0u, a.C, s4);
+  if (a.S_out)
+    *reinterpret_cast<f32x4*>(a.S_out + (size_t)bh * D * D + (size_t)(d0 + dl) * D + e0 + el) =
+        s4[0];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tile[(el + k) * Rc::TP + dl] = s4[0][k];
+  __syncthreads();
+  // operand rows: for each tile column e, TR values over d in runs of 8 (16 bytes)
+  for (int item = t; item < Rc::TE * (Rc::TR / 8); item += 256) {
+    const int e = item / (Rc::TR / 8), dc = 8 * (item % (Rc::TR / 8));
+    const float* src = tile + e * Rc::TP + dc;
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = pack_bf16(src[2 * k], src[2 * k + 1]);
+    *reinterpret_cast<u32x4*>(slh + (size_t)out_row_of<D>(e0 + e) * D + d0 + dc) = w;
+  }
+
+  if (blockIdx.x == 0 && t < D / 4) {
+    f32x4 z4[1];
+    tree_sum4<P, 1>(rs, (uint32_t)(D * D + 4 * t) * 4u, pstride, 0u, a.C, z4);
+    *reinterpret_cast<f32x4*>(a.zf + (size_t)bh * D + 4 * t) = z4[0];
+    if (a.z_out) *reinterpret_cast<f32x4*>(a.z_out + (size_t)bh * D + 4 * t) = z4[0];
+    uint32_t hi[2], lo[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const __bf16 h0 = (__bf16)z4[0][2 * k], h1 = (__bf16)z4[0][2 * k + 1];
+      const __bf16 l0 = (__bf16)(z4[0][2 * k] - (float)h0);
+      const __bf16 l1 = (__bf16)(z4[0][2 * k + 1] - (float)h1);
+      hi[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      lo[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
     }
-  } else if (gid < NS + D) {
-    const int d = gid - NS;
-    float s[1];
-    tree_sum<P, 1>(rs, (uint32_t)(D * D + d) * 4u, pstride, 0u, a.C, s);
-    a.zf[(size_t)bh * D + d] = s[0];
-    if (a.z_out) a.z_out[(size_t)bh * D + d] = s[0];
-    const __bf16 zh = (__bf16)s[0];
-    const __bf16 zl = (__bf16)(s[0] - (float)zh);
-    slh[(size_t)D * D + d] = __builtin_bit_cast(uint16_t, zh);
-    slh[(size_t)(D + 1) * D + d] = __builtin_bit_cast(uint16_t, zl);
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2v*>(slh + (size_t)D * D + 4 * t) = u32x2v{hi[0], hi[1]};
+    *reinterpret_cast<u32x2v*>(slh + (size_t)(D + 1) * D + 4 * t) = u32x2v{lo[0], lo[1]};
   }
 }
 
@@ -1105,7 +1143,7 @@ int table_lds_bytes(const KArgs& a) {
 
 template <int D, int P>
 void launch_reduce(const Plan& p, const KArgs& a, hipStream_t stream) {
-  const dim3 g2((D * D / 2 + D + 255) / 256, p.BH);
+  const dim3 g2(RedCfg<D>::NTILE, p.BH);
   hipLaunchKernelGGL((reduce_kernel<D, P>), g2, dim3(256), 0, stream, a);
 }
 
@@ -1154,10 +1192,8 @@ hipError_t launch_state_d(const Plan& p, KArgs a, hipStream_t stream) {
     launch_reduce<D, 8>(p, a, stream);
   else if (p.C <= 16)
     launch_reduce<D, 16>(p, a, stream);
-  else if (p.C <= 32)
-    launch_reduce<D, 32>(p, a, stream);
   else
-    launch_reduce<D, 64>(p, a, stream);
+    launch_reduce<D, 32>(p, a, stream);
   return hipGetLastError();
 }
 
