@@ -8,8 +8,9 @@ The oracle computes the gated bidirectional linear-attention token mixer of
 "SANA-Video 2.0" (NVlabs Sana docs, section Architecture: gated bidirectional
 linear attention with Wan 3D rotary position embeddings) in plain IEEE double
 arithmetic, one (b, h) head at a time: first the state S and normaliser z,
-then every token's output.  See the header of gla_oracle.c for the exact
-form and the readings it takes where the pages are silent.
+then every token's output.  ``forward_blocks`` is the block-causal form with
+a carried state.  See gla_oracle.c for the exact forms and the readings they
+take where the pages are silent.
 
 Inputs are bf16 bit patterns (numpy uint16 arrays, or torch bfloat16 CPU
 tensors which are viewed as such), layout [B, N, H, D] contiguous.
@@ -70,6 +71,9 @@ def _load():
     lib.gla_oracle_rows.restype = c_int
     lib.gla_oracle_forward.argtypes = ([u16p] * 4 + [c_int] * 4 + grid + [c_double, dp])
     lib.gla_oracle_forward.restype = c_int
+    lib.gla_oracle_forward_blocks.argtypes = ([u16p] * 4 + [c_int] * 4 + grid +
+                                              [c_double, c_long, dp, dp, dp, dp, dp])
+    lib.gla_oracle_forward_blocks.restype = c_int
     _lib = lib
     return lib
 
@@ -185,3 +189,29 @@ def forward(q, k, v, g, grid: Grid | None, eps: float = EPS) -> np.ndarray:
                                       B, N, H, D, *_grid_args(grid), float(eps),
                                       _p(out, ctypes.c_double)))
     return out
+
+
+def forward_blocks(q, k, v, g, grid: Grid | None, block_tokens: int, S_in=None, z_in=None,
+                   eps: float = EPS):
+    """Block-causal pass with a carried state (see gla_oracle_forward_blocks):
+    returns (o [B, N, H, D], S_out [B, H, D, D], z_out [B, H, D]) in fp64."""
+    q, k, v, g = (as_bits(a) for a in (q, k, v, g))
+    B, N, H, D = q.shape
+    for a in (k, v, g):
+        if a.shape != q.shape:
+            raise ValueError("q, k, v, g must share one [B, N, H, D] shape")
+    out = np.empty((B, N, H, D), np.float64)
+    S_out = np.empty((B, H, D, D), np.float64)
+    z_out = np.empty((B, H, D), np.float64)
+    null = ctypes.POINTER(ctypes.c_double)()
+    if S_in is not None:
+        S_in = np.ascontiguousarray(S_in, dtype=np.float64).reshape(B, H, D, D)
+    if z_in is not None:
+        z_in = np.ascontiguousarray(z_in, dtype=np.float64).reshape(B, H, D)
+    _check(_load().gla_oracle_forward_blocks(
+        *(_p(a, ctypes.c_uint16) for a in (q, k, v, g)), B, N, H, D, *_grid_args(grid),
+        float(eps), int(block_tokens),
+        _p(S_in, ctypes.c_double) if S_in is not None else null,
+        _p(z_in, ctypes.c_double) if z_in is not None else null,
+        _p(out, ctypes.c_double), _p(S_out, ctypes.c_double), _p(z_out, ctypes.c_double)))
+    return out, S_out, z_out

@@ -21,6 +21,9 @@
  *     z      = sum_n phi(k_n)                         (D)
  *     o_n[e] = sigmoid(g_n[e]) * ((R_n phi(q_n))^T S)[e] / (phi(q_n).z + eps)
  * "Bidirectional" is read as: no causal mask, S and z sum over all N tokens.
+ * gla_oracle_forward_blocks adds the block-causal form with a carried state
+ * (the constant-memory KV cache for block linear attention of the
+ * "SANA-Video_2B_720p" model card, innovation (2)); see its comment.
  *
  * RoPE reading (the pages only name "Wan 3D rotary position embeddings"):
  *   - the D/2 rotation pairs are (2i, 2i+1), interleaved;
@@ -163,10 +166,10 @@ static int check_args(int B, int N, int H, int D, const oracle_grid* gr) {
   return ORACLE_OK;
 }
 
-/* First pass for head (b, h): S[d*D + e] = sum_n (R_n phi(k_n))[d] v_n[e],
- * z[d] = sum_n phi(k_n)[d].  Sums run over n = 0 .. N-1 in order. */
-static int head_state(const uint16_t* k, const uint16_t* v, int N, int H, int D,
-                      const oracle_grid* gr, int b, int h, double* S, double* z) {
+/* Adds the terms of tokens n0 .. n1-1 of head (b, h), in order:
+ * S[d*D + e] += (R_n phi(k_n))[d] v_n[e],  z[d] += phi(k_n)[d]. */
+static int add_range(const uint16_t* k, const uint16_t* v, int N, int H, int D,
+                     const oracle_grid* gr, int b, int h, long n0, long n1, double* S, double* z) {
   double* fk = malloc(sizeof(double) * D);
   double* rk = malloc(sizeof(double) * D);
   double* vr = malloc(sizeof(double) * D);
@@ -174,9 +177,7 @@ static int head_state(const uint16_t* k, const uint16_t* v, int N, int H, int D,
     free(fk); free(rk); free(vr);
     return ORACLE_ERR_ALLOC;
   }
-  memset(S, 0, sizeof(double) * D * D);
-  memset(z, 0, sizeof(double) * D);
-  for (long n = 0; n < N; ++n) {
+  for (long n = n0; n < n1; ++n) {
     load_row(k, N, H, D, b, h, n, fk);
     load_row(v, N, H, D, b, h, n, vr);
     for (int d = 0; d < D; ++d) fk[d] = relu(fk[d]);
@@ -188,6 +189,15 @@ static int head_state(const uint16_t* k, const uint16_t* v, int N, int H, int D,
   }
   free(fk); free(rk); free(vr);
   return ORACLE_OK;
+}
+
+/* First pass for head (b, h): S[d*D + e] = sum_n (R_n phi(k_n))[d] v_n[e],
+ * z[d] = sum_n phi(k_n)[d].  Sums run over n = 0 .. N-1 in order. */
+static int head_state(const uint16_t* k, const uint16_t* v, int N, int H, int D,
+                      const oracle_grid* gr, int b, int h, double* S, double* z) {
+  memset(S, 0, sizeof(double) * D * D);
+  memset(z, 0, sizeof(double) * D);
+  return add_range(k, v, N, H, D, gr, b, h, 0, N, S, z);
 }
 
 /* Second pass for one token n of head (b, h), given that head's S and z. */
@@ -306,6 +316,70 @@ int gla_oracle_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
         double* dst = out + (((long)b * N + n) * H + h) * (long)D;
         for (int e = 0; e < D; ++e) dst[e] = row[e];
       }
+    }
+    free(S); free(z); free(fq); free(rq); free(gv); free(row);
+    if (r) {
+#pragma omp critical
+      err = r;
+    }
+  }
+  return err;
+}
+
+/* Block-causal form with a carried state: the constant-memory KV cache for
+ * block linear attention ("SANA-Video_2B_720p" model card, innovation (2):
+ * blocks are generated one after another and the cumulative state of linear
+ * attention carries the context of everything before).  Tokens are split
+ * into blocks of L tokens in order (the last block may be shorter); token n
+ * in block n / L sees every token up to the end of its own block, plus a
+ * carried state (S_in, z_in) from earlier calls:
+ *     S_<=b = S_in + sum over tokens m with m / L <= b of (R_m phi(k_m)) v_m^T
+ *     z_<=b = z_in + sum over the same tokens of phi(k_m)
+ *     o_n   = sigmoid(g_n) * ((R_n phi(q_n))^T S_<=b) / (phi(q_n).z_<=b + eps)
+ * with b = n / L.  S_in, z_in ([B, H, D, D] and [B, H, D]) may be NULL
+ * (zero).  S_out, z_out, when not NULL, receive the state after the last
+ * block, which a next call takes as its carried state.  L >= N with no
+ * carried state is the bidirectional mixer of gla_oracle_forward.
+ * The sums run block after block, tokens in order within a block. */
+int gla_oracle_forward_blocks(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const uint16_t* g, int B, int N, int H, int D,
+                              int rope, int T, int Hh, int W, double theta, long t0, long y0,
+                              long x0, double eps, long L, const double* S_in, const double* z_in,
+                              double* out, double* S_out, double* z_out) {
+  oracle_grid g0;
+  const oracle_grid* gr;
+  make_grid(rope, T, Hh, W, theta, t0, y0, x0, &g0, &gr);
+  int rc = check_args(B, N, H, D, gr);
+  if (rc) return rc;
+  if (L <= 0) return ORACLE_ERR_ARG;
+  int err = ORACLE_OK;
+  long BH = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    int b = (int)(bh / H), h = (int)(bh % H);
+    double* S = malloc(sizeof(double) * D * (long)D);
+    double* z = malloc(sizeof(double) * D);
+    double* fq = malloc(sizeof(double) * D);
+    double* rq = malloc(sizeof(double) * D);
+    double* gv = malloc(sizeof(double) * D);
+    double* row = malloc(sizeof(double) * D);
+    int r = (S && z && fq && rq && gv && row) ? ORACLE_OK : ORACLE_ERR_ALLOC;
+    if (!r) {
+      for (long i = 0; i < (long)D * D; ++i) S[i] = S_in ? S_in[bh * D * (long)D + i] : 0.0;
+      for (int d = 0; d < D; ++d) z[d] = z_in ? z_in[bh * D + d] : 0.0;
+      for (long n0 = 0; n0 < N && !r; n0 += L) {
+        long n1 = n0 + L < N ? n0 + L : N;
+        r = add_range(k, v, N, H, D, gr, b, h, n0, n1, S, z);
+        for (long n = n0; n < n1 && !r; ++n) {
+          head_row(q, g, N, H, D, gr, b, h, S, z, eps, n, fq, rq, gv, row);
+          double* dst = out + (((long)b * N + n) * H + h) * (long)D;
+          for (int e = 0; e < D; ++e) dst[e] = row[e];
+        }
+      }
+      if (!r && S_out)
+        for (long i = 0; i < (long)D * D; ++i) S_out[bh * D * (long)D + i] = S[i];
+      if (!r && z_out)
+        for (int d = 0; d < D; ++d) z_out[bh * D + d] = z[d];
     }
     free(S); free(z); free(fq); free(rq); free(gv); free(row);
     if (r) {

@@ -89,3 +89,36 @@ def row(q, k, v, g, b: int, h: int, i: int, grid=None, eps: float = 1e-6) -> np.
     den = (fk @ fq).sum() + eps
     gate = 1.0 / (1.0 + np.exp(-g[b, i, h]))
     return gate * num / den
+
+
+def forward_blocks(q, k, v, g, grid, L: int, S_in=None, z_in=None, eps: float = 1e-6):
+    """Block-causal quadratic form with a carried state.  Token i sees the
+    tokens j with j // L <= i // L (its own block and every earlier one), and
+    the carried state adds (R_i phi(q_i))^T S_in to the numerator and
+    phi(q_i) . z_in to the denominator.  S_in [B, H, D, D], z_in [B, H, D]."""
+    B, N, H, D = q.shape
+    fq = np.maximum(q, 0.0)
+    fk = np.maximum(k, 0.0)
+    if grid is not None:
+        ang = angles(D, *grid)
+        rq = rotate_complex(np.transpose(fq, (0, 2, 1, 3)), ang)
+        rk = rotate_complex(np.transpose(fk, (0, 2, 1, 3)), ang)
+    else:
+        rq = np.transpose(fq, (0, 2, 1, 3))
+        rk = np.transpose(fk, (0, 2, 1, 3))
+    blk = np.arange(N) // L
+    mask = (blk[None, :] <= blk[:, None]).astype(np.float64)   # [i, j]
+    out = np.empty_like(q)
+    for b in range(B):
+        for h in range(H):
+            num_w = (rq[b, h] @ rk[b, h].T) * mask
+            den_w = (fq[b, :, h, :] @ fk[b, :, h, :].T) * mask
+            num = num_w @ v[b, :, h, :]
+            den = den_w.sum(axis=1) + eps
+            if S_in is not None:
+                num = num + rq[b, h] @ S_in[b, h]
+            if z_in is not None:
+                den = den + fq[b, :, h, :] @ z_in[b, h]
+            gate = 1.0 / (1.0 + np.exp(-g[b, :, h, :]))
+            out[b, :, h, :] = gate * num / den[:, None]
+    return out
