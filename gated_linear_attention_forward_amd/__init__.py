@@ -1,4 +1,5 @@
-"""Gated bidirectional linear-attention token mixer for AMD MI355X (gfx950).
+"""Gated linear-attention token mixer for AMD MI355X (gfx950): the
+bidirectional mixer and its block-causal form with a carried state.
 
 The compute path is libgla.so (C ABI in include/gla.h, HIP kernels in
 csrc/); this package is its thin ctypes binding.
@@ -8,7 +9,11 @@ from .gla import (  # noqa: F401
     GlaError,
     RopeTables,
     alloc_workspace,
+    alloc_workspace_blocks,
     gla_forward,
+    gla_forward_blocks,
+    gla_forward_blocks_check,
+    gla_forward_blocks_ws,
     gla_forward_check,
     gla_forward_ws,
     gla_output_ws,
@@ -20,5 +25,6 @@ from .gla import (  # noqa: F401
     gla_state_ws,
     gla_strerror,
     gla_workspace_bytes,
+    gla_workspace_bytes_blocks,
     load_library,
 )

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <new>
@@ -38,38 +39,43 @@ DivMagic make_div_magic(uint32_t d) {
   return r;
 }
 
-// The state kernel wants a few blocks per compute unit in flight (256 CUs),
-// while every chunk adds one fp32 (D*D + D) partial per head.  The output
-// kernel reads only a bf16 copy of the state per block, so it takes more.
-Plan make_plan(int B, int N, int H, int D) {
+// The state kernel wants one block per compute unit (256 CUs), while every
+// chunk adds one fp32 (D*D + D) partial per head.  The output kernel reads
+// only a bf16 copy of the state per block, so it takes more, smaller blocks.
+// Chunks and output ranges never straddle an attention block.
+Plan make_plan(int B, int N, int H, int D, int block_tokens) {
   Plan p{};
   p.B = B; p.N = N; p.H = H; p.D = D;
   p.BH = B * H;
   if (p.BH == 0 || N == 0) return p;
-  // state chunks: whole 16-token tiles, about state_blocks(D) blocks in total
-  const int tiles = ceil_div(N, 16);
-  int C = state_blocks(D) / p.BH;
-  const int cmax = ceil_div(tiles, 4 * kStateMinTilesPerWave);
-  if (C > cmax) C = cmax;
-  if (C > kMaxChunks) C = kMaxChunks;
-  if (C < 1) C = 1;
-  p.L = ceil_div(tiles, C) * 16;
-  p.C = ceil_div(N, p.L);
+  p.BT = (block_tokens <= 0 || block_tokens >= N) ? N : block_tokens;
+  p.NB = ceil_div(N, p.BT);
+  const long long heads_blocks = (long long)p.BH * p.NB;
 
-  const int its = ceil_div(N, kOutputTileTokens);
-  int C2 = ceil_div(kOutputBlocks, p.BH);
-  if (C2 > its) C2 = its;
-  if (C2 < 1) C2 = 1;
-  p.L2 = ceil_div(its, C2) * kOutputTileTokens;
-  p.C2 = ceil_div(N, p.L2);
+  // state chunks: whole 16-token tiles, about kStateBlocks blocks in total
+  const int tiles = ceil_div(p.BT, 16);
+  long long cb = kStateBlocks / heads_blocks;
+  const int cmax = ceil_div(tiles, 4 * kStateMinTilesPerWave);
+  if (cb > cmax) cb = cmax;
+  if (cb > kMaxChunks) cb = kMaxChunks;
+  if (cb < 1) cb = 1;
+  p.L = ceil_div(tiles, (int)cb) * 16;
+  p.CB = ceil_div(p.BT, p.L);
+  p.C = p.NB * p.CB;
+
+  const int its = ceil_div(p.BT, kOutputTileTokens);
+  long long sub = (kOutputBlocks + heads_blocks - 1) / heads_blocks;
+  if (sub > its) sub = its;
+  if (sub < 1) sub = 1;
+  p.L2 = ceil_div(its, (int)sub) * kOutputTileTokens;
+  p.SUB = ceil_div(p.BT, p.L2);
+  p.C2 = p.NB * p.SUB;
 
   size_t off = 0;
   p.off_part = off;
   off = align_up(off + (size_t)p.BH * p.C * (size_t)(D * D + D) * sizeof(float), 256);
   p.off_sl = off;
-  off = align_up(off + (size_t)p.BH * (D + 2) * D * sizeof(uint16_t), 256);
-  p.off_z = off;
-  off = align_up(off + (size_t)p.BH * D * sizeof(float), 256);
+  off = align_up(off + (size_t)p.BH * p.NB * (D + 2) * D * sizeof(uint16_t), 256);
   p.ws_bytes = off;
   return p;
 }
@@ -129,14 +135,18 @@ int check_tensors(std::initializer_list<const void*> ins, const void* out, size_
   return GLA_OK;
 }
 
-// Kernel arguments of one call.  L is the block token range of the kernel the
-// arguments are for (it sets how many t-rows of the table a block stages).
-gla::KArgs kernel_args(const Plan& p, const gla_rope_tables* r, int L, void* ws) {
+// Kernel arguments of one call.  L and CB are the token range and ranges per
+// attention block of the kernel the arguments are for (L also sets how many
+// t-rows of the table a block stages).
+gla::KArgs kernel_args(const Plan& p, const gla_rope_tables* r, int L, int CB, void* ws) {
   gla::KArgs a{};
   a.N = p.N;
   a.H = p.H;
   a.slab_bytes = (uint32_t)((size_t)p.N * p.H * p.D * 2);
   a.L = L;
+  a.CB = CB;
+  a.BT = p.BT;
+  a.NB = p.NB;
   a.C = p.C;
   if (r) {
     a.cs = reinterpret_cast<const float2*>(r->cs);
@@ -152,7 +162,6 @@ gla::KArgs kernel_args(const Plan& p, const gla_rope_tables* r, int L, void* ws)
   char* w = static_cast<char*>(ws);
   a.part = reinterpret_cast<float*>(w + p.off_part);
   a.sl = reinterpret_cast<uint16_t*>(w + p.off_sl);
-  a.zf = reinterpret_cast<float*>(w + p.off_z);
   return a;
 }
 
@@ -220,19 +229,56 @@ int check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? GLA_OK : GLA_ERR_LAUNCH; }
 
+// Limits of the block plan: the output grid's second dimension and each
+// head's partial-state window (32-bit buffer offsets).
+int check_plan_limits(const Plan& p) {
+  if (p.C2 > 65535) return GLA_ERR_DIM;
+  if ((long long)p.C * (p.D * p.D + p.D) * 4 >= (1LL << 31)) return GLA_ERR_DIM;
+  return GLA_OK;
+}
+
+// Carried and returned states of the block-causal pass: each may be NULL;
+// given ones are 16-byte aligned, overlap none of the bf16 tensors, and the
+// returned ones overlap nothing but (exactly) their carried counterpart.
+int check_states(const float* S_in, const float* z_in, const float* S_out, const float* z_out,
+                 int B, int H, int D, std::initializer_list<const void*> tensors, size_t bytes) {
+  const size_t sb = (size_t)B * H * D * D * sizeof(float);
+  const size_t zb = (size_t)B * H * D * sizeof(float);
+  const void* ptr[4] = {S_in, z_in, S_out, z_out};
+  const size_t len[4] = {sb, zb, sb, zb};
+  for (int i = 0; i < 4; ++i) {
+    if (!ptr[i]) continue;
+    if (!aligned16(ptr[i])) return GLA_ERR_ALIGN;
+    for (const void* t : tensors)
+      if (bytes && overlap2(ptr[i], len[i], t, bytes)) return GLA_ERR_ALIAS;
+  }
+  // outputs against everything else, except the in-place pairs
+  for (int o = 2; o < 4; ++o) {
+    if (!ptr[o]) continue;
+    for (int i = 0; i < 4; ++i) {
+      if (i == o || !ptr[i]) continue;
+      if (i == o - 2 && ptr[i] == ptr[o]) continue;  // in-place update
+      if (overlap2(ptr[o], len[o], ptr[i], len[i])) return GLA_ERR_ALIAS;
+    }
+  }
+  return GLA_OK;
+}
+
 int run_state(const Plan& p, const void* k, const void* v, const gla_rope_tables* rope, void* ws,
-              float* S, float* z, void* stream) {
-  gla::KArgs a = kernel_args(p, rope, p.L, ws);
+              float* S, float* z, const float* S_in, const float* z_in, void* stream) {
+  gla::KArgs a = kernel_args(p, rope, p.L, p.CB, ws);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.S_out = S;
   a.z_out = z;
+  a.S_in = S_in;
+  a.z_in = z_in;
   return status_of(gla::launch_state(p, a, static_cast<hipStream_t>(stream)));
 }
 
 int run_output(const Plan& p, const void* q, const void* g, const gla_rope_tables* rope,
                void* out, void* ws, void* stream) {
-  gla::KArgs a = kernel_args(p, rope, p.L2, ws);
+  gla::KArgs a = kernel_args(p, rope, p.L2, p.SUB, ws);
   a.q = static_cast<const uint16_t*>(q);
   a.g = static_cast<const uint16_t*>(g);
   a.out = static_cast<uint16_t*>(out);
@@ -373,7 +419,7 @@ int gla_state_ws(const void* k, const void* v, const gla_rope_tables* rope, int 
   Plan p = gla::make_plan(B, N, H, D);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   if ((rc = rope_device_ok(rope))) return rc;
-  return run_state(p, k, v, rope, workspace, nullptr, nullptr, stream);
+  return run_state(p, k, v, rope, workspace, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 int gla_output_ws(const void* q, const void* g, const gla_rope_tables* rope, void* out, int B,
@@ -399,7 +445,7 @@ int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
   Plan p = gla::make_plan(B, N, H, D);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
   if ((rc = rope_device_ok(rope))) return rc;
-  rc = run_state(p, k, v, rope, workspace, nullptr, nullptr, stream);
+  rc = run_state(p, k, v, rope, workspace, nullptr, nullptr, nullptr, nullptr, stream);
   if (rc) return rc;
   return run_output(p, q, g, rope, out, workspace, stream);
 }
@@ -446,7 +492,76 @@ int gla_state(const void* k, const void* v, const gla_rope_tables* rope, float* 
   void* ws = nullptr;
   if ((rc = get_workspace(p.ws_bytes, stream, &ws))) return rc;
   if ((rc = rope_device_ok(rope))) return rc;
-  return run_state(p, k, v, rope, ws, S, z, stream);
+  return run_state(p, k, v, rope, ws, S, z, nullptr, nullptr, stream);
+}
+
+size_t gla_workspace_bytes_blocks(int B, int N, int H, int D, int block_tokens) {
+  size_t bytes = 0;
+  if (check_shape(B, N, H, D, &bytes) != GLA_OK || block_tokens < 1) return 0;
+  if (bytes == 0) return 0;
+  return gla::make_plan(B, N, H, D, block_tokens).ws_bytes;
+}
+
+int gla_forward_blocks_check(const void* q, const void* k, const void* v, const void* g,
+                             const gla_rope_tables* rope, const void* out, int B, int N, int H,
+                             int D, int block_tokens, const float* S_in, const float* z_in,
+                             const float* S_out, const float* z_out) {
+  size_t bytes = 0;
+  int rc = check_shape(B, N, H, D, &bytes);
+  if (rc) return rc;
+  if (block_tokens < 1) return GLA_ERR_DIM;
+  if ((long long)B * H == 0) return GLA_OK;
+  if ((rc = check_rope(rope, N, D))) return rc;
+  if (bytes) {
+    if ((rc = check_tensors({q, k, v, g}, out, bytes))) return rc;
+    if ((rc = check_plan_limits(gla::make_plan(B, N, H, D, block_tokens)))) return rc;
+  }
+  return check_states(S_in, z_in, S_out, z_out, B, H, D, {q, k, v, g, out}, bytes);
+}
+
+int gla_forward_blocks_ws(const void* q, const void* k, const void* v, const void* g,
+                          const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                          int block_tokens, const float* S_in, const float* z_in, float* S_out,
+                          float* z_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = gla_forward_blocks_check(q, k, v, g, rope, out, B, N, H, D, block_tokens, S_in, z_in,
+                                    S_out, z_out);
+  if (rc) return rc;
+  if ((long long)B * H == 0) return GLA_OK;
+  if (N == 0) {
+    // no tokens: the returned state is the carried one
+    if (!S_out && !z_out) return GLA_OK;
+    Plan p{};
+    p.B = B; p.N = 0; p.H = H; p.D = D; p.BH = B * H;
+    gla::KArgs a{};
+    a.H = H;
+    a.S_in = S_in; a.z_in = z_in; a.S_out = S_out; a.z_out = z_out;
+    return status_of(gla::launch_carry(p, a, static_cast<hipStream_t>(stream)));
+  }
+  Plan p = gla::make_plan(B, N, H, D, block_tokens);
+  if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  if ((rc = rope_device_ok(rope))) return rc;
+  rc = run_state(p, k, v, rope, workspace, S_out, z_out, S_in, z_in, stream);
+  if (rc) return rc;
+  return run_output(p, q, g, rope, out, workspace, stream);
+}
+
+int gla_forward_blocks(const void* q, const void* k, const void* v, const void* g,
+                       const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                       int block_tokens, const float* S_in, const float* z_in, float* S_out,
+                       float* z_out, void* stream) {
+  int rc = gla_forward_blocks_check(q, k, v, g, rope, out, B, N, H, D, block_tokens, S_in, z_in,
+                                    S_out, z_out);
+  if (rc) return rc;
+  if ((long long)B * H == 0) return GLA_OK;
+  void* ws = nullptr;
+  size_t wsb = 0;
+  if (N > 0) {
+    Plan p = gla::make_plan(B, N, H, D, block_tokens);
+    wsb = p.ws_bytes;
+    if ((rc = get_workspace(wsb, stream, &ws))) return rc;
+  }
+  return gla_forward_blocks_ws(q, k, v, g, rope, out, B, N, H, D, block_tokens, S_in, z_in, S_out,
+                               z_out, ws, wsb, stream);
 }
 
 }  // extern "C"

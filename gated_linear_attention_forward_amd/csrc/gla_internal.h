@@ -29,8 +29,14 @@ struct KArgs {
   uint16_t* out;
   int N, H;
   uint32_t slab_bytes;   // N * H * D * 2
-  int L;                 // tokens per block (state: chunk, output: block range)
-  int C;                 // state chunks per head
+  // token ranges: the N tokens of a head form NB attention blocks of BT tokens
+  // (the last may be shorter); a kernel's range index c covers block c / CB,
+  // piece c % CB, whose L tokens start at (c / CB) * BT + (c % CB) * L and
+  // end at the block's end at the latest
+  int L;                 // tokens per range (state: chunk, output: block range)
+  int CB;                // ranges per attention block for this kernel
+  int BT, NB;            // tokens per attention block, attention blocks per head
+  int C;                 // state chunks per head (NB * state CB)
   // RoPE: factorised (cos, sin) table, [T][Pt] | [Hh][Py] | [W][Px] float2
   const float2* cs;      // nullptr: RoPE off
   int T, Hh, W, Pt, Py, Px;
@@ -38,37 +44,46 @@ struct KArgs {
   int nt;                // t-rows of the table staged per block (when staged in LDS)
   // workspace
   float* part;           // [BH][C][D*D + D] fp32 chunk partials
-  uint16_t* sl;          // [BH][D + 2][D] bf16: S^T rows in output order, then z hi/lo rows
-  float* zf;             // [BH][D] fp32 z
-  float* S_out;          // optional fp32 S [BH][D][D]
-  float* z_out;          // optional fp32 z [BH][D]
+  uint16_t* sl;          // [BH][NB][D + 2][D] bf16: per attention block, the state
+                         // S^T rows in output order, then z hi/lo rows
+  float* S_out;          // optional fp32 S [BH][D][D] after the last block
+  float* z_out;          // optional fp32 z [BH][D] after the last block
+  const float* S_in;     // optional carried fp32 S [BH][D][D] (NULL: zero)
+  const float* z_in;     // optional carried fp32 z [BH][D] (NULL: zero)
 };
 
 // How one call splits its work.  Filled by make_plan on the host.
 struct Plan {
   int B, N, H, D;
   int BH;
-  // state kernel: C chunks per head of L tokens (L a multiple of its tile)
-  int C, L;
-  // output kernel: C2 blocks per head of L2 tokens (L2 a multiple of 64)
-  int C2, L2;
+  // attention blocks: NB per head of BT tokens (one block of N tokens for the
+  // bidirectional mixer)
+  int BT, NB;
+  // state kernel: CB chunks per attention block of L tokens (L a multiple of
+  // 16), C = NB * CB chunks per head
+  int CB, C, L;
+  // output kernel: SUB ranges per attention block of L2 tokens (L2 a multiple
+  // of 64), C2 = NB * SUB ranges per head
+  int SUB, C2, L2;
   // workspace byte offsets and total size
-  size_t off_part, off_sl, off_z, ws_bytes;
+  size_t off_part, off_sl, ws_bytes;
 };
 
-Plan make_plan(int B, int N, int H, int D);
+// block_tokens <= 0 or >= N: one attention block (the bidirectional mixer).
+Plan make_plan(int B, int N, int H, int D, int block_tokens = 0);
 
 // Kernel launchers (gla_kernels.hip).  Return the hipError_t of the launch.
 hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream);
+// The scan alone over zero blocks: S_out/z_out = S_in/z_in (or zero).
+hipError_t launch_carry(const Plan& p, KArgs a, hipStream_t stream);
 hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream);
 
 // Tile sizes the plan has to respect.
-constexpr int state_tile_tokens(int D) { return 8192 / D; }
 constexpr int kOutputTileTokens = 64;
 constexpr int kMaxChunks = 256;
 // Blocks of the state kernel the plan aims for: one per compute unit (256
 // compute units); a block's waves together hold a full D x D accumulator.
-constexpr int state_blocks(int D) { return D > 0 ? 256 : 256; }
+constexpr int kStateBlocks = 256;
 // Each wave of a state block should see at least this many 16-token tiles.
 constexpr int kStateMinTilesPerWave = 2;
 constexpr int kOutputBlocks = 2048;

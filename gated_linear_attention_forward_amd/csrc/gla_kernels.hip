@@ -163,6 +163,17 @@ __device__ __forceinline__ RowOff row_offsets(const KArgs& a, const TabView& tv,
   return r;
 }
 
+// Token range [n_begin, n_end) of range index c of a kernel: piece c % CB of
+// attention block c / CB.  A piece that starts past the last token (the last
+// block can be shorter than the others) is the empty range [N, N), which
+// stages no table rows and has no tiles.
+__device__ __forceinline__ void range_of(const KArgs& a, int c, int& n_begin, int& n_end) {
+  const int blk = c / a.CB;
+  const int blk_begin = blk * a.BT;
+  n_begin = min(blk_begin + (c - blk * a.CB) * a.L, a.N);
+  n_end = max(min(min(n_begin + a.L, blk_begin + a.BT), a.N), n_begin);
+}
+
 // Grid position of token n (row-major t, y, x).
 __device__ __forceinline__ void grid_pos(const KArgs& a, uint32_t n, int& t, int& y, int& x) {
   t = (int)fast_div(n, a.div_hw);
@@ -435,8 +446,8 @@ void state_kernel(KArgs a) {
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int n_begin = c * a.L;
-  const int n_end = min(a.N, n_begin + a.L);
+  int n_begin, n_end;
+  range_of(a, c, n_begin, n_end);
 
   TabView tv{};
   if (ROPE) tv = stage_table<D>(a, ltab, TLDS, n_begin, n_end);
@@ -784,8 +795,8 @@ void state_half_kernel(KArgs a) {
   const int c = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int n_begin = c * a.L;
-  const int n_end = min(a.N, n_begin + a.L);
+  int n_begin, n_end;
+  range_of(a, c, n_begin, n_end);
 
   TabView tv{};
   if (ROPE) tv = stage_table<D, 512>(a, ltab, TLDS, n_begin, n_end);
@@ -797,8 +808,11 @@ void state_half_kernel(KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Reduce kernel: per head, S = sum_c S_c and z = sum_c z_c over the C chunk
-// partials.  A block takes a tile of S (16 rows x 64 columns at D = 128);
+// Reduce kernel: per head and attention block b, the state up to the end of
+// block b: S_<=b = S_in + sum over chunks c of blocks <= b of S_c (likewise
+// z), accumulated block after block (for the bidirectional mixer: one block,
+// no carried state, S = sum_c S_c).  A block takes a tile of S (16 rows x 64
+// columns at D = 128);
 // each thread loads, for its 4 consecutive columns e of a row d, the P (a power of two
 // >= C, at most 32) chunk values at once -- loads past the head's C partials
 // fall outside the buffer and read as zero -- and adds them in a fixed
@@ -806,10 +820,10 @@ void state_half_kernel(KArgs a) {
 // first.  More than 32 chunks are summed 32 at a time, groups in order.  The
 // tile is transposed through LDS so the bf16 operand rows go out in 16-byte
 // runs.  The first tile's block also reduces z.
-// Outputs per head, in the output kernel's operand layout (D + 2 rows of D
-// bf16): row R(e) holds S[0..D)[e] (see out_row_of); row D holds bf16(z),
-// row D + 1 holds bf16(z - bf16(z)).  Optional fp32 copies of S and z go to
-// the caller.
+// Outputs per head and attention block, in the output kernel's operand
+// layout (D + 2 rows of D bf16): row R(e) holds S_<=b[0..D)[e] (see
+// out_row_of); row D holds bf16(z), row D + 1 holds bf16(z - bf16(z)).  The
+// fp32 state after the last block optionally goes to the caller.
 
 // Output-kernel operand row of value column e: with MB = D/16 column blocks,
 // row 16 j + c holds column MB c + j, so that lane column c of block j owns
@@ -865,50 +879,64 @@ __global__ __launch_bounds__(256) void reduce_kernel(KArgs a) {
   const int t = threadIdx.x;
   const int d0 = Rc::TR * (blockIdx.x / Rc::NTE), e0 = Rc::TE * (blockIdx.x % Rc::NTE);
   const uint32_t pstride = (uint32_t)(D * D + D) * 4u;  // bytes per chunk partial
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(a.part + (size_t)bh * a.C * (D * D + D), (uint32_t)a.C * pstride);
-  uint16_t* slh = a.sl + (size_t)bh * (D + 2) * D;
+  // attention block blk's chunks: blk * CB .. blk * CB + CB - 1; loads past the
+  // block's last chunk must read zero, so each block gets its own window
+  const uint32_t bstride = (uint32_t)a.CB * pstride;
 
   // row d0 + t / EQ, columns e0 + 4 (t % EQ) .. + 3
   const int dl = t / Rc::EQ, el = 4 * (t % Rc::EQ);
-  f32x4 s4[1];
-  tree_sum4<P, 1>(rs, (uint32_t)((d0 + dl) * D + e0 + el) * 4u, pstride, 0u, a.C, s4);
-  if (a.S_out)
-    *reinterpret_cast<f32x4*>(a.S_out + (size_t)bh * D * D + (size_t)(d0 + dl) * D + e0 + el) =
-        s4[0];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) tile[(el + k) * Rc::TP + dl] = s4[0][k];
-  __syncthreads();
-  // operand rows: for each tile column e, TR values over d in runs of 8 (16 bytes)
-  for (int item = t; item < Rc::TE * (Rc::TR / 8); item += 256) {
-    const int e = item / (Rc::TR / 8), dc = 8 * (item % (Rc::TR / 8));
-    const float* src = tile + e * Rc::TP + dc;
-    u32x4 w;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = pack_bf16(src[2 * k], src[2 * k + 1]);
-    *reinterpret_cast<u32x4*>(slh + (size_t)out_row_of<D>(e0 + e) * D + d0 + dc) = w;
-  }
+  const size_t sidx = (size_t)bh * D * D + (size_t)(d0 + dl) * D + e0 + el;
+  f32x4 acc = a.S_in ? *reinterpret_cast<const f32x4*>(a.S_in + sidx) : f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool zt = blockIdx.x == 0 && t < D / 4;  // threads that also carry z
+  f32x4 zacc = (zt && a.z_in) ? *reinterpret_cast<const f32x4*>(a.z_in + (size_t)bh * D + 4 * t)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (blockIdx.x == 0 && t < D / 4) {
-    f32x4 z4[1];
-    tree_sum4<P, 1>(rs, (uint32_t)(D * D + 4 * t) * 4u, pstride, 0u, a.C, z4);
-    *reinterpret_cast<f32x4*>(a.zf + (size_t)bh * D + 4 * t) = z4[0];
-    if (a.z_out) *reinterpret_cast<f32x4*>(a.z_out + (size_t)bh * D + 4 * t) = z4[0];
-    uint32_t hi[2], lo[2];
+  for (int blk = 0; blk < a.NB; ++blk) {
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(reinterpret_cast<const char*>(a.part + ((size_t)bh * a.C + (size_t)blk * a.CB) *
+                                                             (D * D + D)),
+                  bstride);
+    f32x4 s4[1];
+    tree_sum4<P, 1>(rb, (uint32_t)((d0 + dl) * D + e0 + el) * 4u, pstride, 0u, a.CB, s4);
+    acc = acc + s4[0];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const __bf16 h0 = (__bf16)z4[0][2 * k], h1 = (__bf16)z4[0][2 * k + 1];
-      const __bf16 l0 = (__bf16)(z4[0][2 * k] - (float)h0);
-      const __bf16 l1 = (__bf16)(z4[0][2 * k + 1] - (float)h1);
-      hi[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-      lo[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    for (int k = 0; k < 4; ++k) tile[(el + k) * Rc::TP + dl] = acc[k];
+    __syncthreads();
+    // operand rows: for each tile column e, TR values over d in runs of 8 (16 bytes)
+    uint16_t* slh = a.sl + ((size_t)bh * a.NB + blk) * (D + 2) * D;
+    for (int item = t; item < Rc::TE * (Rc::TR / 8); item += 256) {
+      const int e = item / (Rc::TR / 8), dc = 8 * (item % (Rc::TR / 8));
+      const float* src = tile + e * Rc::TP + dc;
+      u32x4 w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = pack_bf16(src[2 * k], src[2 * k + 1]);
+      *reinterpret_cast<u32x4*>(slh + (size_t)out_row_of<D>(e0 + e) * D + d0 + dc) = w;
     }
-    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<u32x2v*>(slh + (size_t)D * D + 4 * t) = u32x2v{hi[0], hi[1]};
-    *reinterpret_cast<u32x2v*>(slh + (size_t)(D + 1) * D + 4 * t) = u32x2v{lo[0], lo[1]};
+    if (zt) {
+      f32x4 z4[1];
+      tree_sum4<P, 1>(rb, (uint32_t)(D * D + 4 * t) * 4u, pstride, 0u, a.CB, z4);
+      zacc = zacc + z4[0];
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const __bf16 h0 = (__bf16)zacc[2 * k], h1 = (__bf16)zacc[2 * k + 1];
+        const __bf16 l0 = (__bf16)(zacc[2 * k] - (float)h0);
+        const __bf16 l1 = (__bf16)(zacc[2 * k + 1] - (float)h1);
+        hi[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lo[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      }
+      typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u32x2v*>(slh + (size_t)D * D + 4 * t) = u32x2v{hi[0], hi[1]};
+      *reinterpret_cast<u32x2v*>(slh + (size_t)(D + 1) * D + 4 * t) = u32x2v{lo[0], lo[1]};
+    }
+    __syncthreads();  // the tile is rewritten by the next block
   }
+  // the state after the last block (each element is read above and written
+  // here by the same thread, so S_out may be S_in)
+  if (a.S_out) *reinterpret_cast<f32x4*>(a.S_out + sidx) = acc;
+  if (zt && a.z_out) *reinterpret_cast<f32x4*>(a.z_out + (size_t)bh * D + 4 * t) = zacc;
 }
 
 // ---------------------------------------------------------------------------
@@ -991,11 +1019,13 @@ void output_kernel(KArgs a) {
   // a head count divisible by the 8 XCDs each head's blocks share one L2
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int n_begin = blockIdx.y * a.L;
-  const int n_end = min(a.N, n_begin + a.L);
+  int n_begin, n_end;
+  range_of(a, blockIdx.y, n_begin, n_end);
+  const int blk = blockIdx.y / a.CB;  // attention block of the range
 
-  // stage the S^T rows and the z rows
-  const uint4* src = reinterpret_cast<const uint4*>(a.sl + (size_t)bh * ROWS * D);
+  // stage the block's S^T rows and z rows
+  const uint4* src =
+      reinterpret_cast<const uint4*>(a.sl + ((size_t)bh * a.NB + blk) * ROWS * D);
   for (int i = tid; i < ROWS * D / 8; i += 256) {
     const int row = i / (D / 8), u = i % (D / 8);
     *reinterpret_cast<uint4*>(sS + row * PITCH + 16 * u) = src[i];
@@ -1188,9 +1218,9 @@ hipError_t launch_state_d(const Plan& p, KArgs a, hipStream_t stream) {
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.C <= 8)
+  if (p.CB <= 8)
     launch_reduce<D, 8>(p, a, stream);
-  else if (p.C <= 16)
+  else if (p.CB <= 16)
     launch_reduce<D, 16>(p, a, stream);
   else
     launch_reduce<D, 32>(p, a, stream);
@@ -1220,6 +1250,17 @@ hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream) {
     case 128: return launch_state_d<128>(p, a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_carry(const Plan& p, KArgs a, hipStream_t stream) {
+  a.NB = 0;
+  switch (p.D) {
+    case 32: launch_reduce<32, 8>(p, a, stream); break;
+    case 64: launch_reduce<64, 8>(p, a, stream); break;
+    case 128: launch_reduce<128, 8>(p, a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream) {

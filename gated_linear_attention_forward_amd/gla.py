@@ -31,6 +31,8 @@ EXPORTS = (
     "gla_strerror", "gla_rope_table_floats", "gla_rope_fill_host", "gla_rope_create",
     "gla_rope_destroy", "gla_workspace_bytes", "gla_forward", "gla_forward_ws",
     "gla_forward_check", "gla_state_ws", "gla_output_ws", "gla_state",
+    "gla_forward_blocks", "gla_forward_blocks_ws", "gla_workspace_bytes_blocks",
+    "gla_forward_blocks_check",
 )
 
 
@@ -80,6 +82,10 @@ def load_library():
         "gla_state_ws": ([vp, vp, rp] + [i32] * 4 + [vp, sz, vp], i32),
         "gla_output_ws": ([vp, vp, rp, vp] + [i32] * 4 + [vp, sz, vp], i32),
         "gla_state": ([vp, vp, rp, vp, vp] + [i32] * 4 + [vp], i32),
+        "gla_forward_blocks": ([vp] * 4 + [rp, vp] + [i32] * 5 + [vp] * 4 + [vp], i32),
+        "gla_forward_blocks_ws": ([vp] * 4 + [rp, vp] + [i32] * 5 + [vp] * 4 + [vp, sz, vp], i32),
+        "gla_workspace_bytes_blocks": ([i32] * 5, sz),
+        "gla_forward_blocks_check": ([vp] * 4 + [rp, vp] + [i32] * 5 + [vp] * 4, i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -279,3 +285,85 @@ def gla_state(k, v, rope=None, stream=None):
                                      z.data_ptr(), B, N, H, D, _stream_handle(stream, k.device)),
             "gla_state")
     return S, z
+
+
+# ---------------------------------------------------------------------------
+# block-causal pass with a carried state
+
+
+def _check_state(name, t, shape, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+        raise TypeError(f"{name} must be a float32 torch.Tensor")
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {tuple(shape)} tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, q on {device}")
+    return t.data_ptr()
+
+
+def gla_workspace_bytes_blocks(B: int, N: int, H: int, D: int, block_tokens: int) -> int:
+    return load_library().gla_workspace_bytes_blocks(B, N, H, D, block_tokens)
+
+
+def alloc_workspace_blocks(B, N, H, D, block_tokens, device=None) -> torch.Tensor:
+    """A torch-owned uint8 device buffer large enough for gla_forward_blocks_ws."""
+    return torch.empty(max(gla_workspace_bytes_blocks(B, N, H, D, block_tokens), 256),
+                       dtype=torch.uint8, device=device)
+
+
+def gla_forward_blocks_check(q, k, v, g, rope, out, B, N, H, D, block_tokens,
+                             S_in=None, z_in=None, S_out=None, z_out=None) -> int:
+    """Status of the library's argument validation (pointers as integers)."""
+    return load_library().gla_forward_blocks_check(q, k, v, g, _rope_ptr(rope), out, B, N, H, D,
+                                                   block_tokens, S_in, z_in, S_out, z_out)
+
+
+def _blocks_args(q, k, v, g, out, S_in, z_in, S_out, z_out):
+    _check_bf16("q", q)
+    for name, t in (("k", k), ("v", v), ("g", g)):
+        _check_bf16(name, t, q.shape)
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    B, N, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bf16("out", out, q.shape)
+    ptrs = [_check_state("S_in", S_in, (B, H, D, D), q.device),
+            _check_state("z_in", z_in, (B, H, D), q.device),
+            _check_state("S_out", S_out, (B, H, D, D), q.device),
+            _check_state("z_out", z_out, (B, H, D), q.device)]
+    return out, ptrs
+
+
+def gla_forward_blocks(q, k, v, g, rope, block_tokens: int, S_in=None, z_in=None,
+                       S_out=None, z_out=None, out=None, stream=None):
+    """Block-causal pass: token n of block n // block_tokens sees its own and
+    every earlier block plus the carried state (S_in, z_in); the state after
+    the last block goes to S_out, z_out (fp32; S_out may be S_in for an
+    in-place update).  Returns out (bf16 [B, N, H, D])."""
+    out, ptrs = _blocks_args(q, k, v, g, out, S_in, z_in, S_out, z_out)
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_forward_blocks(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                              g.data_ptr(), _rope_ptr(rope), out.data_ptr(),
+                                              B, N, H, D, int(block_tokens), *ptrs,
+                                              _stream_handle(stream, q.device)),
+            "gla_forward_blocks")
+    return out
+
+
+def gla_forward_blocks_ws(q, k, v, g, rope, block_tokens: int, ws: torch.Tensor, S_in=None,
+                          z_in=None, S_out=None, z_out=None, out=None, stream=None):
+    out, ptrs = _blocks_args(q, k, v, g, out, S_in, z_in, S_out, z_out)
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_forward_blocks_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                 g.data_ptr(), _rope_ptr(rope), out.data_ptr(),
+                                                 B, N, H, D, int(block_tokens), *ptrs,
+                                                 ws.data_ptr(), ws.numel() * ws.element_size(),
+                                                 _stream_handle(stream, q.device)),
+            "gla_forward_blocks_ws")
+    return out

@@ -106,7 +106,7 @@ int gla_rope_destroy(gla_rope_tables* tables);
  */
 
 /* Bytes of device workspace gla_forward_ws needs for this shape (per-chunk
- * partial states, the reduced state and the normaliser).  0 for N*B*H == 0. */
+ * partial states and the reduced bf16 state).  0 for N*B*H == 0. */
 size_t gla_workspace_bytes(int B, int N, int H, int D);
 
 /* Runs the mixer: out = o as defined above, bf16, round-to-nearest-even.
@@ -152,6 +152,61 @@ int gla_output_ws(const void* q, const void* g, const gla_rope_tables* rope, voi
  * are then set to zero).  Uses the library-owned workspace. */
 int gla_state(const void* k, const void* v, const gla_rope_tables* rope, float* S, float* z,
               int B, int N, int H, int D, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Block-causal pass with a carried state.
+ *
+ * The constant-memory KV cache of block linear attention ("SANA-Video_2B_720p"
+ * model card, innovation (2): blocks are generated one after another, and the
+ * cumulative state of linear attention carries the context of everything
+ * before at a fixed memory cost).  The N tokens of a head form blocks of
+ * block_tokens tokens in order (the last block may be shorter).  Token n in
+ * block b = n / block_tokens sees every token up to the end of its own block,
+ * plus a carried state (S_in, z_in) from earlier calls:
+ *
+ *     S_<=b = S_in + sum over tokens m with m / block_tokens <= b of
+ *             (R_m phi(k_m)) v_m^T
+ *     z_<=b = z_in + sum over the same tokens of phi(k_m)
+ *     o_n   = sigmoid(g_n) * ((R_n phi(q_n))^T S_<=b) / (phi(q_n) . z_<=b + 1e-6)
+ *
+ * The state after the last block goes to S_out, z_out; a next call takes it
+ * as its carried state (with the RoPE tables' t0 moved on by the frames of
+ * this call).  block_tokens >= N with no carried state equals gla_forward.
+ *
+ * q, k, v, g, out, rope: as for gla_forward.  block_tokens >= 1.
+ * S_in, S_out: device fp32 [B, H, D, D] (element S[d][e] at
+ * ((b*H + h)*D + d)*D + e); z_in, z_out: device fp32 [B, H, D].  Each may be
+ * NULL (a NULL carried state is zero; a NULL returned state is not
+ * written).  Given ones are 16-byte aligned and overlap no bf16 tensor;
+ * S_out may be S_in itself (and z_out z_in), which updates the state in
+ * place, but may not partly overlap it or any other state.  The caller owns
+ * all of them.
+ * Limits (GLA_ERR_DIM): at most 65535 blocks per head, and each head's
+ * partial states (one D*D + D fp32 set per state chunk) under 2 GiB.  N == 0 with B*H > 0 only copies the carried state to
+ * the returned one (zero if none).  Uses a library-owned workspace as
+ * gla_forward does.  Results are bitwise reproducible. */
+int gla_forward_blocks(const void* q, const void* k, const void* v, const void* g,
+                       const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                       int block_tokens, const float* S_in, const float* z_in, float* S_out,
+                       float* z_out, void* stream);
+
+/* Workspace bytes gla_forward_blocks_ws needs: per-chunk partial states and
+ * one bf16 state per head and block.  0 for B*N*H == 0 or block_tokens < 1. */
+size_t gla_workspace_bytes_blocks(int B, int N, int H, int D, int block_tokens);
+
+/* gla_forward_blocks with a caller-owned workspace (>= the size
+ * gla_workspace_bytes_blocks returns, 256-byte aligned; may be NULL when
+ * N == 0).  Never allocates. */
+int gla_forward_blocks_ws(const void* q, const void* k, const void* v, const void* g,
+                          const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                          int block_tokens, const float* S_in, const float* z_in, float* S_out,
+                          float* z_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Argument validation of gla_forward_blocks alone (no HIP call). */
+int gla_forward_blocks_check(const void* q, const void* k, const void* v, const void* g,
+                             const gla_rope_tables* rope, const void* out, int B, int N, int H,
+                             int D, int block_tokens, const float* S_in, const float* z_in,
+                             const float* S_out, const float* z_out);
 
 #ifdef __cplusplus
 }

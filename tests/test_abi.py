@@ -139,3 +139,71 @@ def test_rope_fill_rejects_bad_args():
         gla.gla_rope_fill_host(0, 1, 1, 128)
     with pytest.raises(gla.GlaError):
         gla.gla_rope_fill_host(2, 2, 2, 127)
+
+
+# ---------------------------------------------------------------------------
+# block-causal entry point: validation without a GPU
+
+SB = 2 * 128 * 128 * 4  # S bytes for B=1, H=2, D=128
+ZB = 2 * 128 * 4
+
+
+def bcheck(block_tokens=16, S_in=0, z_in=0, S_out=0, z_out=0, **kw):
+    args = dict(q=A, k=2 * A, v=3 * A, g=4 * A, rope=None, out=5 * A, B=1, N=64, H=2, D=128)
+    args.update(kw)
+    return gla.gla_forward_blocks_check(args["q"], args["k"], args["v"], args["g"], args["rope"],
+                                        args["out"], args["B"], args["N"], args["H"], args["D"],
+                                        block_tokens, S_in or None, z_in or None, S_out or None,
+                                        z_out or None)
+
+
+def test_blocks_valid_arguments():
+    assert bcheck() == 0
+    assert bcheck(block_tokens=1) == 0
+    assert bcheck(block_tokens=10**6) == 0
+    assert bcheck(S_in=8 * A, z_in=9 * A, S_out=10 * A, z_out=11 * A) == 0
+
+
+def test_blocks_bad_block_length():
+    assert bcheck(block_tokens=0) == glamod.GLA_ERR_DIM
+    assert bcheck(block_tokens=-3) == glamod.GLA_ERR_DIM
+
+
+def test_blocks_state_alignment_and_aliasing():
+    assert bcheck(S_in=8 * A + 4) == glamod.GLA_ERR_ALIGN
+    assert bcheck(z_out=11 * A + 8) == glamod.GLA_ERR_ALIGN
+    # in-place update of the carried state is allowed
+    assert bcheck(S_in=8 * A, S_out=8 * A, z_in=9 * A, z_out=9 * A) == 0
+    # partial overlap of the returned and carried states is not
+    assert bcheck(S_in=8 * A, S_out=8 * A + 16) == glamod.GLA_ERR_ALIAS
+    # a state over a bf16 tensor, or the two returned states over each other
+    assert bcheck(S_out=A + 64) == glamod.GLA_ERR_ALIAS
+    assert bcheck(S_in=5 * A) == glamod.GLA_ERR_ALIAS
+    assert bcheck(S_out=10 * A, z_out=10 * A + SB - 16) == glamod.GLA_ERR_ALIAS
+    assert bcheck(S_out=10 * A, z_out=10 * A + SB) == 0
+
+
+def test_blocks_empty_sequence_needs_no_tensors():
+    # N == 0: nothing is read but the carried state
+    assert bcheck(N=0, q=0, k=0, v=0, g=0, out=0, S_in=8 * A, S_out=10 * A) == 0
+    assert bcheck(B=0) == 0
+
+
+def test_blocks_limits():
+    far = dict(q=100 * A, k=200 * A, v=300 * A, g=400 * A, out=500 * A)
+    # 65536 blocks of one token each exceed the output grid (D = 32: the
+    # partial states stay small)
+    assert bcheck(N=65536, H=1, D=32, block_tokens=1, **far) == glamod.GLA_ERR_DIM
+    assert bcheck(N=65535, H=1, D=32, block_tokens=1, **far) == 0
+    # D = 128: 40000 one-token blocks need 2.6 GB of partial states per head
+    assert bcheck(N=40000, H=1, block_tokens=1, **far) == glamod.GLA_ERR_DIM
+    assert bcheck(N=40000, H=1, block_tokens=16, **far) == 0
+
+
+def test_blocks_workspace_size():
+    one = gla.gla_workspace_bytes_blocks(2, 22000, 20, 128, 22000)
+    assert one == gla.gla_workspace_bytes(2, 22000, 20, 128)
+    five = gla.gla_workspace_bytes_blocks(2, 22000, 20, 128, 4400)
+    assert five >= 40 * 5 * (128 * 128 + 128) * 4 + 40 * 5 * 130 * 128 * 2
+    assert five % 256 == 0
+    assert gla.gla_workspace_bytes_blocks(2, 22000, 20, 128, 0) == 0
