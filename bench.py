@@ -110,6 +110,61 @@ def copy_calibration(dev, nbytes=1 << 30):
     del src, dst
 
 
+def block_bench(args, w, gla, dev, tensors, out, rope, stream):
+    """Block-causal pass: K passes of gla_forward_blocks_ws on the workload in
+    blocks of args.block_frames latent frames, with the carried state read
+    and updated in place (as a generator producing block after block would).
+    Prints one JSON line; the roofline is the whole pass against 10*D bytes
+    per (token, head) plus the state read and written."""
+    import torch
+    qd, kd, vd, gd = tensors
+    L = args.block_frames * w.Hh * w.W
+    S = torch.zeros((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    z = torch.zeros((w.B, w.H, w.D), dtype=torch.float32, device=dev)
+    ws = gla.alloc_workspace_blocks(w.B, w.N, w.H, w.D, L, dev)
+
+    def step():
+        gla.gla_forward_blocks_ws(qd, kd, vd, gd, rope, L, ws, S, z, S, z, out, stream)
+
+    log(f"bench: block-causal, {args.block_frames} frames ({L} tokens) per block; "
+        f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    units = w.B * w.N * w.H
+    nbytes = 10 * w.D * units + 2 * w.B * w.H * (w.D * w.D + w.D) * 4
+    achieved = nbytes / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": "block-causal gated linear-attn tokens/s per layer (carried state); "
+                  "achieved HBM GB/s vs peak",
+        "value": w.B * w.N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "D": w.D,
+                   "grid": [w.T, w.Hh, w.W], "block_frames": args.block_frames,
+                   "block_tokens": L, "blocks": -(-w.N // L), "parallelism": "single-gpu"},
+        "roofline": {"kernel": "whole pass (state, scan, output kernels)", "bound": "hbm",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "algorithmic_bytes": nbytes, "avg_ms": ms_step},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +174,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (for hardware byte counters)")
+    ap.add_argument("--block-frames", type=int, default=0,
+                    help="time the block-causal pass (gla_forward_blocks) in blocks of this "
+                         "many latent frames, carrying the state in place, instead of the "
+                         "bidirectional mixer")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -143,6 +202,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.calibrate_copy:
         copy_calibration(dev)
+    if args.block_frames > 0:
+        block_bench(args, w, gla, dev, (qd, kd, vd, gd), out, rope, stream)
+        return
 
     def step(ev=None):
         if ev is not None:

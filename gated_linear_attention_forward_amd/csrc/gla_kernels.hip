@@ -860,6 +860,25 @@ __device__ __forceinline__ void tree_sum4(__amdgpu_buffer_rsrc_t rs, uint32_t of
   }
 }
 
+// The P chunk vectors of one column group (loads past the window read zero).
+template <int P>
+__device__ __forceinline__ void load_chunks(__amdgpu_buffer_rsrc_t rs, uint32_t off0,
+                                            uint32_t cstride, f32x4 (&x)[P]) {
+#pragma unroll
+  for (int cc = 0; cc < P; ++cc)
+    x[cc] = __builtin_bit_cast(f32x4, load16(rs, off0 + (uint32_t)cc * cstride));
+}
+
+// Their fixed pairwise tree sum (the same order tree_sum4 uses for one group).
+template <int P>
+__device__ __forceinline__ f32x4 sum_chunks(f32x4 (&x)[P]) {
+#pragma unroll
+  for (int w = P / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int cc = 0; cc < w; ++cc) x[cc] = x[2 * cc] + x[2 * cc + 1];
+  return x[0];
+}
+
 template <int D>
 struct RedCfg {
   static constexpr int TE = D < 64 ? D : 64;   // tile columns (e)
@@ -891,14 +910,42 @@ __global__ __launch_bounds__(256) void reduce_kernel(KArgs a) {
   f32x4 zacc = (zt && a.z_in) ? *reinterpret_cast<const f32x4*>(a.z_in + (size_t)bh * D + 4 * t)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Block blk + 1's partials are loaded while block blk is summed, written
+  // and transposed (when a block has at most PF_MAX chunks: one group).
+  constexpr int PF_MAX = 16;
+  auto window = [&](int blk) {
+    return make_rsrc(reinterpret_cast<const char*>(a.part + ((size_t)bh * a.C +
+                                                             (size_t)blk * a.CB) * (D * D + D)),
+                     bstride);
+  };
+  const uint32_t soff = (uint32_t)((d0 + dl) * D + e0 + el) * 4u;
+  const uint32_t zoff = (uint32_t)(D * D + 4 * t) * 4u;
+  f32x4 xs[P <= PF_MAX ? P : 1], xz[P <= PF_MAX ? P : 1];
+  if constexpr (P <= PF_MAX) {
+    if (a.NB > 0) {
+      load_chunks<P>(window(0), soff, pstride, xs);
+      if (zt) load_chunks<P>(window(0), zoff, pstride, xz);
+    }
+  }
   for (int blk = 0; blk < a.NB; ++blk) {
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(reinterpret_cast<const char*>(a.part + ((size_t)bh * a.C + (size_t)blk * a.CB) *
-                                                             (D * D + D)),
-                  bstride);
-    f32x4 s4[1];
-    tree_sum4<P, 1>(rb, (uint32_t)((d0 + dl) * D + e0 + el) * 4u, pstride, 0u, a.CB, s4);
-    acc = acc + s4[0];
+    f32x4 s_blk, z_blk = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (P <= PF_MAX) {
+      s_blk = sum_chunks<P>(xs);
+      if (zt) z_blk = sum_chunks<P>(xz);
+      if (blk + 1 < a.NB) {
+        load_chunks<P>(window(blk + 1), soff, pstride, xs);
+        if (zt) load_chunks<P>(window(blk + 1), zoff, pstride, xz);
+      }
+    } else {
+      f32x4 s4[1];
+      tree_sum4<P, 1>(window(blk), soff, pstride, 0u, a.CB, s4);
+      s_blk = s4[0];
+      if (zt) {
+        tree_sum4<P, 1>(window(blk), zoff, pstride, 0u, a.CB, s4);
+        z_blk = s4[0];
+      }
+    }
+    acc = acc + s_blk;
 #pragma unroll
     for (int k = 0; k < 4; ++k) tile[(el + k) * Rc::TP + dl] = acc[k];
     __syncthreads();
@@ -913,9 +960,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(KArgs a) {
       *reinterpret_cast<u32x4*>(slh + (size_t)out_row_of<D>(e0 + e) * D + d0 + dc) = w;
     }
     if (zt) {
-      f32x4 z4[1];
-      tree_sum4<P, 1>(rb, (uint32_t)(D * D + 4 * t) * 4u, pstride, 0u, a.CB, z4);
-      zacc = zacc + z4[0];
+      zacc = zacc + z_blk;
       uint32_t hi[2], lo[2];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
