@@ -74,6 +74,9 @@ def _load():
     lib.gla_oracle_forward_blocks.argtypes = ([u16p] * 4 + [c_int] * 4 + grid +
                                               [c_double, c_long, dp, dp, dp, dp, dp])
     lib.gla_oracle_forward_blocks.restype = c_int
+    lib.gla_oracle_softmax_rows.argtypes = ([u16p] * 4 + [c_int] * 4 + grid +
+                                            [c_int, c_int, lp, c_long, dp])
+    lib.gla_oracle_softmax_rows.restype = c_int
     _lib = lib
     return lib
 
@@ -215,3 +218,32 @@ def forward_blocks(q, k, v, g, grid: Grid | None, block_tokens: int, S_in=None, 
         _p(z_in, ctypes.c_double) if z_in is not None else null,
         _p(out, ctypes.c_double), _p(S_out, ctypes.c_double), _p(z_out, ctypes.c_double)))
     return out, S_out, z_out
+
+
+def softmax_rows(q, k, v, g, grid: Grid | None, b: int, h: int, token_rows) -> np.ndarray:
+    """Gated softmax anchor attention (see gla_oracle_softmax_rows): outputs
+    [len(token_rows), D] of head (b, h) at the given query tokens, fp64."""
+    q, k, v, g = (as_bits(a) for a in (q, k, v, g))
+    B, N, H, D = q.shape
+    for a in (k, v, g):
+        if a.shape != q.shape:
+            raise ValueError("q, k, v, g must share one [B, N, H, D] shape")
+    r = np.ascontiguousarray(token_rows, dtype=np.int64)
+    out = np.empty((r.shape[0], D), np.float64)
+    _check(_load().gla_oracle_softmax_rows(*(_p(a, ctypes.c_uint16) for a in (q, k, v, g)),
+                                           B, N, H, D, *_grid_args(grid), b, h,
+                                           _p(r, ctypes.c_long), r.shape[0],
+                                           _p(out, ctypes.c_double)))
+    return out
+
+
+def softmax_forward(q, k, v, g, grid: Grid | None) -> np.ndarray:
+    """Every output of the gated softmax anchor attention: [B, N, H, D] fp64."""
+    q = as_bits(q)
+    B, N, H, D = q.shape
+    out = np.empty((B, N, H, D), np.float64)
+    rows_all = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            out[b, :, h] = softmax_rows(q, k, v, g, grid, b, h, rows_all)
+    return out

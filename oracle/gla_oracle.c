@@ -23,7 +23,9 @@
  * "Bidirectional" is read as: no causal mask, S and z sum over all N tokens.
  * gla_oracle_forward_blocks adds the block-causal form with a carried state
  * (the constant-memory KV cache for block linear attention of the
- * "SANA-Video_2B_720p" model card, innovation (2)); see its comment.
+ * "SANA-Video_2B_720p" model card, innovation (2)); gla_oracle_softmax_rows
+ * the gated softmax anchor attention of the other quarter of the layers; see
+ * their comments.
  *
  * RoPE reading (the pages only name "Wan 3D rotary position embeddings"):
  *   - the D/2 rotation pairs are (2i, 2i+1), interleaved;
@@ -387,5 +389,96 @@ int gla_oracle_forward_blocks(const uint16_t* q, const uint16_t* k, const uint16
       err = r;
     }
   }
+  return err;
+}
+
+/* ---------------------------------------------------------------------------
+ * Gated softmax anchor attention: the dense softmax layers of the hybrid
+ * ("SANA-Video 2.0" NVlabs Sana docs, section Architecture: a quarter of the
+ * layers are dense softmax anchors, 10 heads x 256 at 5B and 16 x 256 at
+ * 14B, with the same Wan 3D rotary embeddings; "SANA-Video 2.0: Hybrid
+ * Linear Attention with Attention Residuals for Efficient Video Generation"
+ * (mlsanity index), Abstract: periodic gated-softmax anchors).  The reading
+ * taken, per (b, h), with no mask:
+ *     rq_n = R_n q_n,  rk_m = R_m k_m            (RoPE on q and k themselves)
+ *     s_nm = rq_n . rk_m / sqrt(D)
+ *     o_n  = sigmoid(g_n) * sum_m softmax_m(s_nm) v_m
+ * softmax_m(s_nm) = exp(s_nm - max_m s_nm) / sum_m exp(s_nm - max_m s_nm),
+ * two passes over m in order. */
+
+/* Outputs of selected query tokens of head (b, h).  out: [nrows, D]. */
+int gla_oracle_softmax_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const uint16_t* g, int B, int N, int H, int D,
+                            int rope, int T, int Hh, int W, double theta, long t0, long y0,
+                            long x0, int b, int h, const long* rows, long nrows, double* out) {
+  oracle_grid g0;
+  const oracle_grid* gr;
+  make_grid(rope, T, Hh, W, theta, t0, y0, x0, &g0, &gr);
+  int rc = check_args(B, N, H, D, gr);
+  if (rc) return rc;
+  if (b < 0 || b >= B || h < 0 || h >= H || N < 1) return ORACLE_ERR_ARG;
+  for (long i = 0; i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= N) return ORACLE_ERR_ARG;
+  /* every key rotated once */
+  double* rk = malloc(sizeof(double) * (size_t)N * D);
+  if (!rk) return ORACLE_ERR_ALLOC;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* u = malloc(sizeof(double) * D);
+    if (!u) {
+#pragma omp critical
+      err = ORACLE_ERR_ALLOC;
+    } else {
+#pragma omp for schedule(static)
+      for (long m = 0; m < N; ++m) {
+        load_row(k, N, H, D, b, h, m, u);
+        rotate(D, gr, m, u, rk + m * (long)D);
+      }
+    }
+    free(u);
+  }
+  const double scale = 1.0 / sqrt((double)D);
+  if (!err) {
+#pragma omp parallel
+    {
+      double* qr = malloc(sizeof(double) * D);
+      double* rq = malloc(sizeof(double) * D);
+      double* gv = malloc(sizeof(double) * D);
+      double* vr = malloc(sizeof(double) * D);
+      double* s = malloc(sizeof(double) * (size_t)N);
+      double* acc = malloc(sizeof(double) * D);
+      if (!qr || !rq || !gv || !vr || !s || !acc) {
+#pragma omp critical
+        err = ORACLE_ERR_ALLOC;
+      } else {
+#pragma omp for schedule(dynamic, 1)
+        for (long i = 0; i < nrows; ++i) {
+          long n = rows[i];
+          load_row(q, N, H, D, b, h, n, qr);
+          load_row(g, N, H, D, b, h, n, gv);
+          rotate(D, gr, n, qr, rq);
+          double mx = -INFINITY;
+          for (long m = 0; m < N; ++m) {
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += rq[d] * rk[m * (long)D + d];
+            s[m] = dot * scale;
+            if (s[m] > mx) mx = s[m];
+          }
+          double den = 0.0;
+          for (int e = 0; e < D; ++e) acc[e] = 0.0;
+          for (long m = 0; m < N; ++m) {
+            double p = exp(s[m] - mx);
+            den += p;
+            load_row(v, N, H, D, b, h, m, vr);
+            for (int e = 0; e < D; ++e) acc[e] += p * vr[e];
+          }
+          for (int e = 0; e < D; ++e) out[i * D + e] = sigmoid(gv[e]) * acc[e] / den;
+        }
+      }
+      free(qr); free(rq); free(gv); free(vr); free(s); free(acc);
+    }
+  }
+  free(rk);
   return err;
 }

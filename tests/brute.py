@@ -122,3 +122,25 @@ def forward_blocks(q, k, v, g, grid, L: int, S_in=None, z_in=None, eps: float = 
             gate = 1.0 / (1.0 + np.exp(-g[b, :, h, :]))
             out[b, :, h, :] = gate * num / den[:, None]
     return out
+
+
+def softmax_attention(q, k, v, g, grid=None) -> np.ndarray:
+    """Gated softmax attention in numpy: o = sigmoid(g) * softmax(rq rk^T /
+    sqrt(D)) v, with RoPE on q and k done as complex rotation."""
+    B, N, H, D = q.shape
+    qt = np.transpose(q, (0, 2, 1, 3))
+    kt = np.transpose(k, (0, 2, 1, 3))
+    if grid is not None:
+        ang = angles(D, *grid)
+        qt = rotate_complex(qt, ang)
+        kt = rotate_complex(kt, ang)
+    out = np.empty_like(q)
+    for b in range(B):
+        for h in range(H):
+            s = qt[b, h] @ kt[b, h].T / np.sqrt(D)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)
+            gate = 1.0 / (1.0 + np.exp(-g[b, :, h, :]))
+            out[b, :, h, :] = gate * (p @ v[b, :, h, :])
+    return out
