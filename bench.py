@@ -70,7 +70,7 @@ def cpu_baseline(w, q, k, v, g, min_seconds=10.0):
 
 COUNTERS = os.path.join(ROOT, "profiles", "counters_5b_720p_193f.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_linear_attention_forward_amd", "csrc", f)
-                  for f in ("gla_kernels.hip", "gla_api.cpp", "gla_internal.h")]
+                  for f in ("gla_kernels.hip", "gla_device.h", "gla_api.cpp", "gla_internal.h")]
 
 
 def kernel_source_digest():

@@ -1,5 +1,6 @@
 """Gated linear-attention token mixer for AMD MI355X (gfx950): the
-bidirectional mixer and its block-causal form with a carried state.
+bidirectional mixer, its block-causal form with a carried state, and the
+gated softmax anchor attention of the hybrid's other layers.
 
 The compute path is libgla.so (C ABI in include/gla.h, HIP kernels in
 csrc/); this package is its thin ctypes binding.
@@ -10,6 +11,7 @@ from .gla import (  # noqa: F401
     RopeTables,
     alloc_workspace,
     alloc_workspace_blocks,
+    alloc_workspace_softmax,
     gla_forward,
     gla_forward_blocks,
     gla_forward_blocks_check,
@@ -21,6 +23,10 @@ from .gla import (  # noqa: F401
     gla_rope_destroy,
     gla_rope_fill_host,
     gla_rope_table_floats,
+    gla_softmax_forward,
+    gla_softmax_forward_check,
+    gla_softmax_forward_ws,
+    gla_softmax_workspace_bytes,
     gla_state,
     gla_state_ws,
     gla_strerror,

@@ -36,14 +36,17 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    kobj = os.path.join(BUILD, "gla_kernels.o")
+    objs = []
+    for src in ("gla_kernels.hip", "gla_softmax.hip"):
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        _run(["hipcc", *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
     aobj = os.path.join(BUILD, "gla_api.o")
-    _run(["hipcc", *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
-          os.path.join(CSRC, "gla_kernels.hip"), "-o", kobj], verbose)
     _run(["hipcc", *HOST_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
           os.path.join(CSRC, "gla_api.cpp"), "-o", aobj], verbose)
     tmp = LIB + ".tmp"
-    _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, "-o", tmp], verbose)
+    _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, aobj, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -342,7 +342,7 @@ int gla_rope_create(int T, int Hh, int W, int D, double theta, int t0, int y0, i
                     void* stream, gla_rope_tables** out) {
   if (!out) return GLA_ERR_NULL;
   *out = nullptr;
-  if (!dim_ok(D)) return GLA_ERR_DIM;
+  if (!dim_ok(D) && D != 256) return GLA_ERR_DIM;
   const size_t nf = gla_rope_table_floats(T, Hh, W, D);
   if (nf == 0) return GLA_ERR_DIM;
   if ((long long)T * Hh * W > INT32_MAX) return GLA_ERR_DIM;
@@ -562,6 +562,76 @@ int gla_forward_blocks(const void* q, const void* k, const void* v, const void* 
   }
   return gla_forward_blocks_ws(q, k, v, g, rope, out, B, N, H, D, block_tokens, S_in, z_in, S_out,
                                z_out, ws, wsb, stream);
+}
+
+// ---- gated softmax anchor attention -------------------------------------
+
+static int check_softmax_shape(int B, int N, int H, int D, size_t* bytes) {
+  if (B < 0 || N < 0 || H < 0) return GLA_ERR_DIM;
+  if (D != 128 && D != 256) return GLA_ERR_DIM;
+  if ((long long)B * H > 65535) return GLA_ERR_DIM;
+  if ((long long)N * H * D * 2 >= (1LL << 31)) return GLA_ERR_DIM;
+  *bytes = (size_t)B * N * H * D * 2;
+  return GLA_OK;
+}
+
+size_t gla_softmax_workspace_bytes(int B, int N, int H, int D) {
+  size_t bytes = 0;
+  if (check_softmax_shape(B, N, H, D, &bytes) != GLA_OK || bytes == 0) return 0;
+  return 2 * gla::align_up(bytes, 256);
+}
+
+int gla_softmax_forward_check(const void* q, const void* k, const void* v, const void* g,
+                              const gla_rope_tables* rope, const void* out, int B, int N, int H,
+                              int D) {
+  size_t bytes = 0;
+  int rc = check_softmax_shape(B, N, H, D, &bytes);
+  if (rc) return rc;
+  if (bytes == 0) return GLA_OK;
+  if ((rc = check_rope(rope, N, D))) return rc;
+  return check_tensors({q, k, v, g}, out, bytes);
+}
+
+int gla_softmax_forward_ws(const void* q, const void* k, const void* v, const void* g,
+                           const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = gla_softmax_forward_check(q, k, v, g, rope, out, B, N, H, D);
+  if (rc) return rc;
+  size_t bytes = 0;
+  check_softmax_shape(B, N, H, D, &bytes);
+  if (bytes == 0) return GLA_OK;
+  const size_t need = gla_softmax_workspace_bytes(B, N, H, D);
+  if (!workspace) return GLA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+    return GLA_ERR_WORKSPACE;
+  if (overlap2(workspace, need, q, bytes) || overlap2(workspace, need, k, bytes) ||
+      overlap2(workspace, need, v, bytes) || overlap2(workspace, need, g, bytes) ||
+      overlap2(workspace, need, out, bytes))
+    return GLA_ERR_ALIAS;
+  if ((rc = rope_device_ok(rope))) return rc;
+  Plan p{};
+  p.B = B; p.N = N; p.H = H; p.D = D; p.BH = B * H;
+  gla::KArgs a = kernel_args(p, rope, 0, 1, workspace);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.g = static_cast<const uint16_t*>(g);
+  a.out = static_cast<uint16_t*>(out);
+  uint16_t* qr = static_cast<uint16_t*>(workspace);
+  uint16_t* kr = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + need / 2);
+  return status_of(gla::launch_softmax(p, a, qr, kr, static_cast<hipStream_t>(stream)));
+}
+
+int gla_softmax_forward(const void* q, const void* k, const void* v, const void* g,
+                        const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                        void* stream) {
+  int rc = gla_softmax_forward_check(q, k, v, g, rope, out, B, N, H, D);
+  if (rc) return rc;
+  const size_t need = gla_softmax_workspace_bytes(B, N, H, D);
+  if (need == 0) return GLA_OK;
+  void* ws = nullptr;
+  if ((rc = get_workspace(need, stream, &ws))) return rc;
+  return gla_softmax_forward_ws(q, k, v, g, rope, out, B, N, H, D, ws, need, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,246 @@
+// gla_device.h -- device helpers shared by the HIP kernel files (buffer
+// addressing, bf16 packing, exact division, RoPE table lookups, transposing
+// LDS reads).  Included inside each file's own anonymous namespace.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "gla_internal.h"
+
+namespace gla {
+namespace {
+
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kEps = 1e-6f;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr uint32_t kOob = 0x80000000u;  // offset past every slab (slabs are < 2 GiB)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Stores of the output stream carry the non-temporal hint (cache policy bit
+// nt): nothing reads them back, and without the hint their write-back lands
+// in the next pass's state kernel instead of this one.
+constexpr int kCpolNt = 2;
+
+__device__ __forceinline__ void store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNt);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ReLU of two bf16 in one dword: as int16 a bf16 is negative exactly when its
+// sign bit is set, so a packed signed max with 0 zeroes the negative halves
+// (and -0) and keeps the rest bit for bit.
+__device__ __forceinline__ uint32_t relu2(uint32_t w) {
+  s16x2 x = __builtin_bit_cast(s16x2, w);
+  x = __builtin_elementwise_max(x, (s16x2){0, 0});
+  return __builtin_bit_cast(uint32_t, x);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round two floats to bf16 (nearest-even) and pack them, a in the low half
+// (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 y = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, y);
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, DivMagic d) {
+  uint32_t t = __umulhi(n, d.m);
+  return (t + ((n - t) >> d.s1)) >> d.s2;
+}
+
+// Compile-time loop: calls f(std::integral_constant<int, i>) for i in [0, N).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<0, N>(f);
+}
+
+// Pairs per RoPE axis for head dimension D: y and x get floor(D/6) pairs each,
+// t the rest (the split the host-side table builder uses).
+template <int D>
+struct Axes {
+  static constexpr int Py = D / 6;
+  static constexpr int Px = D / 6;
+  static constexpr int Pt = D / 2 - 2 * (D / 6);
+};
+
+// Where a block reads its RoPE factors: the factorised table, either staged
+// in LDS (t-rows of the block's own token range plus the y and x tables) or
+// straight from global memory.
+struct TabView {
+  const float2* tab;
+  int tbase;   // first t-row present
+  int ntr;     // t-rows present
+  int t_last;  // last t of the block's tokens (positions past the range clamp to it)
+};
+
+// Copies the table rows a block of NT threads needs into LDS.  Caller
+// synchronises.
+template <int D, int NT = 256>
+__device__ __forceinline__ TabView stage_table(const KArgs& a, float2* ltab, bool in_lds,
+                                               int n_begin, int n_end) {
+  using X = Axes<D>;
+  TabView tv;
+  const int t_first = (int)fast_div((uint32_t)n_begin, a.div_hw);
+  tv.t_last = (int)fast_div((uint32_t)(n_end - 1), a.div_hw);
+  if (in_lds) {
+    const int nt_blk = tv.t_last - t_first + 1;
+    const float2* src_t = a.cs + (size_t)t_first * X::Pt;
+    for (int i = threadIdx.x; i < nt_blk * X::Pt; i += NT) ltab[i] = src_t[i];
+    const float2* src_yx = a.cs + (size_t)a.T * X::Pt;
+    const int nyx = a.Hh * X::Py + a.W * X::Px;
+    for (int i = threadIdx.x; i < nyx; i += NT) ltab[a.nt * X::Pt + i] = src_yx[i];
+    tv.tab = ltab;
+    tv.tbase = t_first;
+    tv.ntr = a.nt;
+  } else {
+    tv.tab = a.cs;
+    tv.tbase = 0;
+    tv.ntr = a.T;
+  }
+  return tv;
+}
+
+// Per-axis row offsets (in pairs, each minus its axis's first pair index) of
+// grid position (t, y, x) in a TabView.
+struct RowOff {
+  int ot, oy, ox;
+};
+
+template <int D>
+__device__ __forceinline__ RowOff row_offsets(const KArgs& a, const TabView& tv, int t, int y,
+                                              int x) {
+  using X = Axes<D>;
+  RowOff r;
+  t = min(t, tv.t_last);
+  r.ot = (t - tv.tbase) * X::Pt;
+  r.oy = tv.ntr * X::Pt + y * X::Py - X::Pt;
+  r.ox = tv.ntr * X::Pt + a.Hh * X::Py + x * X::Px - X::Pt - X::Py;
+  return r;
+}
+
+// Token range [n_begin, n_end) of range index c of a kernel: piece c % CB of
+// attention block c / CB.  A piece that starts past the last token (the last
+// block can be shorter than the others) is the empty range [N, N), which
+// stages no table rows and has no tiles.
+__device__ __forceinline__ void range_of(const KArgs& a, int c, int& n_begin, int& n_end) {
+  const int blk = c / a.CB;
+  const int blk_begin = blk * a.BT;
+  n_begin = min(blk_begin + (c - blk * a.CB) * a.L, a.N);
+  n_end = max(min(min(n_begin + a.L, blk_begin + a.BT), a.N), n_begin);
+}
+
+// Grid position of token n (row-major t, y, x).
+__device__ __forceinline__ void grid_pos(const KArgs& a, uint32_t n, int& t, int& y, int& x) {
+  t = (int)fast_div(n, a.div_hw);
+  const uint32_t rem = n - (uint32_t)t * (uint32_t)(a.Hh * a.W);
+  y = (int)fast_div(rem, a.div_w);
+  x = (int)(rem - (uint32_t)y * (uint32_t)a.W);
+}
+
+// (cos, sin) of pair p, where p is known to lie in [PMIN, PMAX]: when that
+// range sits inside one axis block the table row is chosen at compile time,
+// otherwise by masks (no branches).
+template <int D, int PMIN, int PMAX>
+__device__ __forceinline__ float2 rope_factor(const TabView& tv, const RowOff& r, int p) {
+  using X = Axes<D>;
+  int base;
+  if constexpr (PMAX < X::Pt) {
+    base = r.ot;
+  } else if constexpr (PMIN >= X::Pt && PMAX < X::Pt + X::Py) {
+    base = r.oy;
+  } else if constexpr (PMIN >= X::Pt + X::Py) {
+    base = r.ox;
+  } else {
+    const int my = -(int)(p >= X::Pt && p < X::Pt + X::Py);
+    const int mx = -(int)(p >= X::Pt + X::Py);
+    base = r.ot + ((r.oy - r.ot) & my) + ((r.ox - r.ot) & mx);
+  }
+  return tv.tab[base + p];
+}
+
+// RoPE factors of the 4 pairs of one 16-byte chunk: chunk index c = 4 S + m
+// with S compile-time and m in [0, 3].
+template <int D, int S>
+__device__ __forceinline__ void rope_factors(const TabView& tv, const RowOff& ro, int m,
+                                             float2 (&cs)[4]) {
+  static_for<4>([&](auto U) {
+    constexpr int u = decltype(U)::value;
+    cs[u] = rope_factor<D, 16 * S + u, 16 * S + 12 + u>(tv, ro, 4 * (4 * S + m) + u);
+  });
+}
+
+// Rotates the 4 pairs of one 16-byte chunk (8 features, ReLU already
+// applied, as packed bf16) and returns them as packed bf16.
+__device__ __forceinline__ u32x4 rotate_chunk(const u32x4 fq, const float2 (&cs)[4]) {
+  u32x4 pk;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float a0 = bf_lo(fq[u]);
+    const float a1 = bf_hi(fq[u]);
+    pk[u] = pack_bf16(a0 * cs[u].x - a1 * cs[u].y, a0 * cs[u].y + a1 * cs[u].x);
+  }
+  return pk;
+}
+
+template <int D, int S>
+__device__ __forceinline__ u32x4 rope_chunk(const u32x4 fq, const TabView& tv, const RowOff& ro,
+                                            int m) {
+  float2 cs[4];
+  rope_factors<D, S>(tv, ro, m, cs);
+  return rotate_chunk(fq, cs);
+}
+
+
+constexpr int tile_pitch(int row_bytes) {
+  int dw = row_bytes / 4;
+  while (dw % 64 != 16 && dw % 64 != 48) ++dw;
+  return 4 * dw;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA operand of features [32 i, 32 i + 32) over the 16 tokens of a
+// token-major LDS tile (see the state kernel's description).
+__device__ __forceinline__ bf16x8 frag_tr(const unsigned char* tile, int pitch, int i, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int f = 32 * i + 16 * (g & 1) + 4 * (s & 3);
+  const int tok = 8 * (g >> 1) + (s >> 2);
+  const unsigned char* p0 = tile + tok * pitch + 2 * f;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * pitch));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+}  // namespace
+}  // namespace gla

@@ -77,6 +77,10 @@ hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream);
 // The scan alone over zero blocks: S_out/z_out = S_in/z_in (or zero).
 hipError_t launch_carry(const Plan& p, KArgs a, hipStream_t stream);
 hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream);
+// Gated softmax anchor attention (gla_softmax.hip): prep (rotated, scaled q
+// into qr, rotated k into kr, [B, N, H, D] bf16 each) then the flash kernel.
+// Reads a.q, a.k, a.v, a.g, a.cs (nullptr: RoPE off), writes a.out.
+hipError_t launch_softmax(const Plan& p, KArgs a, uint16_t* qr, uint16_t* kr, hipStream_t stream);
 
 // Tile sizes the plan has to respect.
 constexpr int kOutputTileTokens = 64;

@@ -32,7 +32,8 @@ EXPORTS = (
     "gla_rope_destroy", "gla_workspace_bytes", "gla_forward", "gla_forward_ws",
     "gla_forward_check", "gla_state_ws", "gla_output_ws", "gla_state",
     "gla_forward_blocks", "gla_forward_blocks_ws", "gla_workspace_bytes_blocks",
-    "gla_forward_blocks_check",
+    "gla_forward_blocks_check", "gla_softmax_forward", "gla_softmax_forward_ws",
+    "gla_softmax_workspace_bytes", "gla_softmax_forward_check",
 )
 
 
@@ -86,6 +87,10 @@ def load_library():
         "gla_forward_blocks_ws": ([vp] * 4 + [rp, vp] + [i32] * 5 + [vp] * 4 + [vp, sz, vp], i32),
         "gla_workspace_bytes_blocks": ([i32] * 5, sz),
         "gla_forward_blocks_check": ([vp] * 4 + [rp, vp] + [i32] * 5 + [vp] * 4, i32),
+        "gla_softmax_forward": ([vp] * 4 + [rp, vp] + [i32] * 4 + [vp], i32),
+        "gla_softmax_forward_ws": ([vp] * 4 + [rp, vp] + [i32] * 4 + [vp, sz, vp], i32),
+        "gla_softmax_workspace_bytes": ([i32] * 4, sz),
+        "gla_softmax_forward_check": ([vp] * 4 + [rp, vp] + [i32] * 4, i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -366,4 +371,62 @@ def gla_forward_blocks_ws(q, k, v, g, rope, block_tokens: int, ws: torch.Tensor,
                                                  ws.data_ptr(), ws.numel() * ws.element_size(),
                                                  _stream_handle(stream, q.device)),
             "gla_forward_blocks_ws")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# gated softmax anchor attention
+
+
+def gla_softmax_workspace_bytes(B: int, N: int, H: int, D: int) -> int:
+    return load_library().gla_softmax_workspace_bytes(B, N, H, D)
+
+
+def alloc_workspace_softmax(B, N, H, D, device=None) -> torch.Tensor:
+    """A torch-owned uint8 device buffer large enough for gla_softmax_forward_ws."""
+    return torch.empty(max(gla_softmax_workspace_bytes(B, N, H, D), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def gla_softmax_forward_check(q, k, v, g, rope, out, B, N, H, D) -> int:
+    """Status of the library's argument validation (pointers as integers)."""
+    return load_library().gla_softmax_forward_check(q, k, v, g, _rope_ptr(rope), out,
+                                                    B, N, H, D)
+
+
+def _softmax_args(q, k, v, g, out):
+    _check_bf16("q", q)
+    for name, t in (("k", k), ("v", v), ("g", g)):
+        _check_bf16(name, t, q.shape)
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bf16("out", out, q.shape)
+    return out
+
+
+def gla_softmax_forward(q, k, v, g, rope=None, out=None, stream=None) -> torch.Tensor:
+    """o = sigmoid(g) * softmax(R q . R k / sqrt(D)) v per head; bf16 [B, N, H, D]."""
+    out = _softmax_args(q, k, v, g, out)
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_softmax_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                               g.data_ptr(), _rope_ptr(rope), out.data_ptr(),
+                                               B, N, H, D, _stream_handle(stream, q.device)),
+            "gla_softmax_forward")
+    return out
+
+
+def gla_softmax_forward_ws(q, k, v, g, rope, ws: torch.Tensor, out=None, stream=None):
+    out = _softmax_args(q, k, v, g, out)
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_softmax_forward_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                  g.data_ptr(), _rope_ptr(rope), out.data_ptr(),
+                                                  B, N, H, D, ws.data_ptr(),
+                                                  ws.numel() * ws.element_size(),
+                                                  _stream_handle(stream, q.device)),
+            "gla_softmax_forward_ws")
     return out

@@ -93,7 +93,8 @@ int gla_rope_fill_host(int T, int Hh, int W, int D, double theta, int t0, int y0
 
 /* Builds the table on the host, copies it to the current device (enqueued on
  * `stream`, then synchronised so the host copy can be released) and returns
- * a library-owned descriptor in *out.  D must be 32, 64 or 128. */
+ * a library-owned descriptor in *out.  D must be 32, 64, 128 or 256 (256 for
+ * the softmax anchor layers only). */
 int gla_rope_create(int T, int Hh, int W, int D, double theta, int t0, int y0, int x0,
                     void* stream, gla_rope_tables** out);
 
@@ -207,6 +208,45 @@ int gla_forward_blocks_check(const void* q, const void* k, const void* v, const 
                              const gla_rope_tables* rope, const void* out, int B, int N, int H,
                              int D, int block_tokens, const float* S_in, const float* z_in,
                              const float* S_out, const float* z_out);
+
+/* ---------------------------------------------------------------------
+ * Gated softmax anchor attention.
+ *
+ * The dense softmax layers of the hybrid ("SANA-Video 2.0", NVlabs Sana
+ * docs, section Architecture: a quarter of the layers are dense softmax
+ * anchors, 10 heads x 256 at 5B and 16 heads x 256 at 14B, with Wan 3D rotary
+ * position embeddings; "SANA-Video 2.0: Hybrid Linear Attention with
+ * Attention Residuals ..." (mlsanity index), Abstract: periodic gated-softmax
+ * anchors).  Per batch b and head h, with no mask:
+ *
+ *     o_n = sigmoid(g_n) * sum_m softmax_m(R_n q_n . R_m k_m / sqrt(D)) v_m
+ *
+ * RoPE (the same tables as above, built for this D) turns q and k
+ * themselves; rope == NULL switches it off.  q, k, v, g, out: device bf16
+ * [B, N, H, D] as for gla_forward, 16-byte aligned, out overlapping no input;
+ * D must be 128 or 256.  The scores, the softmax (online, base 2) and the
+ * value sums run in fp32 on bf16 MFMA with q scaled by log2(e)/sqrt(D) and q
+ * and k rotated into bf16 copies first.  Uses a library-owned workspace
+ * (grown with hipMalloc, which may synchronise).  B*N*H == 0 is a no-op.
+ * Results are bitwise reproducible. */
+int gla_softmax_forward(const void* q, const void* k, const void* v, const void* g,
+                        const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                        void* stream);
+
+/* Workspace bytes gla_softmax_forward_ws needs (the rotated q and k), 0 for
+ * bad shapes or B*N*H == 0. */
+size_t gla_softmax_workspace_bytes(int B, int N, int H, int D);
+
+/* gla_softmax_forward with a caller-owned device workspace (>= the size
+ * above, 256-byte aligned, overlapping no tensor).  Never allocates. */
+int gla_softmax_forward_ws(const void* q, const void* k, const void* v, const void* g,
+                           const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Argument validation of gla_softmax_forward alone (no HIP call). */
+int gla_softmax_forward_check(const void* q, const void* k, const void* v, const void* g,
+                              const gla_rope_tables* rope, const void* out, int B, int N, int H,
+                              int D);
 
 #ifdef __cplusplus
 }

@@ -207,3 +207,33 @@ def test_blocks_workspace_size():
     assert five >= 40 * 5 * (128 * 128 + 128) * 4 + 40 * 5 * 130 * 128 * 2
     assert five % 256 == 0
     assert gla.gla_workspace_bytes_blocks(2, 22000, 20, 128, 0) == 0
+
+
+# ---------------------------------------------------------------------------
+# softmax anchor attention: validation without a GPU
+
+
+def scheck(**kw):
+    args = dict(q=A, k=2 * A, v=3 * A, g=4 * A, rope=None, out=5 * A, B=1, N=64, H=2, D=256)
+    args.update(kw)
+    return gla.gla_softmax_forward_check(args["q"], args["k"], args["v"], args["g"],
+                                         args["rope"], args["out"], args["B"], args["N"],
+                                         args["H"], args["D"])
+
+
+def test_softmax_validation():
+    assert scheck() == 0 and scheck(D=128) == 0
+    for D in (32, 64, 192, 512):
+        assert scheck(D=D) == glamod.GLA_ERR_DIM
+    assert scheck(q=0) == glamod.GLA_ERR_NULL
+    assert scheck(v=3 * A + 4) == glamod.GLA_ERR_ALIGN
+    assert scheck(out=2 * A) == glamod.GLA_ERR_ALIAS
+    assert scheck(N=0) == 0
+    assert scheck(N=64, rope=_host_rope(4, 4, 4, 256)) == 0
+    assert scheck(N=64, rope=_host_rope(4, 4, 4, 128)) == glamod.GLA_ERR_ROPE
+
+
+def test_softmax_workspace_size():
+    assert gla.gla_softmax_workspace_bytes(2, 22000, 10, 256) >= 2 * 2 * 22000 * 10 * 256 * 2
+    assert gla.gla_softmax_workspace_bytes(1, 10, 1, 64) == 0
+    assert gla.gla_softmax_workspace_bytes(0, 10, 1, 256) == 0

@@ -1,0 +1,116 @@
+"""GPU parity of the gated softmax anchor attention (through the C ABI)
+against the fp64 oracle: relative L2 <= 5e-3 and max abs <= 3e-2 on the bf16
+output.  The GPU rounds R q (scaled) and R k to bf16, the softmax weights to
+bf16 for the value MFMA and the output to bf16.  Small shapes are compared
+in full; the anchor layers of the 5B and 14B models on sampled query rows
+that the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import gated_linear_attention_forward_amd as gla
+import oracle
+from workloads import ANCHOR_WORKLOADS, BY_NAME, make_inputs, random_inputs
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 5e-3
+ABS_TOL = 3e-2
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def assert_close(got, ref, what):
+    got = np.asarray(got, np.float64)
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    mx = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    say(f"  {what}: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_TOL, f"{what}: rel_l2 {rel}"
+    assert mx <= ABS_TOL, f"{what}: max_abs {mx}"
+
+
+def gpu_softmax(q, k, v, g, grid):
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    rope = gla.gla_rope_create(*grid, q.shape[-1]) if grid is not None else None
+    out = gla.gla_softmax_forward(qd, kd, vd, gd, rope)
+    torch.cuda.synchronize()
+    if rope is not None:
+        rope.close()
+    return out
+
+
+SMALL = [
+    # B, H, D, grid
+    (1, 2, 256, (2, 3, 5)),      # 30 tokens: one partial tile
+    (1, 1, 256, (1, 1, 1)),      # a single token
+    (2, 3, 256, (3, 7, 13)),     # 273 tokens: ragged query blocks and key tiles
+    (1, 2, 128, (4, 5, 13)),     # D = 128, 260 tokens
+    (2, 1, 128, (1, 1, 64)),     # exactly one key tile
+    (1, 1, 256, (2, 1, 129)),    # one past two query blocks
+]
+
+
+@pytest.mark.parametrize("B,H,D,grid", SMALL)
+@pytest.mark.parametrize("rope", [True, False])
+def test_softmax_small_shapes(B, H, D, grid, rope):
+    N = grid[0] * grid[1] * grid[2]
+    say(f"case softmax B={B} H={H} D={D} grid={grid} rope={rope}")
+    q, k, v, g = random_inputs(B, N, H, D, seed=3000 + N + D + H)
+    got = gpu_softmax(q, k, v, g, grid if rope else None).double().cpu().numpy()
+    ref = oracle.softmax_forward(q, k, v, g, oracle.Grid(*grid) if rope else None)
+    assert_close(got, ref, "out")
+
+
+@pytest.mark.parametrize("name", [w.name for w in ANCHOR_WORKLOADS])
+def test_anchor_layers_sampled(name):
+    w = BY_NAME[name]
+    say(f"case softmax {name} B={w.B} N={w.N} H={w.H} D={w.D}")
+    q, k, v, g = make_inputs(w)
+    out = gpu_softmax(q, k, v, g, (w.T, w.Hh, w.W)).cpu()
+    rng = np.random.default_rng(w.seed)
+    grid = oracle.Grid(w.T, w.Hh, w.W)
+    got_all, ref_all = [], []
+    for (b, h) in sorted({(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(0, w.B)),
+                                                         int(rng.integers(0, w.H)))}):
+        toks = np.unique(np.concatenate([rng.integers(0, w.N, 40), [0, 127, 128, w.N - 1]]))
+        ref_all.append(oracle.softmax_rows(q, k, v, g, grid, b, h, toks))
+        got_all.append(out[b, torch.from_numpy(toks), h].double().numpy())
+    assert_close(np.concatenate(got_all), np.concatenate(ref_all), "sampled rows")
+    assert torch.isfinite(out.float()).all()
+
+
+def test_softmax_constant_values_closed_form():
+    """Every value row equal to c: o = sigmoid(g) * c whatever q and k are."""
+    B, N, H, D = 1, 200, 2, 256
+    say("case softmax constant v")
+    q, k, _, g = random_inputs(B, N, H, D, seed=3100)
+    c = torch.linspace(-2, 2, D).to(torch.bfloat16)
+    v = c.expand(B, N, H, D).contiguous()
+    got = gpu_softmax(q, k, v, g, (2, 10, 10)).double().cpu().numpy()
+    ref = 1.0 / (1.0 + np.exp(-g.double().numpy())) * c.double().numpy()
+    assert_close(got, ref, "out")
+
+
+def test_softmax_deterministic():
+    w = BY_NAME["anchor_5b_480p_81f"]
+    say("case softmax determinism")
+    q, k, v, g = (t.to(DEV) for t in make_inputs(w))
+    rope = gla.gla_rope_create(w.T, w.Hh, w.W, w.D)
+    o1 = gla.gla_softmax_forward(q, k, v, g, rope)
+    ws = gla.alloc_workspace_softmax(w.B, w.N, w.H, w.D, DEV)
+    o2 = gla.gla_softmax_forward_ws(q, k, v, g, rope, ws)
+    torch.cuda.synchronize()
+    rope.close()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_softmax_empty_and_errors():
+    say("case softmax empty / errors")
+    q = torch.empty((1, 0, 2, 256), dtype=torch.bfloat16, device=DEV)
+    assert gla.gla_softmax_forward(q, q.clone(), q.clone(), q.clone()).shape == q.shape
+    x = torch.zeros((1, 16, 2, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gla.GlaError):
+        gla.gla_softmax_forward(x, x.clone(), x.clone(), x.clone())  # D = 64 is not served

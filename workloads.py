@@ -55,7 +55,14 @@ WORKLOADS = [
     Workload("14b_480p_193f", B=2, H=32, D=128, T=25, Hh=15, W=26, qk_scale=0.5, seed=3),
     Workload("5b_720p_60s", B=1, H=20, D=128, T=181, Hh=22, W=40, qk_scale=1.0, seed=4),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
+# The gated softmax anchor layers of the same models: 10 heads x 256 (5B) and
+# 16 heads x 256 (14B) (section Architecture), on the same latent grids.
+ANCHOR_WORKLOADS = [
+    Workload("anchor_5b_480p_81f", B=1, H=10, D=256, T=11, Hh=15, W=26, qk_scale=1.0, seed=11),
+    Workload("anchor_5b_720p_193f", B=2, H=10, D=256, T=25, Hh=22, W=40, qk_scale=1.0, seed=12),
+    Workload("anchor_14b_480p_193f", B=2, H=16, D=256, T=25, Hh=15, W=26, qk_scale=1.0, seed=13),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + ANCHOR_WORKLOADS}
 
 
 def random_inputs(B: int, N: int, H: int, D: int, seed: int, qk_scale: float = 1.0):
