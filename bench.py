@@ -15,6 +15,9 @@ launch from the committed rocprofv3 byte counters (profiles/), or null when
 the kernel source differs from the one those counters were taken on.
 `cpu_baseline` times the fp64 oracle on a sample of the workload's heads
 (about ten seconds of CPU work) and scales to the whole workload.
+
+`--block-frames F` times the block-causal form instead, and `--softmax` the
+gated softmax anchor attention (an MFMA-bound roofline in TFLOP/s).
 """
 from __future__ import annotations
 
@@ -165,6 +168,104 @@ def block_bench(args, w, gla, dev, tensors, out, rope, stream):
     print(json.dumps(result), flush=True)
 
 
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def softmax_cpu_baseline(w, q, k, v, g, min_seconds=10.0):
+    """Times the fp64 oracle's softmax rows on query tokens of head (0, 0),
+    in batches of rows until about `min_seconds` of CPU work, and scales the
+    per-row time to every (token, head) of the workload."""
+    import numpy as np
+
+    import oracle
+    grid = oracle.Grid(w.T, w.Hh, w.W, w.theta)
+    threads = oracle.num_threads()
+    qs, ks, vs, gs = (t[:1, :, :1].contiguous() for t in (q, k, v, g))
+    batch = 4 * threads
+    rows_done = 0
+    t0 = time.perf_counter()
+    while True:
+        rows = (np.arange(batch) * 7919 + rows_done) % w.N
+        oracle.softmax_rows(qs, ks, vs, gs, grid, 0, 0, rows)
+        rows_done += batch
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    per_row = dt / rows_done
+    whole = per_row * w.B * w.H * w.N
+    return {
+        "value": (w.B * w.N) / whole,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{rows_done} query rows of head (0, 0) against all N={w.N} keys in "
+                  f"{dt:.1f} s; {per_row * 1e3:.2f} ms per row, scaled to "
+                  f"{w.B * w.H * w.N} (token, head) rows",
+    }
+
+
+def softmax_bench(args, w, gla, dev, tensors, rope, stream):
+    """Gated softmax anchor attention: K passes of gla_softmax_forward_ws (a
+    rotation prep kernel, then the flash kernel).  The roofline is MFMA-bound:
+    4*N*N*D flops per head (the score product and the value product, 2*N*N*D
+    each) against the bf16 dense peak, over the whole call's event time (the
+    prep kernel's share included)."""
+    import torch
+    qd, kd, vd, gd = tensors
+    out = torch.empty_like(qd)
+    ws = gla.alloc_workspace_softmax(w.B, w.N, w.H, w.D, dev)
+
+    def step():
+        gla.gla_softmax_forward_ws(qd, kd, vd, gd, rope, ws, out, stream)
+
+    log(f"bench: softmax anchor attention; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    log(f"bench: {args.steps} instrumented steps")
+    for e in evs:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ev_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    flops = 4.0 * w.B * w.H * w.N * w.N * w.D
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    result = {
+        "metric": "gated softmax anchor attention tokens/s per layer; achieved bf16 MFMA "
+                  "TFLOP/s vs peak",
+        "value": w.B * w.N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "D": w.D,
+                   "grid": [w.T, w.Hh, w.W], "parallelism": "single-gpu"},
+        "roofline": {"kernel": "softmax prep + flash kernels", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "algorithmic_flops": flops, "avg_ms": ev_ms},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle (cpu_baseline)")
+        q, k, v, g = (t.cpu() for t in tensors)
+        result["cpu_baseline"] = softmax_cpu_baseline(w, q, k, v, g)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,7 +279,12 @@ def main():
                     help="time the block-causal pass (gla_forward_blocks) in blocks of this "
                          "many latent frames, carrying the state in place, instead of the "
                          "bidirectional mixer")
+    ap.add_argument("--softmax", action="store_true",
+                    help="time the gated softmax anchor attention (gla_softmax_forward) "
+                         "instead; the workload defaults to anchor_5b_720p_193f")
     args = ap.parse_args()
+    if args.softmax and args.workload == DEFAULT_WORKLOAD:
+        args.workload = "anchor_5b_720p_193f"
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the mixer's state is exchanged within one "
@@ -196,12 +302,15 @@ def main():
     log(f"bench: workload {w.name} B={w.B} N={w.N} H={w.H} D={w.D}; generating inputs")
     q, k, v, g = make_inputs(w)
     qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
-    out = torch.empty_like(qd)
     rope = gla.gla_rope_create(w.T, w.Hh, w.W, w.D, w.theta)
-    ws = gla.alloc_workspace(w.B, w.N, w.H, w.D, dev)
     stream = torch.cuda.current_stream(dev)
     if args.calibrate_copy:
         copy_calibration(dev)
+    if args.softmax:
+        softmax_bench(args, w, gla, dev, (qd, kd, vd, gd), rope, stream)
+        return
+    out = torch.empty_like(qd)
+    ws = gla.alloc_workspace(w.B, w.N, w.H, w.D, dev)
     if args.block_frames > 0:
         block_bench(args, w, gla, dev, (qd, kd, vd, gd), out, rope, stream)
         return
