@@ -9,7 +9,9 @@ The oracle computes the gated bidirectional linear-attention token mixer of
 linear attention with Wan 3D rotary position embeddings) in plain IEEE double
 arithmetic, one (b, h) head at a time: first the state S and normaliser z,
 then every token's output.  ``forward_blocks`` is the block-causal form with
-a carried state.  See gla_oracle.c for the exact forms and the readings they
+a carried state; ``softmax_rows`` the gated softmax anchor attention;
+``backward`` (and its state / row helpers) the exact derivative of the
+bidirectional mixer given the output gradient.  See gla_oracle.c for the exact forms and the readings they
 take where the pages are silent.
 
 Inputs are bf16 bit patterns (numpy uint16 arrays, or torch bfloat16 CPU
@@ -45,7 +47,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_SRC) > os.path.getmtime(_LIB_PATH):
         build()
     lib = ctypes.CDLL(_LIB_PATH)
     u16p = ctypes.POINTER(ctypes.c_uint16)
@@ -77,6 +79,19 @@ def _load():
     lib.gla_oracle_softmax_rows.argtypes = ([u16p] * 4 + [c_int] * 4 + grid +
                                             [c_int, c_int, lp, c_long, dp])
     lib.gla_oracle_softmax_rows.restype = c_int
+    lib.gla_oracle_backward.argtypes = ([u16p] * 5 + [c_int] * 4 + grid +
+                                        [c_double, dp, dp, dp, dp])
+    lib.gla_oracle_backward.restype = c_int
+    lib.gla_oracle_backward_state.argtypes = ([u16p] * 3 + [c_int] * 4 + grid +
+                                              [c_double, dp, dp, dp, dp])
+    lib.gla_oracle_backward_state.restype = c_int
+    lib.gla_oracle_backward_q_rows.argtypes = ([u16p] * 3 + [c_int] * 4 + grid +
+                                               [c_double, c_int, c_int, dp, dp, lp, c_long, dp,
+                                                dp])
+    lib.gla_oracle_backward_q_rows.restype = c_int
+    lib.gla_oracle_backward_kv_rows.argtypes = ([u16p] * 2 + [c_int] * 4 + grid +
+                                                [c_int, c_int, dp, dp, lp, c_long, dp, dp])
+    lib.gla_oracle_backward_kv_rows.restype = c_int
     _lib = lib
     return lib
 
@@ -247,3 +262,82 @@ def softmax_forward(q, k, v, g, grid: Grid | None) -> np.ndarray:
         for h in range(H):
             out[b, :, h] = softmax_rows(q, k, v, g, grid, b, h, rows_all)
     return out
+
+
+def _same_shape(*arrays):
+    shape = arrays[0].shape
+    for a in arrays[1:]:
+        if a.shape != shape:
+            raise ValueError("inputs must share one [B, N, H, D] shape")
+    return shape
+
+
+def backward(q, k, v, g, dout, grid: Grid | None, eps: float = EPS):
+    """Gradients (dq, dk, dv, dg), each [B, N, H, D] fp64, of the loss whose
+    gradient with respect to the mixer's output is dout (see
+    gla_oracle_backward for the chain-rule form)."""
+    q, k, v, g, dout = (as_bits(a) for a in (q, k, v, g, dout))
+    B, N, H, D = _same_shape(q, k, v, g, dout)
+    outs = [np.empty((B, N, H, D), np.float64) for _ in range(4)]
+    _check(_load().gla_oracle_backward(*(_p(a, ctypes.c_uint16) for a in (q, k, v, g, dout)),
+                                       B, N, H, D, *_grid_args(grid), eps,
+                                       *(_p(o, ctypes.c_double) for o in outs)))
+    return tuple(outs)
+
+
+def backward_state(q, g, dout, grid: Grid | None, S, z, eps: float = EPS):
+    """dS [B, H, D, D] = sum_n rq_n a_n^T and dz [B, H, D] = sum_n dden_n phi(q_n),
+    given the forward state S, z (as ``state`` returns)."""
+    q, g, dout = (as_bits(a) for a in (q, g, dout))
+    B, N, H, D = _same_shape(q, g, dout)
+    S = np.ascontiguousarray(S, dtype=np.float64)
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    if S.shape != (B, H, D, D) or z.shape != (B, H, D):
+        raise ValueError("S must be [B, H, D, D] and z [B, H, D]")
+    dS = np.empty((B, H, D, D), np.float64)
+    dz = np.empty((B, H, D), np.float64)
+    _check(_load().gla_oracle_backward_state(*(_p(a, ctypes.c_uint16) for a in (q, g, dout)),
+                                             B, N, H, D, *_grid_args(grid), eps,
+                                             _p(S, ctypes.c_double), _p(z, ctypes.c_double),
+                                             _p(dS, ctypes.c_double), _p(dz, ctypes.c_double)))
+    return dS, dz
+
+
+def backward_q_rows(q, g, dout, grid: Grid | None, b: int, h: int, S_bh, z_bh, token_rows,
+                    eps: float = EPS):
+    """dq and dg rows [len(token_rows), D] of head (b, h), given its S [D, D], z [D]."""
+    q, g, dout = (as_bits(a) for a in (q, g, dout))
+    B, N, H, D = _same_shape(q, g, dout)
+    S_bh = np.ascontiguousarray(S_bh, dtype=np.float64)
+    z_bh = np.ascontiguousarray(z_bh, dtype=np.float64)
+    if S_bh.shape != (D, D) or z_bh.shape != (D,):
+        raise ValueError("S_bh must be [D, D] and z_bh [D]")
+    r = np.ascontiguousarray(token_rows, dtype=np.int64)
+    dq = np.empty((r.shape[0], D), np.float64)
+    dg = np.empty((r.shape[0], D), np.float64)
+    _check(_load().gla_oracle_backward_q_rows(*(_p(a, ctypes.c_uint16) for a in (q, g, dout)),
+                                              B, N, H, D, *_grid_args(grid), eps, b, h,
+                                              _p(S_bh, ctypes.c_double), _p(z_bh, ctypes.c_double),
+                                              _p(r, ctypes.c_long), r.shape[0],
+                                              _p(dq, ctypes.c_double), _p(dg, ctypes.c_double)))
+    return dq, dg
+
+
+def backward_kv_rows(k, v, grid: Grid | None, b: int, h: int, dS_bh, dz_bh, token_rows):
+    """dk and dv rows [len(token_rows), D] of head (b, h), given its dS [D, D], dz [D]."""
+    k, v = (as_bits(a) for a in (k, v))
+    B, N, H, D = _same_shape(k, v)
+    dS_bh = np.ascontiguousarray(dS_bh, dtype=np.float64)
+    dz_bh = np.ascontiguousarray(dz_bh, dtype=np.float64)
+    if dS_bh.shape != (D, D) or dz_bh.shape != (D,):
+        raise ValueError("dS_bh must be [D, D] and dz_bh [D]")
+    r = np.ascontiguousarray(token_rows, dtype=np.int64)
+    dk = np.empty((r.shape[0], D), np.float64)
+    dv = np.empty((r.shape[0], D), np.float64)
+    _check(_load().gla_oracle_backward_kv_rows(*(_p(a, ctypes.c_uint16) for a in (k, v)),
+                                               B, N, H, D, *_grid_args(grid), b, h,
+                                               _p(dS_bh, ctypes.c_double),
+                                               _p(dz_bh, ctypes.c_double),
+                                               _p(r, ctypes.c_long), r.shape[0],
+                                               _p(dk, ctypes.c_double), _p(dv, ctypes.c_double)))
+    return dk, dv

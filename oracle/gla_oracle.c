@@ -24,8 +24,9 @@
  * gla_oracle_forward_blocks adds the block-causal form with a carried state
  * (the constant-memory KV cache for block linear attention of the
  * "SANA-Video_2B_720p" model card, innovation (2)); gla_oracle_softmax_rows
- * the gated softmax anchor attention of the other quarter of the layers; see
- * their comments.
+ * the gated softmax anchor attention of the other quarter of the layers;
+ * gla_oracle_backward and its row/state helpers the exact derivative of the
+ * bidirectional mixer; see their comments.
  *
  * RoPE reading (the pages only name "Wan 3D rotary position embeddings"):
  *   - the D/2 rotation pairs are (2i, 2i+1), interleaved;
@@ -480,5 +481,281 @@ int gla_oracle_softmax_rows(const uint16_t* q, const uint16_t* k, const uint16_t
     }
   }
   free(rk);
+  return err;
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward pass of the bidirectional mixer: the exact derivative of the
+ * forward form above, for training the linear layers from scratch ("SANA-
+ * Video 2.0: Hybrid Linear Attention with Attention Residuals for Efficient
+ * Video Generation" (mlsanity index), Abstract: the hybrid is trained, not
+ * distilled from a softmax model).  Given the gradient dout of a loss with
+ * respect to the output, per (b, h), written out by the chain rule through
+ * the forward definition with
+ *     fq = phi(q_n), rq = R_n fq, den = fq.z + eps, s = sigmoid(g_n),
+ *     num = S^T rq,  o_n = s * num / den:
+ *     dg_n  = dout_n * o_n * (1 - s)             (sigmoid' = s (1 - s))
+ *     a_n   = dout_n * s / den                   (gradient reaching num)
+ *     dden  = -(a_n . num) / den                 (gradient reaching den)
+ *     dq_n  = [q_n > 0] * (R_n^T (S a_n) + dden z)
+ *     dS    = sum_n rq a_n^T,   dz = sum_n dden fq
+ *     dv_m  = dS^T (R_m phi(k_m))
+ *     dk_m  = [k_m > 0] * (R_m^T (dS v_m) + dz)
+ * R_n^T is the rotation by the negated angles (R_n is orthogonal).  The
+ * derivative of phi at 0 is taken as 0 (the one-sided choice of common
+ * autograd systems; the pages do not discuss it).
+ * ------------------------------------------------------------------------ */
+
+/* out = R_n^T u: each pair rotated by the negated angle. */
+static void rotate_back(int D, const oracle_grid* gr, long n, const double* u, double* out) {
+  if (gr == NULL) {
+    for (int d = 0; d < D; ++d) out[d] = u[d];
+    return;
+  }
+  long t, y, x;
+  token_position(gr, n, &t, &y, &x);
+  for (int p = 0; p < D / 2; ++p) {
+    double w = gla_oracle_angle(D, gr->theta, p, t, y, x);
+    double c = cos(w), s = sin(w);
+    double a = u[2 * p], b = u[2 * p + 1];
+    out[2 * p] = a * c + b * s;
+    out[2 * p + 1] = -a * s + b * c;
+  }
+}
+
+typedef struct {
+  double *x, *f, *r, *gv, *dv, *num, *a, *t, *t2;
+} bwd_scratch;
+
+static int scratch_alloc(bwd_scratch* w, int D) {
+  double** p[] = {&w->x, &w->f, &w->r, &w->gv, &w->dv, &w->num, &w->a, &w->t, &w->t2};
+  int ok = 1;
+  for (unsigned i = 0; i < sizeof p / sizeof p[0]; ++i) {
+    *p[i] = malloc(sizeof(double) * D);
+    if (!*p[i]) ok = 0;
+  }
+  return ok ? ORACLE_OK : ORACLE_ERR_ALLOC;
+}
+
+static void scratch_free(bwd_scratch* w) {
+  free(w->x); free(w->f); free(w->r); free(w->gv); free(w->dv);
+  free(w->num); free(w->a); free(w->t); free(w->t2);
+}
+
+/* Query side of token n of head (b, h), given S and z: writes dq_row and
+ * dg_row (either may be NULL) and, when dS / dz are not NULL, adds the
+ * token's terms rq a^T and dden fq to them. */
+static void bwd_query_token(const uint16_t* q, const uint16_t* g, const uint16_t* dout, int N,
+                            int H, int D, const oracle_grid* gr, int b, int h, const double* S,
+                            const double* z, double eps, long n, bwd_scratch* w, double* dq_row,
+                            double* dg_row, double* dS, double* dz) {
+  load_row(q, N, H, D, b, h, n, w->x);
+  load_row(g, N, H, D, b, h, n, w->gv);
+  load_row(dout, N, H, D, b, h, n, w->dv);
+  for (int d = 0; d < D; ++d) w->f[d] = relu(w->x[d]);
+  rotate(D, gr, n, w->f, w->r);
+  double den = 0.0;
+  for (int d = 0; d < D; ++d) den += w->f[d] * z[d];
+  den += eps;
+  for (int e = 0; e < D; ++e) {
+    double num = 0.0;
+    for (int d = 0; d < D; ++d) num += w->r[d] * S[(long)d * D + e];
+    w->num[e] = num;
+  }
+  double dden = 0.0;
+  for (int e = 0; e < D; ++e) {
+    double s = sigmoid(w->gv[e]);
+    double o = s * w->num[e] / den;
+    if (dg_row) dg_row[e] = w->dv[e] * o * (1.0 - s);
+    w->a[e] = w->dv[e] * s / den;
+    dden -= w->a[e] * w->num[e];
+  }
+  dden /= den;
+  if (dq_row) {
+    for (int d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int e = 0; e < D; ++e) acc += S[(long)d * D + e] * w->a[e];
+      w->t[d] = acc;
+    }
+    rotate_back(D, gr, n, w->t, w->t2);
+    for (int d = 0; d < D; ++d)
+      dq_row[d] = w->x[d] > 0.0 ? w->t2[d] + dden * z[d] : 0.0;
+  }
+  if (dS)
+    for (int d = 0; d < D; ++d)
+      for (int e = 0; e < D; ++e) dS[(long)d * D + e] += w->r[d] * w->a[e];
+  if (dz)
+    for (int d = 0; d < D; ++d) dz[d] += dden * w->f[d];
+}
+
+/* Key/value side of token m of head (b, h), given dS and dz. */
+static void bwd_key_token(const uint16_t* k, const uint16_t* v, int N, int H, int D,
+                          const oracle_grid* gr, int b, int h, const double* dS, const double* dz,
+                          long m, bwd_scratch* w, double* dk_row, double* dv_row) {
+  load_row(k, N, H, D, b, h, m, w->x);
+  load_row(v, N, H, D, b, h, m, w->gv);
+  for (int d = 0; d < D; ++d) w->f[d] = relu(w->x[d]);
+  rotate(D, gr, m, w->f, w->r);
+  if (dv_row)
+    for (int e = 0; e < D; ++e) {
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d) acc += dS[(long)d * D + e] * w->r[d];
+      dv_row[e] = acc;
+    }
+  if (dk_row) {
+    for (int d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int e = 0; e < D; ++e) acc += dS[(long)d * D + e] * w->gv[e];
+      w->t[d] = acc;
+    }
+    rotate_back(D, gr, m, w->t, w->t2);
+    for (int d = 0; d < D; ++d) dk_row[d] = w->x[d] > 0.0 ? w->t2[d] + dz[d] : 0.0;
+  }
+}
+
+/* Gradient state of every head: dS[B, H, D, D] = sum_n rq_n a_n^T and
+ * dz[B, H, D] = sum_n dden_n phi(q_n), given the forward state S [B, H, D, D]
+ * and z [B, H, D] (as gla_oracle_state writes them).  Sums in token order. */
+int gla_oracle_backward_state(const uint16_t* q, const uint16_t* g, const uint16_t* dout,
+                              int B, int N, int H, int D, int rope, int T, int Hh, int W,
+                              double theta, long t0, long y0, long x0, double eps,
+                              const double* S, const double* z, double* dS, double* dz) {
+  oracle_grid g0;
+  const oracle_grid* gr;
+  make_grid(rope, T, Hh, W, theta, t0, y0, x0, &g0, &gr);
+  int rc = check_args(B, N, H, D, gr);
+  if (rc) return rc;
+  int err = ORACLE_OK;
+  long BH = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    int b = (int)(bh / H), h = (int)(bh % H);
+    bwd_scratch w;
+    int r = scratch_alloc(&w, D);
+    double* dSh = dS + bh * D * (long)D;
+    double* dzh = dz + bh * D;
+    memset(dSh, 0, sizeof(double) * D * D);
+    memset(dzh, 0, sizeof(double) * D);
+    if (!r)
+      for (long n = 0; n < N; ++n)
+        bwd_query_token(q, g, dout, N, H, D, gr, b, h, S + bh * D * (long)D, z + bh * D, eps,
+                        n, &w, NULL, NULL, dSh, dzh);
+    scratch_free(&w);
+    if (r) {
+#pragma omp critical
+      err = r;
+    }
+  }
+  return err;
+}
+
+/* dq and dg of selected tokens of head (b, h), given that head's S and z.
+ * dq_rows, dg_rows: [nrows, D]. */
+int gla_oracle_backward_q_rows(const uint16_t* q, const uint16_t* g, const uint16_t* dout,
+                               int B, int N, int H, int D, int rope, int T, int Hh, int W,
+                               double theta, long t0, long y0, long x0, double eps, int b, int h,
+                               const double* S, const double* z, const long* rows, long nrows,
+                               double* dq_rows, double* dg_rows) {
+  oracle_grid g0;
+  const oracle_grid* gr;
+  make_grid(rope, T, Hh, W, theta, t0, y0, x0, &g0, &gr);
+  int rc = check_args(B, N, H, D, gr);
+  if (rc) return rc;
+  if (b < 0 || b >= B || h < 0 || h >= H) return ORACLE_ERR_ARG;
+  for (long i = 0; i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= N) return ORACLE_ERR_ARG;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    bwd_scratch w;
+    if (scratch_alloc(&w, D)) {
+#pragma omp critical
+      err = ORACLE_ERR_ALLOC;
+    } else {
+#pragma omp for schedule(static)
+      for (long i = 0; i < nrows; ++i)
+        bwd_query_token(q, g, dout, N, H, D, gr, b, h, S, z, eps, rows[i], &w, dq_rows + i * D,
+                        dg_rows + i * D, NULL, NULL);
+    }
+    scratch_free(&w);
+  }
+  return err;
+}
+
+/* dk and dv of selected tokens of head (b, h), given that head's dS and dz.
+ * dk_rows, dv_rows: [nrows, D]. */
+int gla_oracle_backward_kv_rows(const uint16_t* k, const uint16_t* v, int B, int N, int H, int D,
+                                int rope, int T, int Hh, int W, double theta, long t0, long y0,
+                                long x0, int b, int h, const double* dS, const double* dz,
+                                const long* rows, long nrows, double* dk_rows, double* dv_rows) {
+  oracle_grid g0;
+  const oracle_grid* gr;
+  make_grid(rope, T, Hh, W, theta, t0, y0, x0, &g0, &gr);
+  int rc = check_args(B, N, H, D, gr);
+  if (rc) return rc;
+  if (b < 0 || b >= B || h < 0 || h >= H) return ORACLE_ERR_ARG;
+  for (long i = 0; i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= N) return ORACLE_ERR_ARG;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    bwd_scratch w;
+    if (scratch_alloc(&w, D)) {
+#pragma omp critical
+      err = ORACLE_ERR_ALLOC;
+    } else {
+#pragma omp for schedule(static)
+      for (long i = 0; i < nrows; ++i)
+        bwd_key_token(k, v, N, H, D, gr, b, h, dS, dz, rows[i], &w, dk_rows + i * D,
+                      dv_rows + i * D);
+    }
+    scratch_free(&w);
+  }
+  return err;
+}
+
+/* Whole backward pass: dq, dk, dv, dg [B, N, H, D] (doubles) from bf16 q, k,
+ * v, g and the output gradient dout.  Per head: the forward state, then the
+ * query side of every token (dq, dg, and the sums dS, dz), then the key side
+ * of every token (dk, dv). */
+int gla_oracle_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                        const uint16_t* dout, int B, int N, int H, int D, int rope, int T, int Hh,
+                        int W, double theta, long t0, long y0, long x0, double eps, double* dq,
+                        double* dk, double* dv, double* dg) {
+  oracle_grid g0;
+  const oracle_grid* gr;
+  make_grid(rope, T, Hh, W, theta, t0, y0, x0, &g0, &gr);
+  int rc = check_args(B, N, H, D, gr);
+  if (rc) return rc;
+  int err = ORACLE_OK;
+  long BH = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    int b = (int)(bh / H), h = (int)(bh % H);
+    double* S = malloc(sizeof(double) * D * (long)D);
+    double* z = malloc(sizeof(double) * D);
+    double* dS = calloc((size_t)D * D, sizeof(double));
+    double* dz = calloc((size_t)D, sizeof(double));
+    bwd_scratch w;
+    int r = scratch_alloc(&w, D);
+    if (!S || !z || !dS || !dz) r = ORACLE_ERR_ALLOC;
+    if (!r) r = head_state(k, v, N, H, D, gr, b, h, S, z);
+    if (!r) {
+      for (long n = 0; n < N; ++n) {
+        long o = (((long)b * N + n) * H + h) * (long)D;
+        bwd_query_token(q, g, dout, N, H, D, gr, b, h, S, z, eps, n, &w, dq + o, dg + o, dS, dz);
+      }
+      for (long m = 0; m < N; ++m) {
+        long o = (((long)b * N + m) * H + h) * (long)D;
+        bwd_key_token(k, v, N, H, D, gr, b, h, dS, dz, m, &w, dk + o, dv + o);
+      }
+    }
+    scratch_free(&w);
+    free(S); free(z); free(dS); free(dz);
+    if (r) {
+#pragma omp critical
+      err = r;
+    }
+  }
   return err;
 }

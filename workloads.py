@@ -79,6 +79,15 @@ def random_inputs(B: int, N: int, H: int, D: int, seed: int, qk_scale: float = 1
     return tuple(out)
 
 
+def random_grad(B: int, N: int, H: int, D: int, seed: int):
+    """Output gradient for the backward pass: bf16 CPU tensor [B, N, H, D],
+    iid N(0, 1) from its own seeded generator (drawn after nothing else)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    x = torch.randn((B, N, H, D), generator=gen, dtype=torch.float32)
+    return x.to(torch.bfloat16)
+
+
 def make_inputs(w: Workload, seed: int | None = None):
     """Seeded inputs of a named workload (seed defaults to the workload's own)."""
     return random_inputs(w.B, w.N, w.H, w.D, w.seed if seed is None else seed, w.qk_scale)
