@@ -1,6 +1,7 @@
 """Gated linear-attention token mixer for AMD MI355X (gfx950): the
-bidirectional mixer, its block-causal form with a carried state, and the
-gated softmax anchor attention of the hybrid's other layers.
+bidirectional mixer and its backward pass, its block-causal form with a
+carried state, and the gated softmax anchor attention of the hybrid's other
+layers.
 
 The compute path is libgla.so (C ABI in include/gla.h, HIP kernels in
 csrc/); this package is its thin ctypes binding.
@@ -10,8 +11,13 @@ from .gla import (  # noqa: F401
     GlaError,
     RopeTables,
     alloc_workspace,
+    alloc_workspace_backward,
     alloc_workspace_blocks,
     alloc_workspace_softmax,
+    gla_backward,
+    gla_backward_check,
+    gla_backward_workspace_bytes,
+    gla_backward_ws,
     gla_forward,
     gla_forward_blocks,
     gla_forward_blocks_check,

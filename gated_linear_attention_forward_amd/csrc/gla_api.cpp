@@ -634,4 +634,136 @@ int gla_softmax_forward(const void* q, const void* k, const void* v, const void*
   return gla_softmax_forward_ws(q, k, v, g, rope, out, B, N, H, D, ws, need, stream);
 }
 
+// ---- backward pass of the bidirectional mixer ----------------------------
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the backward pass: the forward plan's partials and S^T
+// operand, then the S rows operand, fp32 z, dz partials and the bf16 a tensor.
+struct BwdLayout {
+  Plan p;
+  size_t off_sl2, off_z, off_dzp, off_a, bytes;
+};
+
+BwdLayout bwd_layout(int B, int N, int H, int D) {
+  BwdLayout l{};
+  l.p = gla::make_plan(B, N, H, D);
+  size_t off = l.p.ws_bytes;
+  l.off_sl2 = off;
+  off = gla::align_up(off + (size_t)l.p.BH * D * D * sizeof(uint16_t), 256);
+  l.off_z = off;
+  off = gla::align_up(off + (size_t)l.p.BH * D * sizeof(float), 256);
+  l.off_dzp = off;
+  off = gla::align_up(off + (size_t)l.p.BH * l.p.C2 * D * sizeof(float), 256);
+  l.off_a = off;
+  off = gla::align_up(off + (size_t)B * N * H * D * sizeof(uint16_t), 256);
+  l.bytes = off;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gla_backward_workspace_bytes(int B, int N, int H, int D) {
+  size_t bytes = 0;
+  if (check_shape(B, N, H, D, &bytes) != GLA_OK || bytes == 0) return 0;
+  return bwd_layout(B, N, H, D).bytes;
+}
+
+int gla_backward_check(const void* q, const void* k, const void* v, const void* g,
+                       const void* dout, const gla_rope_tables* rope, const void* dq,
+                       const void* dk, const void* dv, const void* dg, int B, int N, int H,
+                       int D) {
+  size_t bytes = 0;
+  int rc = check_shape(B, N, H, D, &bytes);
+  if (rc) return rc;
+  if (bytes == 0) return GLA_OK;
+  if ((rc = check_rope(rope, N, D))) return rc;
+  const void* outs[4] = {dq, dk, dv, dg};
+  for (const void* o : outs)
+    if ((rc = check_tensors({q, k, v, g, dout}, o, bytes))) return rc;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j], bytes)) return GLA_ERR_ALIAS;
+  return check_plan_limits(gla::make_plan(B, N, H, D));
+}
+
+int gla_backward_ws(const void* q, const void* k, const void* v, const void* g, const void* dout,
+                    const gla_rope_tables* rope, void* dq, void* dk, void* dv, void* dg, int B,
+                    int N, int H, int D, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = gla_backward_check(q, k, v, g, dout, rope, dq, dk, dv, dg, B, N, H, D);
+  if (rc) return rc;
+  size_t bytes = 0;
+  check_shape(B, N, H, D, &bytes);
+  if (bytes == 0) return GLA_OK;
+  const BwdLayout l = bwd_layout(B, N, H, D);
+  if (!workspace) return GLA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < l.bytes)
+    return GLA_ERR_WORKSPACE;
+  for (const void* t : {q, k, v, g, dout, static_cast<const void*>(dq),
+                        static_cast<const void*>(dk), static_cast<const void*>(dv),
+                        static_cast<const void*>(dg)})
+    if (overlap2(workspace, l.bytes, t, bytes)) return GLA_ERR_ALIAS;
+  if ((rc = rope_device_ok(rope))) return rc;
+  const Plan& p = l.p;
+  char* w = static_cast<char*>(workspace);
+  uint16_t* sl2 = reinterpret_cast<uint16_t*>(w + l.off_sl2);
+  float* zbuf = reinterpret_cast<float*>(w + l.off_z);
+  float* dzp = reinterpret_cast<float*>(w + l.off_dzp);
+  uint16_t* abuf = reinterpret_cast<uint16_t*>(w + l.off_a);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  gla::BArgs bw{};
+  bw.dout = static_cast<const uint16_t*>(dout);
+  bw.dq = static_cast<uint16_t*>(dq);
+  bw.dk = static_cast<uint16_t*>(dk);
+  bw.dv = static_cast<uint16_t*>(dv);
+  bw.dg = static_cast<uint16_t*>(dg);
+  bw.abuf = abuf;
+  bw.z = zbuf;
+  bw.dzp = dzp;
+  bw.C2 = p.C2;
+
+  // 1. S (both operand layouts) and fp32 z from k and v
+  gla::KArgs a1 = kernel_args(p, rope, p.L, p.CB, workspace);
+  a1.k = static_cast<const uint16_t*>(k);
+  a1.v = static_cast<const uint16_t*>(v);
+  a1.sl2 = sl2;
+  a1.z_out = zbuf;
+  if ((rc = status_of(gla::launch_state(p, a1, s)))) return rc;
+  // 2. query side: dq, dg, a, dz partials
+  gla::KArgs a2 = kernel_args(p, rope, p.L2, p.SUB, workspace);
+  a2.q = static_cast<const uint16_t*>(q);
+  a2.g = static_cast<const uint16_t*>(g);
+  a2.sl2 = sl2;
+  if ((rc = status_of(gla::launch_bwd_query(p, a2, bw, s)))) return rc;
+  // 3. dS (both operand layouts) from q and a: the state pass with q, a in
+  //    the places of k, v
+  gla::KArgs a3 = kernel_args(p, rope, p.L, p.CB, workspace);
+  a3.k = static_cast<const uint16_t*>(q);
+  a3.v = abuf;
+  a3.sl2 = sl2;
+  if ((rc = status_of(gla::launch_state(p, a3, s)))) return rc;
+  // 4. key side: dk, dv
+  gla::KArgs a4 = kernel_args(p, rope, p.L2, p.SUB, workspace);
+  a4.k = static_cast<const uint16_t*>(k);
+  a4.v = static_cast<const uint16_t*>(v);
+  a4.sl2 = sl2;
+  return status_of(gla::launch_bwd_key(p, a4, bw, s));
+}
+
+int gla_backward(const void* q, const void* k, const void* v, const void* g, const void* dout,
+                 const gla_rope_tables* rope, void* dq, void* dk, void* dv, void* dg, int B,
+                 int N, int H, int D, void* stream) {
+  int rc = gla_backward_check(q, k, v, g, dout, rope, dq, dk, dv, dg, B, N, H, D);
+  if (rc) return rc;
+  const size_t need = gla_backward_workspace_bytes(B, N, H, D);
+  if (need == 0) return GLA_OK;
+  void* ws = nullptr;
+  if ((rc = get_workspace(need, stream, &ws))) return rc;
+  return gla_backward_ws(q, k, v, g, dout, rope, dq, dk, dv, dg, B, N, H, D, ws, need, stream);
+}
+
 }  // extern "C"

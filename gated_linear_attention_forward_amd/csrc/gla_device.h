@@ -219,6 +219,47 @@ __device__ __forceinline__ u32x4 rope_chunk(const u32x4 fq, const TabView& tv, c
 }
 
 
+// Loads and non-temporal stores of OB bytes (16, 8 or 4) per lane: one
+// token's owned output columns in the accumulator layout of the 16x16x32
+// MFMA (MB = D / 16 bf16 values).
+template <int OB>
+struct Chunk;
+template <>
+struct Chunk<16> {
+  typedef u32x4 T;
+};
+template <>
+struct Chunk<8> {
+  typedef uint32_t T __attribute__((ext_vector_type(2)));
+};
+template <>
+struct Chunk<4> {
+  typedef uint32_t T __attribute__((ext_vector_type(1)));
+};
+
+template <int OB>
+__device__ __forceinline__ typename Chunk<OB>::T load_chunk(__amdgpu_buffer_rsrc_t r,
+                                                            uint32_t off) {
+  using T = typename Chunk<OB>::T;
+  if constexpr (OB == 16)
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  else if constexpr (OB == 8)
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  else
+    return T{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)};
+}
+
+template <int OB>
+__device__ __forceinline__ void store_chunk_nt(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               typename Chunk<OB>::T v) {
+  if constexpr (OB == 16)
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNt);
+  else if constexpr (OB == 8)
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolNt);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(v[0], r, off, 0, kCpolNt);
+}
+
 constexpr int tile_pitch(int row_bytes) {
   int dw = row_bytes / 4;
   while (dw % 64 != 16 && dw % 64 != 48) ++dw;
@@ -240,6 +281,25 @@ __device__ __forceinline__ bf16x8 frag_tr(const unsigned char* tile, int pitch, 
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---- host-side launch helpers ----
+
+// Bytes of the RoPE table slice a block stages in LDS.
+inline int table_lds_bytes(const KArgs& a) {
+  return 8 * (a.nt * a.Pt + a.Hh * a.Py + a.W * a.Px);
+}
+
+// A kernel that takes more than 64 KB of dynamic LDS raises its limit to the
+// largest size asked for so far (one record per kernel).
+template <auto K>
+hipError_t allow_lds(size_t bytes) {
+  static size_t granted = 0;
+  if (bytes <= 65536 || bytes <= granted) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(K),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) granted = bytes;
+  return e;
 }
 
 }  // namespace

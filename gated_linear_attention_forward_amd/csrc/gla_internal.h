@@ -46,6 +46,8 @@ struct KArgs {
   float* part;           // [BH][C][D*D + D] fp32 chunk partials
   uint16_t* sl;          // [BH][NB][D + 2][D] bf16: per attention block, the state
                          // S^T rows in output order, then z hi/lo rows
+  uint16_t* sl2;         // optional [BH][NB][D][D] bf16: the state's rows S[d][0..D)
+                         // in the same row order (row R(d) holds row d)
   float* S_out;          // optional fp32 S [BH][D][D] after the last block
   float* z_out;          // optional fp32 z [BH][D] after the last block
   const float* S_in;     // optional carried fp32 S [BH][D][D] (NULL: zero)
@@ -81,6 +83,25 @@ hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream);
 // into qr, rotated k into kr, [B, N, H, D] bf16 each) then the flash kernel.
 // Reads a.q, a.k, a.v, a.g, a.cs (nullptr: RoPE off), writes a.out.
 hipError_t launch_softmax(const Plan& p, KArgs a, uint16_t* qr, uint16_t* kr, hipStream_t stream);
+
+// Backward pass of the bidirectional mixer (gla_backward.hip).
+struct BArgs {
+  const uint16_t* dout;  // output gradient [B, N, H, D] bf16
+  uint16_t* dq;          // gradients written [B, N, H, D] bf16
+  uint16_t* dk;
+  uint16_t* dv;
+  uint16_t* dg;
+  uint16_t* abuf;        // [B, N, H, D] bf16: a = dout * sigmoid(g) / den
+  const float* z;        // forward z [BH][D] fp32
+  float* dzp;            // [BH][C2][D] fp32 per-range partial sums of dz
+  int C2;                // query/key kernel ranges per head
+};
+// Query side: reads q, g, dout and the state operands a.sl (S^T rows + z
+// rows) and a.sl2 (S rows); writes dq, dg, abuf and dzp.
+hipError_t launch_bwd_query(const Plan& p, KArgs a, BArgs b, hipStream_t stream);
+// Key side: reads k, v, the gradient-state operands a.sl (dS^T rows) and
+// a.sl2 (dS rows) and dzp; writes dk, dv.
+hipError_t launch_bwd_key(const Plan& p, KArgs a, BArgs b, hipStream_t stream);
 
 // Tile sizes the plan has to respect.
 constexpr int kOutputTileTokens = 64;

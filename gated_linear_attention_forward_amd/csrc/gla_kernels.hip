@@ -595,8 +595,10 @@ void state_half_kernel(KArgs a) {
 // runs.  The first tile's block also reduces z.
 // Outputs per head and attention block, in the output kernel's operand
 // layout (D + 2 rows of D bf16): row R(e) holds S_<=b[0..D)[e] (see
-// out_row_of); row D holds bf16(z), row D + 1 holds bf16(z - bf16(z)).  The
-// fp32 state after the last block optionally goes to the caller.
+// out_row_of); row D holds bf16(z), row D + 1 holds bf16(z - bf16(z)).
+// Optionally also the row-major operand (D rows: row R(d) holds S[d][0..D),
+// which the backward pass contracts over the value index).  The fp32 state
+// after the last block optionally goes to the caller.
 
 // Output-kernel operand row of value column e: with MB = D/16 column blocks,
 // row 16 j + c holds column MB c + j, so that lane column c of block j owns
@@ -719,6 +721,13 @@ __global__ __launch_bounds__(256) void reduce_kernel(KArgs a) {
       }
     }
     acc = acc + s_blk;
+    if (a.sl2) {
+      // the row-major operand: row R(d) holds S[d][0..D), 4 columns per thread
+      typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+      uint16_t* r2 = a.sl2 + ((size_t)bh * a.NB + blk) * D * D;
+      *reinterpret_cast<u32x2v*>(r2 + (size_t)out_row_of<D>(d0 + dl) * D + e0 + el) =
+          u32x2v{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) tile[(el + k) * Rc::TP + dl] = acc[k];
     __syncthreads();
@@ -775,44 +784,6 @@ __global__ __launch_bounds__(256) void reduce_kernel(KArgs a) {
 // phi(q).z uses the unrotated features, exact in bf16, against B columns
 // that alternate bf16(z) and bf16(z - bf16(z)); adding the neighbouring
 // lane's value gives phi(q).z in fp32 for the same four tokens.
-template <int OB>
-struct Chunk;
-template <>
-struct Chunk<16> {
-  typedef u32x4 T;
-};
-template <>
-struct Chunk<8> {
-  typedef uint32_t T __attribute__((ext_vector_type(2)));
-};
-template <>
-struct Chunk<4> {
-  typedef uint32_t T __attribute__((ext_vector_type(1)));
-};
-
-template <int OB>
-__device__ __forceinline__ typename Chunk<OB>::T load_chunk(__amdgpu_buffer_rsrc_t r,
-                                                            uint32_t off) {
-  using T = typename Chunk<OB>::T;
-  if constexpr (OB == 16)
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  else if constexpr (OB == 8)
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-  else
-    return T{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)};
-}
-
-template <int OB>
-__device__ __forceinline__ void store_chunk_nt(__amdgpu_buffer_rsrc_t r, uint32_t off,
-                                               typename Chunk<OB>::T v) {
-  if constexpr (OB == 16)
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNt);
-  else if constexpr (OB == 8)
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpolNt);
-  else
-    __builtin_amdgcn_raw_buffer_store_b32(v[0], r, off, 0, kCpolNt);
-}
-
 template <int D, bool ROPE, bool TLDS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void output_kernel(KArgs a) {
@@ -984,9 +955,6 @@ constexpr int output_lds_bytes() {
   return (D + 2) * (D * 2 + 16);
 }
 
-int table_lds_bytes(const KArgs& a) {
-  return 8 * (a.nt * a.Pt + a.Hh * a.Py + a.W * a.Px);
-}
 
 
 template <int D, int P>
@@ -995,17 +963,6 @@ void launch_reduce(const Plan& p, const KArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((reduce_kernel<D, P>), g2, dim3(256), 0, stream, a);
 }
 
-// A kernel that takes more than 64 KB of dynamic LDS raises its limit to the
-// largest size asked for so far (one record per kernel).
-template <auto K>
-hipError_t allow_lds(size_t bytes) {
-  static size_t granted = 0;
-  if (bytes <= 65536 || bytes <= granted) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(K),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) granted = bytes;
-  return e;
-}
 
 template <int D, bool ROPE, bool TLDS>
 hipError_t launch_state_k(const Plan& p, const KArgs& a, size_t lds, hipStream_t stream) {

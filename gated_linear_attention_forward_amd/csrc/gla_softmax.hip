@@ -278,15 +278,6 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
     }
 }
 
-template <auto K>
-hipError_t allow_lds(size_t bytes) {
-  static size_t granted = 0;
-  if (bytes <= 65536 || bytes <= granted) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(K),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) granted = bytes;
-  return e;
-}
 
 template <int D>
 hipError_t launch_softmax_d(const Plan& p, KArgs a, uint16_t* qr, uint16_t* kr,

@@ -33,7 +33,8 @@ EXPORTS = (
     "gla_forward_check", "gla_state_ws", "gla_output_ws", "gla_state",
     "gla_forward_blocks", "gla_forward_blocks_ws", "gla_workspace_bytes_blocks",
     "gla_forward_blocks_check", "gla_softmax_forward", "gla_softmax_forward_ws",
-    "gla_softmax_workspace_bytes", "gla_softmax_forward_check",
+    "gla_softmax_workspace_bytes", "gla_softmax_forward_check", "gla_backward",
+    "gla_backward_ws", "gla_backward_workspace_bytes", "gla_backward_check",
 )
 
 
@@ -91,6 +92,10 @@ def load_library():
         "gla_softmax_forward_ws": ([vp] * 4 + [rp, vp] + [i32] * 4 + [vp, sz, vp], i32),
         "gla_softmax_workspace_bytes": ([i32] * 4, sz),
         "gla_softmax_forward_check": ([vp] * 4 + [rp, vp] + [i32] * 4, i32),
+        "gla_backward": ([vp] * 5 + [rp] + [vp] * 4 + [i32] * 4 + [vp], i32),
+        "gla_backward_ws": ([vp] * 5 + [rp] + [vp] * 4 + [i32] * 4 + [vp, sz, vp], i32),
+        "gla_backward_workspace_bytes": ([i32] * 4, sz),
+        "gla_backward_check": ([vp] * 5 + [rp] + [vp] * 4 + [i32] * 4, i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -430,3 +435,66 @@ def gla_softmax_forward_ws(q, k, v, g, rope, ws: torch.Tensor, out=None, stream=
                                                   _stream_handle(stream, q.device)),
             "gla_softmax_forward_ws")
     return out
+
+
+# ---------------------------------------------------------------------------
+# backward pass of the bidirectional mixer
+
+
+def gla_backward_workspace_bytes(B: int, N: int, H: int, D: int) -> int:
+    return load_library().gla_backward_workspace_bytes(B, N, H, D)
+
+
+def alloc_workspace_backward(B, N, H, D, device=None) -> torch.Tensor:
+    """A torch-owned uint8 device buffer large enough for gla_backward_ws."""
+    return torch.empty(max(gla_backward_workspace_bytes(B, N, H, D), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def gla_backward_check(q, k, v, g, dout, rope, dq, dk, dv, dg, B, N, H, D) -> int:
+    """Status of the library's argument validation (pointers as integers)."""
+    return load_library().gla_backward_check(q, k, v, g, dout, _rope_ptr(rope), dq, dk, dv, dg,
+                                             B, N, H, D)
+
+
+def _backward_args(q, k, v, g, dout, grads):
+    _check_bf16("q", q)
+    for name, t in (("k", k), ("v", v), ("g", g), ("dout", dout)):
+        _check_bf16(name, t, q.shape)
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    out = []
+    for name, t in zip(("dq", "dk", "dv", "dg"), grads):
+        if t is None:
+            t = torch.empty_like(q)
+        else:
+            _check_bf16(name, t, q.shape)
+        out.append(t)
+    return out
+
+
+def gla_backward(q, k, v, g, dout, rope=None, dq=None, dk=None, dv=None, dg=None, stream=None):
+    """(dq, dk, dv, dg), bf16 [B, N, H, D]: gradients of the mixer given dout."""
+    grads = _backward_args(q, k, v, g, dout, (dq, dk, dv, dg))
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                        dout.data_ptr(), _rope_ptr(rope),
+                                        *(t.data_ptr() for t in grads), B, N, H, D,
+                                        _stream_handle(stream, q.device)),
+            "gla_backward")
+    return tuple(grads)
+
+
+def gla_backward_ws(q, k, v, g, dout, rope, ws: torch.Tensor, dq=None, dk=None, dv=None, dg=None,
+                    stream=None):
+    grads = _backward_args(q, k, v, g, dout, (dq, dk, dv, dg))
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_backward_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           g.data_ptr(), dout.data_ptr(), _rope_ptr(rope),
+                                           *(t.data_ptr() for t in grads), B, N, H, D,
+                                           ws.data_ptr(), ws.numel() * ws.element_size(),
+                                           _stream_handle(stream, q.device)),
+            "gla_backward_ws")
+    return tuple(grads)

@@ -248,6 +248,54 @@ int gla_softmax_forward_check(const void* q, const void* k, const void* v, const
                               const gla_rope_tables* rope, const void* out, int B, int N, int H,
                               int D);
 
+/* ---------------------------------------------------------------------
+ * Backward pass of the bidirectional mixer.
+ *
+ * The exact derivative of gla_forward, for training the linear layers
+ * ("SANA-Video 2.0: Hybrid Linear Attention with Attention Residuals ..."
+ * (mlsanity index), Abstract: the hybrid is trained; the pages give no
+ * formula, so this is the chain rule through the form at the top of this
+ * file).  Given dout = dL/dout, per batch b and head h, with
+ * fq = phi(q_n), rq = R_n fq, den = fq . z + 1e-6, s = sigmoid(g_n),
+ * num = S^T rq and o_n = s * num / den:
+ *
+ *     dg_n = dout_n * o_n * (1 - s)
+ *     a_n  = dout_n * s / den,         dden_n = -(dout_n . o_n) / den
+ *     dq_n = [q_n > 0] * (R_n^T (S a_n) + dden_n z)
+ *     dS   = sum_n rq a_n^T,           dz = sum_n dden_n fq
+ *     dv_m = dS^T (R_m phi(k_m))
+ *     dk_m = [k_m > 0] * (R_m^T (dS v_m) + dz)
+ *
+ * The derivative of phi at 0 is taken as 0.  q, k, v, g, dout: device bf16
+ * [B, N, H, D] inputs; dq, dk, dv, dg: device bf16 [B, N, H, D] outputs
+ * (written in full), each 16-byte aligned, overlapping no input and no
+ * other output.  D must be 32, 64 or 128; rope as for gla_forward (NULL:
+ * RoPE off).  S and z are recomputed from k and v (no saved state is
+ * needed).  The contractions run on bf16 MFMA with fp32 accumulation: S, dS,
+ * the rotated features and a_n are rounded to bf16 as MFMA operands.  Uses
+ * a library-owned workspace (grown with hipMalloc, which may synchronise).
+ * B*N*H == 0 is a no-op.  Results are bitwise reproducible. */
+int gla_backward(const void* q, const void* k, const void* v, const void* g, const void* dout,
+                 const gla_rope_tables* rope, void* dq, void* dk, void* dv, void* dg, int B,
+                 int N, int H, int D, void* stream);
+
+/* Workspace bytes gla_backward_ws needs (the forward's partials and state
+ * operands, the S rows operand, z, dz partials and the bf16 a_n tensor of
+ * B*N*H*D elements), 0 for bad shapes or B*N*H == 0. */
+size_t gla_backward_workspace_bytes(int B, int N, int H, int D);
+
+/* gla_backward with a caller-owned device workspace (>= the size above,
+ * 256-byte aligned, overlapping no tensor).  Never allocates. */
+int gla_backward_ws(const void* q, const void* k, const void* v, const void* g, const void* dout,
+                    const gla_rope_tables* rope, void* dq, void* dk, void* dv, void* dg, int B,
+                    int N, int H, int D, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Argument validation of gla_backward alone (no HIP call). */
+int gla_backward_check(const void* q, const void* k, const void* v, const void* g,
+                       const void* dout, const gla_rope_tables* rope, const void* dq,
+                       const void* dk, const void* dv, const void* dg, int B, int N, int H,
+                       int D);
+
 #ifdef __cplusplus
 }
 #endif

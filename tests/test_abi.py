@@ -237,3 +237,47 @@ def test_softmax_workspace_size():
     assert gla.gla_softmax_workspace_bytes(2, 22000, 10, 256) >= 2 * 2 * 22000 * 10 * 256 * 2
     assert gla.gla_softmax_workspace_bytes(1, 10, 1, 64) == 0
     assert gla.gla_softmax_workspace_bytes(0, 10, 1, 256) == 0
+
+
+# ---------------------------------------------------------------------------
+# backward pass: validation without a GPU
+
+
+def bcheck_bwd(**kw):
+    args = dict(q=A, k=2 * A, v=3 * A, g=4 * A, dout=5 * A, rope=None, dq=6 * A, dk=7 * A,
+                dv=8 * A, dg=9 * A, B=1, N=64, H=2, D=128)
+    args.update(kw)
+    return gla.gla_backward_check(*(args[n] for n in ("q", "k", "v", "g", "dout", "rope", "dq",
+                                                      "dk", "dv", "dg", "B", "N", "H", "D")))
+
+
+def test_backward_validation():
+    assert bcheck_bwd() == 0 and bcheck_bwd(D=32) == 0 and bcheck_bwd(D=64) == 0
+    for D in (16, 48, 256):
+        assert bcheck_bwd(D=D) == glamod.GLA_ERR_DIM
+    assert bcheck_bwd(dout=0) == glamod.GLA_ERR_NULL
+    assert bcheck_bwd(dk=0) == glamod.GLA_ERR_NULL
+    assert bcheck_bwd(dg=9 * A + 8) == glamod.GLA_ERR_ALIGN
+    assert bcheck_bwd(N=0) == 0 and bcheck_bwd(B=0, q=0) == 0
+    assert bcheck_bwd(N=64, rope=_host_rope(4, 4, 4, 128)) == 0
+    assert bcheck_bwd(N=64, rope=_host_rope(4, 4, 4, 64)) == glamod.GLA_ERR_ROPE
+
+
+def test_backward_alias_detection():
+    nbytes = 1 * 64 * 2 * 128 * 2
+    assert bcheck_bwd(dq=A) == glamod.GLA_ERR_ALIAS             # dq is q
+    assert bcheck_bwd(dv=5 * A + nbytes - 16) == glamod.GLA_ERR_ALIAS  # dv overlaps dout
+    assert bcheck_bwd(dk=6 * A) == glamod.GLA_ERR_ALIAS         # two outputs share memory
+    assert bcheck_bwd(dg=6 * A + nbytes - 16) == glamod.GLA_ERR_ALIAS  # dg overlaps dq's end
+    assert bcheck_bwd(dg=6 * A + nbytes) == 0                   # dg right after dq
+    assert bcheck_bwd(dg=10 * A) == 0
+
+
+def test_backward_workspace_size():
+    for (B, N, H, D) in ((1, 256, 2, 32), (2, 22000, 20, 128)):
+        ws = gla.gla_backward_workspace_bytes(B, N, H, D)
+        # the forward's workspace, the S rows operand, z, and the bf16 a tensor
+        assert ws >= gla.gla_workspace_bytes(B, N, H, D) + B * H * D * D * 2 + B * N * H * D * 2
+        assert ws % 256 == 0
+    assert gla.gla_backward_workspace_bytes(1, 0, 2, 128) == 0
+    assert gla.gla_backward_workspace_bytes(1, 10, 1, 48) == 0
