@@ -16,8 +16,9 @@ the kernel source differs from the one those counters were taken on.
 `cpu_baseline` times the fp64 oracle on a sample of the workload's heads
 (about ten seconds of CPU work) and scales to the whole workload.
 
-`--block-frames F` times the block-causal form instead, and `--softmax` the
-gated softmax anchor attention (an MFMA-bound roofline in TFLOP/s).
+`--block-frames F` times the block-causal form instead, `--softmax` the
+gated softmax anchor attention (an MFMA-bound roofline in TFLOP/s) and
+`--backward` the mixer's backward pass.
 """
 from __future__ import annotations
 
@@ -266,6 +267,98 @@ def softmax_bench(args, w, gla, dev, tensors, rope, stream):
     print(json.dumps(result), flush=True)
 
 
+def backward_cpu_baseline(w, q, k, v, g, dout, min_seconds=10.0):
+    """Times the fp64 oracle's backward on the first `hs` heads of batch
+    element 0 (one head per oracle thread) until about `min_seconds` of CPU
+    work, and scales the per-head time to the whole workload."""
+    import oracle
+    grid = oracle.Grid(w.T, w.Hh, w.W, w.theta)
+    threads = oracle.num_threads()
+    hs = max(1, min(w.H, threads))
+    qs, ks, vs, gs, ds = (t[:1, :, :hs].contiguous() for t in (q, k, v, g, dout))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.backward(qs, ks, vs, gs, ds, grid)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    per_head = dt / (reps * hs)
+    return {
+        "value": (w.B * w.N) / (per_head * w.B * w.H),
+        "unit": "tokens/s",
+        "cores": hs,
+        "kind": "oracle",
+        "sample": f"{hs} of {w.B * w.H} heads (batch 0, all N={w.N} tokens), {reps} passes in "
+                  f"{dt:.1f} s; {per_head:.3f} s per head, scaled to {w.B * w.H} heads",
+    }
+
+
+def backward_bench(args, w, gla, dev, tensors, rope, stream):
+    """Backward pass: K passes of gla_backward_ws (state, query, gradient
+    state and key kernels).  The roofline is the whole pass against the
+    algorithmic minimum of 18*D bytes per (token, head): q, k, v, g and dout
+    read, dq, dk, dv and dg written, once each."""
+    import torch
+
+    from workloads import random_grad
+    qd, kd, vd, gd = tensors
+    dout = random_grad(w.B, w.N, w.H, w.D, seed=w.seed + 1000).to(dev)
+    grads = [torch.empty_like(qd) for _ in range(4)]
+    ws = gla.alloc_workspace_backward(w.B, w.N, w.H, w.D, dev)
+
+    def step():
+        gla.gla_backward_ws(qd, kd, vd, gd, dout, rope, ws, *grads, stream=stream)
+
+    log(f"bench: backward; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    log(f"bench: {args.steps} instrumented steps")
+    for e in evs:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ev_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    units = w.B * w.N * w.H
+    nbytes = 18 * w.D * units
+    achieved = nbytes / (ev_ms * 1e-3) / 1e9
+    result = {
+        "metric": "gated linear-attn backward tokens/s per layer; achieved HBM GB/s vs peak",
+        "value": w.B * w.N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "D": w.D,
+                   "grid": [w.T, w.Hh, w.W], "parallelism": "single-gpu"},
+        "roofline": {"kernel": "whole backward (state, query, gradient state, key kernels)",
+                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "algorithmic_bytes": nbytes, "avg_ms": ev_ms},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle (cpu_baseline)")
+        q, k, v, g = (t.cpu() for t in tensors)
+        result["cpu_baseline"] = backward_cpu_baseline(w, q, k, v, g, dout.cpu())
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +375,8 @@ def main():
     ap.add_argument("--softmax", action="store_true",
                     help="time the gated softmax anchor attention (gla_softmax_forward) "
                          "instead; the workload defaults to anchor_5b_720p_193f")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the mixer's backward pass (gla_backward) instead")
     args = ap.parse_args()
     if args.softmax and args.workload == DEFAULT_WORKLOAD:
         args.workload = "anchor_5b_720p_193f"
@@ -308,6 +403,9 @@ def main():
         copy_calibration(dev)
     if args.softmax:
         softmax_bench(args, w, gla, dev, (qd, kd, vd, gd), rope, stream)
+        return
+    if args.backward:
+        backward_bench(args, w, gla, dev, (qd, kd, vd, gd), rope, stream)
         return
     out = torch.empty_like(qd)
     ws = gla.alloc_workspace(w.B, w.N, w.H, w.D, dev)
