@@ -11,7 +11,9 @@ arithmetic, one (b, h) head at a time: first the state S and normaliser z,
 then every token's output.  ``forward_blocks`` is the block-causal form with
 a carried state; ``softmax_rows`` the gated softmax anchor attention;
 ``backward`` (and its state / row helpers) the exact derivative of the
-bidirectional mixer given the output gradient.  See gla_oracle.c for the exact forms and the readings they
+bidirectional mixer given the output gradient; ``project`` the linear maps
+producing q, k, v, g from the hidden states and ``projected_forward`` the
+projections followed by the mixer.  See gla_oracle.c for the exact forms and the readings they
 take where the pages are silent.
 
 Inputs are bf16 bit patterns (numpy uint16 arrays, or torch bfloat16 CPU
@@ -79,6 +81,13 @@ def _load():
     lib.gla_oracle_softmax_rows.argtypes = ([u16p] * 4 + [c_int] * 4 + grid +
                                             [c_int, c_int, lp, c_long, dp])
     lib.gla_oracle_softmax_rows.restype = c_int
+    lib.gla_oracle_round_bf16.argtypes = [c_double]
+    lib.gla_oracle_round_bf16.restype = ctypes.c_uint16
+    lib.gla_oracle_round_bf16_array.argtypes = [dp, c_long, u16p]
+    lib.gla_oracle_round_bf16_array.restype = None
+    lib.gla_oracle_project.argtypes = [u16p, u16p, c_int, c_int, c_int, c_int,
+                                       ctypes.POINTER(c_int), c_int, dp]
+    lib.gla_oracle_project.restype = c_int
     lib.gla_oracle_backward.argtypes = ([u16p] * 5 + [c_int] * 4 + grid +
                                         [c_double, dp, dp, dp, dp])
     lib.gla_oracle_backward.restype = c_int
@@ -341,3 +350,47 @@ def backward_kv_rows(k, v, grid: Grid | None, b: int, h: int, dS_bh, dz_bh, toke
                                                _p(r, ctypes.c_long), r.shape[0],
                                                _p(dk, ctypes.c_double), _p(dv, ctypes.c_double)))
     return dk, dv
+
+
+def round_bf16(values) -> np.ndarray:
+    """bf16 bit patterns (uint16) of doubles rounded to nearest, ties to even."""
+    a = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(a.shape, np.uint16)
+    _load().gla_oracle_round_bf16_array(_p(a, ctypes.c_double), a.size, _p(out, ctypes.c_uint16))
+    return out
+
+
+def project(x, w, features) -> np.ndarray:
+    """x [B, N, C] and w [P, C] bf16: the fp64 products x w[features]^T,
+    [B, N, len(features)]."""
+    x, w = as_bits(x), as_bits(w)
+    if w.ndim == 3:                       # stacked [4, H*D, C]
+        w = np.ascontiguousarray(w.reshape(-1, w.shape[-1]))
+    if x.ndim != 3 or w.ndim != 2 or x.shape[2] != w.shape[1]:
+        raise ValueError("x must be [B, N, C] and w [P, C] (or [4, H*D, C])")
+    B, N, C = x.shape
+    feat = np.ascontiguousarray(features, dtype=np.int32)
+    out = np.empty((B, N, feat.shape[0]), np.float64)
+    _check(_load().gla_oracle_project(_p(x, ctypes.c_uint16), _p(w, ctypes.c_uint16), B, N, C,
+                                      w.shape[0], _p(feat, ctypes.c_int), feat.shape[0],
+                                      _p(out, ctypes.c_double)))
+    return out
+
+
+def projected_heads(x, w, H: int, D: int, heads, which="qkvg"):
+    """bf16 bit patterns of the projections of the given heads, each
+    [B, N, len(heads), D]: dict map name -> array (maps stacked q, k, v, g)."""
+    idx = {"q": 0, "k": 1, "v": 2, "g": 3}
+    out = {}
+    for name in which:
+        feats = np.concatenate([idx[name] * H * D + h * D + np.arange(D) for h in heads])
+        y = project(x, w, feats)
+        B, N = y.shape[:2]
+        out[name] = round_bf16(y).reshape(B, N, len(heads), D)
+    return out
+
+
+def projected_forward(x, w, H: int, D: int, grid: Grid | None, eps: float = EPS) -> np.ndarray:
+    """The projections rounded to bf16, then the mixer: [B, N, H, D] fp64."""
+    t = projected_heads(x, w, H, D, range(H))
+    return forward(t["q"], t["k"], t["v"], t["g"], grid, eps)

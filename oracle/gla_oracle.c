@@ -26,7 +26,8 @@
  * "SANA-Video_2B_720p" model card, innovation (2)); gla_oracle_softmax_rows
  * the gated softmax anchor attention of the other quarter of the layers;
  * gla_oracle_backward and its row/state helpers the exact derivative of the
- * bidirectional mixer; see their comments.
+ * bidirectional mixer; gla_oracle_project the linear maps that produce q, k,
+ * v and g from the hidden states; see their comments.
  *
  * RoPE reading (the pages only name "Wan 3D rotary position embeddings"):
  *   - the D/2 rotation pairs are (2i, 2i+1), interleaved;
@@ -758,4 +759,59 @@ int gla_oracle_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     }
   }
   return err;
+}
+
+/* ---------------------------------------------------------------------------
+ * Projection prologue: the linear maps that produce q, k, v and g from the
+ * hidden states ("SANA-Video 2.0", NVlabs Sana docs, section Architecture:
+ * hidden size 2,560 with 20 heads x 128 at 5B, 4,096 with 32 heads x 128 at
+ * 14B).  The pages give no further detail; the reading taken is four
+ * bias-free linear maps, y = x W^T with W of shape [H*D, C] per map (the
+ * weights stacked as [4][H*D][C] in the order q, k, v, g), each result
+ * rounded to bf16 as a BF16 model stores it (section Model zoo: BF16
+ * inference), and then the mixer above on the four bf16 tensors.
+ * ------------------------------------------------------------------------ */
+
+/* Round a double to the nearest bf16 value (ties to even) and return its
+ * bit pattern.  bf16 keeps 8 significant bits: with x = f 2^E, 0.5 <= |f| < 1,
+ * the spacing is 2^(E-8).  Finite inputs of normal bf16 magnitude only
+ * (|x| in [2^-126, 2^127]) or zero. */
+uint16_t gla_oracle_round_bf16(double x) {
+  if (x == 0.0) return signbit(x) ? 0x8000 : 0;
+  int E;
+  frexp(x, &E);
+  double ulp = ldexp(1.0, E - 8);
+  double r = nearbyint(x / ulp) * ulp;   /* default rounding: nearest, ties to even */
+  float f = (float)r;                    /* exact: r has 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+/* out[b][n][i] = sum_c x[b][n][c] * w[feat[i]][c] in fp64, for the nfeat
+ * output features listed in feat (rows of the stacked [4*H*D][C] weights).
+ * x: bf16 [B, N, C]; w: bf16 [P, C]; out: [B, N, nfeat] doubles. */
+int gla_oracle_project(const uint16_t* x, const uint16_t* w, int B, int N, int C, int P,
+                       const int* feat, int nfeat, double* out) {
+  if (B < 0 || N < 0 || C <= 0 || P <= 0 || nfeat < 0) return ORACLE_ERR_ARG;
+  for (int i = 0; i < nfeat; ++i)
+    if (feat[i] < 0 || feat[i] >= P) return ORACLE_ERR_ARG;
+  long rows = (long)B * N;
+#pragma omp parallel for schedule(static)
+  for (long r = 0; r < rows; ++r) {
+    const uint16_t* xr = x + r * (long)C;
+    for (int i = 0; i < nfeat; ++i) {
+      const uint16_t* wr = w + (long)feat[i] * C;
+      double acc = 0.0;
+      for (int c = 0; c < C; ++c)
+        acc += gla_oracle_bf16_to_f64(xr[c]) * gla_oracle_bf16_to_f64(wr[c]);
+      out[r * nfeat + i] = acc;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* gla_oracle_round_bf16 over an array. */
+void gla_oracle_round_bf16_array(const double* in, long n, uint16_t* out) {
+  for (long i = 0; i < n; ++i) out[i] = gla_oracle_round_bf16(in[i]);
 }

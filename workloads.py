@@ -35,6 +35,7 @@ class Workload:
     qk_scale: float
     seed: int
     theta: float = 10000.0
+    C: int = 0      # hidden size of the projection workloads (0: mixer inputs only)
 
     @property
     def N(self) -> int:
@@ -62,7 +63,21 @@ ANCHOR_WORKLOADS = [
     Workload("anchor_5b_720p_193f", B=2, H=10, D=256, T=25, Hh=22, W=40, qk_scale=1.0, seed=12),
     Workload("anchor_14b_480p_193f", B=2, H=16, D=256, T=25, Hh=15, W=26, qk_scale=1.0, seed=13),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS + ANCHOR_WORKLOADS}
+# The projection prologue of the linear layers: hidden states x [B, N, C]
+# with C = 2,560 (5B) or 4,096 (14B) (section Architecture) and the four
+# stacked maps q, k, v, g of shape [4, H*D, C].
+PROJ_WORKLOADS = [
+    Workload("proj_tiny_d32_4x8x8", B=1, H=2, D=32, T=4, Hh=8, W=8, qk_scale=1.0, seed=20, C=128),
+    Workload("proj_5b_480p_81f", B=1, H=20, D=128, T=11, Hh=15, W=26, qk_scale=1.0, seed=21,
+             C=2560),
+    Workload("proj_5b_720p_193f", B=2, H=20, D=128, T=25, Hh=22, W=40, qk_scale=1.0, seed=22,
+             C=2560),
+    Workload("proj_14b_480p_193f", B=2, H=32, D=128, T=25, Hh=15, W=26, qk_scale=1.0, seed=23,
+             C=4096),
+    Workload("proj_5b_720p_60s", B=1, H=20, D=128, T=181, Hh=22, W=40, qk_scale=1.0, seed=24,
+             C=2560),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + ANCHOR_WORKLOADS + PROJ_WORKLOADS}
 
 
 def random_inputs(B: int, N: int, H: int, D: int, seed: int, qk_scale: float = 1.0):
@@ -86,6 +101,24 @@ def random_grad(B: int, N: int, H: int, D: int, seed: int):
     gen.manual_seed(seed)
     x = torch.randn((B, N, H, D), generator=gen, dtype=torch.float32)
     return x.to(torch.bfloat16)
+
+
+def random_projection(B: int, N: int, C: int, H: int, D: int, seed: int):
+    """(x, w): hidden states x [B, N, C] iid N(0, 1) and stacked weights
+    w [4, H*D, C] iid N(0, 1/C) (so each projection is ~N(0, 1) like the
+    mixer's own inputs), drawn in that order from one seeded CPU generator
+    in fp32 and rounded to bf16."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    x = torch.randn((B, N, C), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    w = torch.randn((4, H * D, C), generator=gen, dtype=torch.float32)
+    w = w.mul_(C ** -0.5).to(torch.bfloat16)
+    return x, w
+
+
+def make_projection(w: Workload, seed: int | None = None):
+    """Seeded (x, w) of a projection workload."""
+    return random_projection(w.B, w.N, w.C, w.H, w.D, w.seed if seed is None else seed)
 
 
 def make_inputs(w: Workload, seed: int | None = None):
