@@ -1,7 +1,7 @@
 """Gated linear-attention token mixer for AMD MI355X (gfx950): the
-bidirectional mixer and its backward pass, its block-causal form with a
-carried state, and the gated softmax anchor attention of the hybrid's other
-layers.
+bidirectional mixer and its backward pass, the projection prologue fused
+with it, its block-causal form with a carried state, and the gated softmax
+anchor attention of the hybrid's other layers.
 
 The compute path is libgla.so (C ABI in include/gla.h, HIP kernels in
 csrc/); this package is its thin ctypes binding.
@@ -13,6 +13,7 @@ from .gla import (  # noqa: F401
     alloc_workspace,
     alloc_workspace_backward,
     alloc_workspace_blocks,
+    alloc_workspace_proj,
     alloc_workspace_softmax,
     gla_backward,
     gla_backward_check,
@@ -23,8 +24,12 @@ from .gla import (  # noqa: F401
     gla_forward_blocks_check,
     gla_forward_blocks_ws,
     gla_forward_check,
+    gla_forward_proj,
+    gla_forward_proj_check,
+    gla_forward_proj_ws,
     gla_forward_ws,
     gla_output_ws,
+    gla_proj_workspace_bytes,
     gla_rope_create,
     gla_rope_destroy,
     gla_rope_fill_host,

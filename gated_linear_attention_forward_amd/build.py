@@ -37,7 +37,7 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    for src in ("gla_kernels.hip", "gla_softmax.hip", "gla_backward.hip"):
+    for src in ("gla_kernels.hip", "gla_softmax.hip", "gla_backward.hip", "gla_project.hip"):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         _run(["hipcc", *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
               os.path.join(CSRC, src), "-o", obj], verbose)

@@ -767,3 +767,109 @@ int gla_backward(const void* q, const void* k, const void* v, const void* g, con
 }
 
 }  // extern "C"
+
+// ---- projection prologue fused with the mixer ------------------------------
+
+namespace {
+
+// Workspace: the forward plan's partials and state operand, then the
+// projected q and g.
+struct ProjLayout {
+  Plan p;
+  size_t off_q, off_g, bytes;
+};
+
+ProjLayout proj_layout(int B, int N, int H, int D) {
+  ProjLayout l{};
+  l.p = gla::make_plan(B, N, H, D);
+  const size_t t = (size_t)B * N * H * D * sizeof(uint16_t);
+  size_t off = l.p.ws_bytes;
+  l.off_q = off;
+  off = gla::align_up(off + t, 256);
+  l.off_g = off;
+  off = gla::align_up(off + t, 256);
+  l.bytes = off;
+  return l;
+}
+
+int check_proj_shape(int B, int N, int C, int H, int D, size_t* out_bytes) {
+  int rc = check_shape(B, N, H, D, out_bytes);
+  if (rc) return rc;
+  if (C < 64 || C % 64 != 0) return GLA_ERR_DIM;
+  if ((long long)N * C * 2 >= (1LL << 31)) return GLA_ERR_DIM;           // x slab offsets
+  if (4LL * H * D * C * 2 >= (1LL << 31)) return GLA_ERR_DIM;            // weight offsets
+  if ((long long)(N + gla::kProjTileTokens - 1) / gla::kProjTileTokens > 65535) return GLA_ERR_DIM;
+  return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gla_proj_workspace_bytes(int B, int N, int C, int H, int D) {
+  size_t bytes = 0;
+  if (check_proj_shape(B, N, C, H, D, &bytes) != GLA_OK || bytes == 0) return 0;
+  return proj_layout(B, N, H, D).bytes;
+}
+
+int gla_forward_proj_check(const void* x, const void* w, const gla_rope_tables* rope,
+                           const void* out, int B, int N, int C, int H, int D) {
+  size_t bytes = 0;
+  int rc = check_proj_shape(B, N, C, H, D, &bytes);
+  if (rc) return rc;
+  if (bytes == 0) return GLA_OK;
+  if ((rc = check_rope(rope, N, D))) return rc;
+  if (!x || !w || !out) return GLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return GLA_ERR_ALIGN;
+  const size_t xb = (size_t)B * N * C * 2, wb = (size_t)4 * H * D * C * 2;
+  if (overlap2(out, bytes, x, xb) || overlap2(out, bytes, w, wb)) return GLA_ERR_ALIAS;
+  return check_plan_limits(gla::make_plan(B, N, H, D));
+}
+
+int gla_forward_proj_ws(const void* x, const void* w, const gla_rope_tables* rope, void* out,
+                        int B, int N, int C, int H, int D, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int rc = gla_forward_proj_check(x, w, rope, out, B, N, C, H, D);
+  if (rc) return rc;
+  size_t bytes = 0;
+  check_proj_shape(B, N, C, H, D, &bytes);
+  if (bytes == 0) return GLA_OK;
+  const ProjLayout l = proj_layout(B, N, H, D);
+  if (!workspace) return GLA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < l.bytes)
+    return GLA_ERR_WORKSPACE;
+  const size_t xb = (size_t)B * N * C * 2, wb = (size_t)4 * H * D * C * 2;
+  if (overlap2(workspace, l.bytes, x, xb) || overlap2(workspace, l.bytes, w, wb) ||
+      overlap2(workspace, l.bytes, out, bytes))
+    return GLA_ERR_ALIAS;
+  if ((rc = rope_device_ok(rope))) return rc;
+  const Plan& p = l.p;
+  char* wsb = static_cast<char*>(workspace);
+  gla::PArgs pa{};
+  pa.x = static_cast<const uint16_t*>(x);
+  pa.w = static_cast<const uint16_t*>(w);
+  pa.Cdim = C;
+  pa.qbuf = reinterpret_cast<uint16_t*>(wsb + l.off_q);
+  pa.gbuf = reinterpret_cast<uint16_t*>(wsb + l.off_g);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // k, v -> state partials (chunks of the state plan); q, g -> workspace
+  const gla::KArgs akv = kernel_args(p, rope, p.L, p.CB, workspace);
+  const int tiles = (N + gla::kProjTileTokens - 1) / gla::kProjTileTokens;
+  const gla::KArgs aqg = kernel_args(p, nullptr, gla::kProjTileTokens, tiles, workspace);
+  if ((rc = status_of(gla::launch_proj(p, akv, aqg, pa, s)))) return rc;
+  if ((rc = status_of(gla::launch_reduce_state(p, akv, s)))) return rc;
+  return run_output(p, pa.qbuf, pa.gbuf, rope, out, workspace, stream);
+}
+
+int gla_forward_proj(const void* x, const void* w, const gla_rope_tables* rope, void* out, int B,
+                     int N, int C, int H, int D, void* stream) {
+  int rc = gla_forward_proj_check(x, w, rope, out, B, N, C, H, D);
+  if (rc) return rc;
+  const size_t need = gla_proj_workspace_bytes(B, N, C, H, D);
+  if (need == 0) return GLA_OK;
+  void* ws = nullptr;
+  if ((rc = get_workspace(need, stream, &ws))) return rc;
+  return gla_forward_proj_ws(x, w, rope, out, B, N, C, H, D, ws, need, stream);
+}
+
+}  // extern "C"

@@ -103,6 +103,21 @@ hipError_t launch_bwd_query(const Plan& p, KArgs a, BArgs b, hipStream_t stream)
 // a.sl2 (dS rows) and dzp; writes dk, dv.
 hipError_t launch_bwd_key(const Plan& p, KArgs a, BArgs b, hipStream_t stream);
 
+// Projection prologue (gla_project.hip): q, k, v, g = x W^T per map.
+struct PArgs {
+  const uint16_t* x;     // hidden states [B, N, C] bf16
+  const uint16_t* w;     // stacked weights [4][H * D][C] bf16 (q, k, v, g)
+  int Cdim;              // hidden size C (a multiple of 64)
+  uint16_t* qbuf;        // projected q [B, N, H, D] bf16 (written)
+  uint16_t* gbuf;        // projected g [B, N, H, D] bf16 (written)
+};
+// akv: the state plan's chunks (writes a.part, as the state kernel does);
+// aqg: token tiles of kProjTileTokens (one per range; writes qbuf, gbuf).
+hipError_t launch_proj(const Plan& p, KArgs akv, KArgs aqg, PArgs pa, hipStream_t stream);
+// The reduce kernel alone over the state partials in a.part.
+hipError_t launch_reduce_state(const Plan& p, KArgs a, hipStream_t stream);
+constexpr int kProjTileTokens = 128;
+
 // Tile sizes the plan has to respect.
 constexpr int kOutputTileTokens = 64;
 constexpr int kMaxChunks = 256;

@@ -964,6 +964,17 @@ void launch_reduce(const Plan& p, const KArgs& a, hipStream_t stream) {
 }
 
 
+template <int D>
+hipError_t launch_reduce_d(const Plan& p, const KArgs& a, hipStream_t stream) {
+  if (p.CB <= 8)
+    launch_reduce<D, 8>(p, a, stream);
+  else if (p.CB <= 16)
+    launch_reduce<D, 16>(p, a, stream);
+  else
+    launch_reduce<D, 32>(p, a, stream);
+  return hipGetLastError();
+}
+
 template <int D, bool ROPE, bool TLDS>
 hipError_t launch_state_k(const Plan& p, const KArgs& a, size_t lds, hipStream_t stream) {
   const dim3 g1(p.C, p.BH);
@@ -993,13 +1004,7 @@ hipError_t launch_state_d(const Plan& p, KArgs a, hipStream_t stream) {
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.CB <= 8)
-    launch_reduce<D, 8>(p, a, stream);
-  else if (p.CB <= 16)
-    launch_reduce<D, 16>(p, a, stream);
-  else
-    launch_reduce<D, 32>(p, a, stream);
-  return hipGetLastError();
+  return launch_reduce_d<D>(p, a, stream);
 }
 
 template <int D>
@@ -1023,6 +1028,15 @@ hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream) {
     case 32: return launch_state_d<32>(p, a, stream);
     case 64: return launch_state_d<64>(p, a, stream);
     case 128: return launch_state_d<128>(p, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_reduce_state(const Plan& p, KArgs a, hipStream_t stream) {
+  switch (p.D) {
+    case 32: return launch_reduce_d<32>(p, a, stream);
+    case 64: return launch_reduce_d<64>(p, a, stream);
+    case 128: return launch_reduce_d<128>(p, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

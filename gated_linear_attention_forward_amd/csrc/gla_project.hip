@@ -1,0 +1,389 @@
+// gla_project.hip -- gfx950 kernels of the projection prologue: q, k, v and
+// g as linear maps of the hidden states ("SANA-Video 2.0", NVlabs Sana docs,
+// section Architecture: hidden size 2,560 with 20 heads x 128 at 5B, 4,096
+// with 32 heads x 128 at 14B), fused with the mixer's state contraction so
+// that k and v never go to memory.
+//
+// x is bf16 [B, N, C]; the weights are bf16 [4][H*D][C] (maps q, k, v, g;
+// row j of a map is output feature j, contiguous over C).  Each map is
+// y = x W^T, rounded to bf16 as a BF16 model stores it.
+//
+// Both kernels run the same GEMM main loop on a tile of TM = 128 tokens of
+// one batch element and the 2 D output features of one head in two maps
+// (k and v, or q and g): 4 waves, wave (wm, wn) computes tokens
+// 64 wm .. + 64 of map wn on v_mfma_f32_32x32x16_bf16 (A = x rows, B = W
+// rows: both operands are contiguous over C).  Per K-step of 64 the x tile
+// (128 x 64) and the W tile (2 D x 64) go through registers into one of two
+// LDS stages while the other stage is multiplied.
+//
+//   kv kernel  one block per (state chunk, head), looping over the chunk's
+//              tiles; after each tile's GEMM: bf16(k) with ReLU and bf16(v)
+//              to feature-major LDS tiles, the rotation applied in place
+//              (each thread owns four tokens and every eighth pair) while z
+//              accumulates the unrotated features, then S += rk^T v over the
+//              tile's tokens on MFMA (each wave owns a quarter of S's 32x32
+//              tiles); at the end the block writes the same fp32 (S_c, z_c)
+//              partial the state kernel writes, for the same reduce kernel;
+//   qg kernel  one block per (token tile, head): q and g through a
+//              token-major LDS tile to 16-byte row stores.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gla_device.h"
+#include "gla_internal.h"
+
+namespace gla {
+namespace {
+
+template <int D>
+struct ProjCfg {
+  static constexpr int TM = kProjTileTokens;  // tokens per tile
+  static constexpr int KT = 64;               // K per stage
+  static constexpr int AP = KT * 2 + 16;      // stage row pitch (bytes)
+  static constexpr int A_BYTES = TM * AP;
+  static constexpr int B_BYTES = 2 * D * AP;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int MI = 2;                // 32-row subtiles per wave (64 tokens)
+  static constexpr int NI = D / 32;           // 32-column subtiles per wave (one map)
+  static constexpr int ACH = TM * (KT / 8) / 256;      // 16-byte x chunks per thread
+  static constexpr int BCH = 2 * D * (KT / 8) / 256;   // 16-byte W chunks per thread
+  // kv epilogue: feature-major tiles [D][TM] of R phi(k) and v
+  static constexpr int FP = TM * 2 + 16;
+  static constexpr int KV_BYTES = 2 * D * FP;
+  static constexpr int ST = (D / 32) * (D / 32);        // 32x32 tiles of S
+  static constexpr int STW = (ST + 3) / 4;              // per wave
+  // qg epilogue: token-major tile [TM][2 D]
+  static constexpr int QP = 4 * D + 16;
+  static constexpr int QG_BYTES = TM * QP;
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static_assert(KV_BYTES <= LDS_BYTES && QG_BYTES <= LDS_BYTES, "epilogue tiles fit the stages");
+  static_assert(ACH >= 1 && BCH >= 1, "one chunk per thread at least");
+};
+
+struct Gemm {
+  __amdgpu_buffer_rsrc_t rx, rw;
+  uint32_t x_row;      // bytes per x row (C * 2)
+  int n_tile_end;      // tokens at or past this one load zeros
+  int wrow[2];         // first W row of the two maps' head slices
+};
+
+// The main loop: acc[mi][ni] += x[tile rows] W[cols]^T over the whole of C.
+template <int D>
+__device__ __forceinline__ void gemm_tile(const Gemm& gm, int tile0, int Cdim, unsigned char* smem,
+                                          f32x16 (&acc)[2][D / 32]) {
+  using Cf = ProjCfg<D>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+  for (int mi = 0; mi < Cf::MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < Cf::NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  u32x4 ra[Cf::ACH], rb[Cf::BCH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < Cf::ACH; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, col = c & 7;
+      const int n = tile0 + row;
+      const uint32_t off = n < gm.n_tile_end
+                               ? (uint32_t)n * gm.x_row + (uint32_t)(k0 + 8 * col) * 2u
+                               : kOob;
+      ra[i] = load16(gm.rx, off);
+    }
+#pragma unroll
+    for (int i = 0; i < Cf::BCH; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, col = c & 7;
+      const int wr = gm.wrow[row / D] + row % D;
+      rb[i] = load16(gm.rw, (uint32_t)wr * gm.x_row + (uint32_t)(k0 + 8 * col) * 2u);
+    }
+  };
+  auto lwrite = [&](unsigned char* st) {
+#pragma unroll
+    for (int i = 0; i < Cf::ACH; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(st + (c >> 3) * Cf::AP + 16 * (c & 7)) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Cf::BCH; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(st + Cf::A_BYTES + (c >> 3) * Cf::AP + 16 * (c & 7)) = rb[i];
+    }
+  };
+  const int nk = Cdim / Cf::KT;
+  gload(0);
+  lwrite(smem);
+  __syncthreads();
+  const int arow = 64 * wm + (lane & 31), brow = D * wn + (lane & 31);
+  const int kb = 16 * (lane >> 5);  // byte offset of the lane's 8 k values in a 16-wide step
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload((kt + 1) * Cf::KT);
+    const unsigned char* st = smem + (kt & 1) * Cf::STAGE;
+#pragma unroll
+    for (int ks = 0; ks < Cf::KT / 16; ++ks) {
+      bf16x8 A[Cf::MI], Bm[Cf::NI];
+#pragma unroll
+      for (int mi = 0; mi < Cf::MI; ++mi)
+        A[mi] = *reinterpret_cast<const bf16x8*>(st + (arow + 32 * mi) * Cf::AP + 32 * ks + kb);
+#pragma unroll
+      for (int ni = 0; ni < Cf::NI; ++ni)
+        Bm[ni] = *reinterpret_cast<const bf16x8*>(st + Cf::A_BYTES + (brow + 32 * ni) * Cf::AP +
+                                                  32 * ks + kb);
+#pragma unroll
+      for (int mi = 0; mi < Cf::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < Cf::NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mi], Bm[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lwrite(smem + ((kt + 1) & 1) * Cf::STAGE);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kv kernel
+template <int D, bool ROPE, bool TLDS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void proj_kv_kernel(KArgs a, PArgs pa) {
+  using Cf = ProjCfg<D>;
+  constexpr int TM = Cf::TM, FP = Cf::FP, NPG = D / 16;  // pairs per thread
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float2* ltab = reinterpret_cast<float2*>(smem + Cf::LDS_BYTES);
+  unsigned char* ktile = smem;
+  unsigned char* vtile = smem + D * FP;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  int n_begin, n_end;
+  range_of(a, c, n_begin, n_end);
+  TabView tv{};
+  if (ROPE) tv = stage_table<D>(a, ltab, TLDS, n_begin, n_end);
+  __syncthreads();
+
+  const int HD = a.H * D;
+  Gemm gm;
+  gm.rx = make_rsrc(pa.x + (size_t)b * a.N * pa.Cdim, (uint32_t)((size_t)a.N * pa.Cdim * 2));
+  gm.rw = make_rsrc(pa.w, (uint32_t)((size_t)4 * HD * pa.Cdim * 2));
+  gm.x_row = (uint32_t)pa.Cdim * 2u;
+  gm.n_tile_end = n_end;
+  gm.wrow[0] = 1 * HD + h * D;  // k
+  gm.wrow[1] = 2 * HD + h * D;  // v
+
+  f32x16 accS[Cf::STW];
+#pragma unroll
+  for (int u = 0; u < Cf::STW; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accS[u][r] = 0.f;
+  float zacc[NPG][2];
+#pragma unroll
+  for (int i = 0; i < NPG; ++i) zacc[i][0] = zacc[i][1] = 0.f;
+  const int tq = tid & 31, pg = tid >> 5;
+
+  for (int tile0 = n_begin; tile0 < n_end; tile0 += TM) {
+    f32x16 acc[2][D / 32];
+    gemm_tile<D>(gm, tile0, pa.Cdim, smem, acc);
+    // bf16 phi(k) and bf16 v, feature-major: lane column = feature, four
+    // consecutive tokens per accumulator quarter
+    unsigned char* dst = wn ? vtile : ktile;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < D / 32; ++ni)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int f = 32 * ni + (lane & 31);
+          const int t = 64 * wm + 32 * mi + 8 * rg + 4 * (lane >> 5);
+          float y[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float val = acc[mi][ni][4 * rg + j];
+            y[j] = wn ? val : fmaxf(val, 0.f);
+          }
+          typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<u32x2v*>(dst + f * FP + 2 * t) =
+              u32x2v{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+        }
+    __syncthreads();
+    // z and the rotation: thread (tq, pg) owns tokens 4 tq .. + 3 and pairs
+    // pg, pg + 8, ...
+    {
+      RowOff ro[4];
+      if (ROPE) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int t, y, x;
+          grid_pos(a, (uint32_t)min(tile0 + 4 * tq + j, n_end - 1), t, y, x);
+          ro[j] = row_offsets<D>(a, tv, t, y, x);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NPG; ++i) {
+        const int p = pg + 8 * i;
+        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+        u32x2v* r0 = reinterpret_cast<u32x2v*>(ktile + (2 * p) * FP + 8 * tq);
+        u32x2v* r1 = reinterpret_cast<u32x2v*>(ktile + (2 * p + 1) * FP + 8 * tq);
+        const u32x2v w0 = *r0, w1 = *r1;
+        float e0[4] = {bf_lo(w0[0]), bf_hi(w0[0]), bf_lo(w0[1]), bf_hi(w0[1])};
+        float e1[4] = {bf_lo(w1[0]), bf_hi(w1[0]), bf_lo(w1[1]), bf_hi(w1[1])};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          zacc[i][0] += e0[j];
+          zacc[i][1] += e1[j];
+        }
+        if (ROPE) {
+          float o0[4], o1[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float2 f = rope_factor<D, 0, D / 2 - 1>(tv, ro[j], p);
+            o0[j] = e0[j] * f.x - e1[j] * f.y;
+            o1[j] = e0[j] * f.y + e1[j] * f.x;
+          }
+          *r0 = u32x2v{pack_bf16(o0[0], o0[1]), pack_bf16(o0[2], o0[3])};
+          *r1 = u32x2v{pack_bf16(o1[0], o1[1]), pack_bf16(o1[2], o1[3])};
+        }
+      }
+    }
+    __syncthreads();
+    // S += rk^T v over the tile's tokens (k-steps of 16 tokens)
+#pragma unroll
+    for (int u = 0; u < Cf::STW; ++u) {
+      const int q = wave + 4 * u;
+      if (q < Cf::ST) {
+        const int ti = q / (D / 32), tj = q % (D / 32);
+        const unsigned char* ar = ktile + (32 * ti + (lane & 31)) * FP + 16 * (lane >> 5);
+        const unsigned char* br = vtile + (32 * tj + (lane & 31)) * FP + 16 * (lane >> 5);
+#pragma unroll
+        for (int ks = 0; ks < TM / 16; ++ks) {
+          const bf16x8 A = *reinterpret_cast<const bf16x8*>(ar + 32 * ks);
+          const bf16x8 Bv = *reinterpret_cast<const bf16x8*>(br + 32 * ks);
+          accS[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bv, accS[u], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // the tiles are the next GEMM's stages
+  }
+
+  float* dstp = a.part + ((size_t)bh * a.C + c) * (size_t)(D * D + D);
+#pragma unroll
+  for (int u = 0; u < Cf::STW; ++u) {
+    const int q = wave + 4 * u;
+    if (q < Cf::ST) {
+      const int ti = q / (D / 32), tj = q % (D / 32);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * ti + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int e = 32 * tj + (lane & 31);
+        dstp[d * D + e] = accS[u][r];
+      }
+    }
+  }
+  // z: the 32 threads of a pair group hold the same features
+#pragma unroll
+  for (int i = 0; i < NPG; ++i)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float s = zacc[i][hf];
+#pragma unroll
+      for (int msk = 1; msk < 32; msk *= 2) s += __shfl_xor(s, msk);
+      if (tq == 0) dstp[D * D + 2 * (pg + 8 * i) + hf] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// qg kernel
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void proj_qg_kernel(KArgs a, PArgs pa) {
+  using Cf = ProjCfg<D>;
+  constexpr int TM = Cf::TM, QP = Cf::QP;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  int n_begin, n_end;
+  range_of(a, blockIdx.y, n_begin, n_end);
+
+  const int HD = a.H * D;
+  Gemm gm;
+  gm.rx = make_rsrc(pa.x + (size_t)b * a.N * pa.Cdim, (uint32_t)((size_t)a.N * pa.Cdim * 2));
+  gm.rw = make_rsrc(pa.w, (uint32_t)((size_t)4 * HD * pa.Cdim * 2));
+  gm.x_row = (uint32_t)pa.Cdim * 2u;
+  gm.n_tile_end = n_end;
+  gm.wrow[0] = 0 * HD + h * D;  // q
+  gm.wrow[1] = 3 * HD + h * D;  // g
+
+  f32x16 acc[2][D / 32];
+  gemm_tile<D>(gm, n_begin, pa.Cdim, smem, acc);
+  // token-major tile: row t holds q (D bf16) then g (D bf16)
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < D / 32; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 64 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int f = D * wn + 32 * ni + (lane & 31);
+        const __bf16 y = (__bf16)acc[mi][ni][r];
+        *reinterpret_cast<__bf16*>(smem + t * QP + 2 * f) = y;
+      }
+  __syncthreads();
+  const size_t boff = (size_t)b * a.N * a.H * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(pa.qbuf + boff, a.slab_bytes);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(pa.gbuf + boff, a.slab_bytes);
+  const uint32_t tokstride = (uint32_t)a.H * D * 2;
+  constexpr int CPR = D / 8;  // 16-byte chunks per map row
+  for (int cidx = tid; cidx < TM * 2 * CPR; cidx += 256) {
+    const int t = cidx / (2 * CPR), part = (cidx / CPR) & 1, u = cidx % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + t * QP + 2 * (part * D + 8 * u));
+    const int n = n_begin + t;
+    const uint32_t off =
+        n < n_end ? (uint32_t)n * tokstride + (uint32_t)h * D * 2 + 16u * u : kOob;
+    __builtin_amdgcn_raw_buffer_store_b128(v, part ? rg : rq, off, 0, 0);
+  }
+}
+
+template <int D>
+hipError_t launch_proj_d(const Plan& p, const KArgs& akv, const KArgs& aqg, const PArgs& pa,
+                         hipStream_t s) {
+  using Cf = ProjCfg<D>;
+  // k, v and the state partials
+  const bool tl = akv.cs && table_lds_bytes(akv) <= kMaxLdsTableBytes;
+  const size_t lds = Cf::LDS_BYTES + (tl ? table_lds_bytes(akv) : 0);
+  const dim3 g1(p.C, p.BH);
+  hipError_t e;
+  if (!akv.cs) {
+    if ((e = allow_lds<proj_kv_kernel<D, false, false>>(lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((proj_kv_kernel<D, false, false>), g1, dim3(256), lds, s, akv, pa);
+  } else if (tl) {
+    if ((e = allow_lds<proj_kv_kernel<D, true, true>>(lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((proj_kv_kernel<D, true, true>), g1, dim3(256), lds, s, akv, pa);
+  } else {
+    if ((e = allow_lds<proj_kv_kernel<D, true, false>>(lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((proj_kv_kernel<D, true, false>), g1, dim3(256), lds, s, akv, pa);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // q and g
+  if ((e = allow_lds<proj_qg_kernel<D>>(Cf::LDS_BYTES)) != hipSuccess) return e;
+  const dim3 g2(p.BH, aqg.CB);
+  hipLaunchKernelGGL((proj_qg_kernel<D>), g2, dim3(256), Cf::LDS_BYTES, s, aqg, pa);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_proj(const Plan& p, KArgs akv, KArgs aqg, PArgs pa, hipStream_t stream) {
+  switch (p.D) {
+    case 32: return launch_proj_d<32>(p, akv, aqg, pa, stream);
+    case 64: return launch_proj_d<64>(p, akv, aqg, pa, stream);
+    case 128: return launch_proj_d<128>(p, akv, aqg, pa, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gla

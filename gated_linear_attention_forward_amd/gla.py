@@ -35,6 +35,8 @@ EXPORTS = (
     "gla_forward_blocks_check", "gla_softmax_forward", "gla_softmax_forward_ws",
     "gla_softmax_workspace_bytes", "gla_softmax_forward_check", "gla_backward",
     "gla_backward_ws", "gla_backward_workspace_bytes", "gla_backward_check",
+    "gla_forward_proj", "gla_forward_proj_ws", "gla_proj_workspace_bytes",
+    "gla_forward_proj_check",
 )
 
 
@@ -96,6 +98,10 @@ def load_library():
         "gla_backward_ws": ([vp] * 5 + [rp] + [vp] * 4 + [i32] * 4 + [vp, sz, vp], i32),
         "gla_backward_workspace_bytes": ([i32] * 4, sz),
         "gla_backward_check": ([vp] * 5 + [rp] + [vp] * 4 + [i32] * 4, i32),
+        "gla_forward_proj": ([vp, vp, rp, vp] + [i32] * 5 + [vp], i32),
+        "gla_forward_proj_ws": ([vp, vp, rp, vp] + [i32] * 5 + [vp, sz, vp], i32),
+        "gla_proj_workspace_bytes": ([i32] * 5, sz),
+        "gla_forward_proj_check": ([vp, vp, rp, vp] + [i32] * 5, i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -498,3 +504,65 @@ def gla_backward_ws(q, k, v, g, dout, rope, ws: torch.Tensor, dq=None, dk=None, 
                                            _stream_handle(stream, q.device)),
             "gla_backward_ws")
     return tuple(grads)
+
+
+# ---------------------------------------------------------------------------
+# projection prologue fused with the mixer
+
+
+def gla_proj_workspace_bytes(B: int, N: int, C: int, H: int, D: int) -> int:
+    return load_library().gla_proj_workspace_bytes(B, N, C, H, D)
+
+
+def alloc_workspace_proj(B, N, C, H, D, device=None) -> torch.Tensor:
+    """A torch-owned uint8 device buffer large enough for gla_forward_proj_ws."""
+    return torch.empty(max(gla_proj_workspace_bytes(B, N, C, H, D), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def gla_forward_proj_check(x, w, rope, out, B, N, C, H, D) -> int:
+    """Status of the library's argument validation (pointers as integers)."""
+    return load_library().gla_forward_proj_check(x, w, _rope_ptr(rope), out, B, N, C, H, D)
+
+
+def _proj_args(x, w, out):
+    for name, t, nd in (("x", x, 3), ("w", w, 3)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 tensor")
+        if t.dim() != nd or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a contiguous {nd}-d GPU tensor")
+    B, N, C = x.shape
+    if w.shape[0] != 4 or w.shape[2] != C or w.device != x.device:
+        raise ValueError(f"w must be [4, H*D, {C}] on {x.device}, got {tuple(w.shape)}")
+    return B, N, C
+
+
+def gla_forward_proj(x, w, H: int, D: int, rope=None, out=None, stream=None) -> torch.Tensor:
+    """The mixer on q, k, v, g = bf16(x W^T) per map; x [B, N, C], w [4, H*D, C];
+    returns bf16 [B, N, H, D]."""
+    B, N, C = _proj_args(x, w, out)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check_bf16("out", out, (B, N, H, D))
+    with torch.cuda.device(x.device):
+        _ok(load_library().gla_forward_proj(x.data_ptr(), w.data_ptr(), _rope_ptr(rope),
+                                            out.data_ptr(), B, N, C, H, D,
+                                            _stream_handle(stream, x.device)),
+            "gla_forward_proj")
+    return out
+
+
+def gla_forward_proj_ws(x, w, H: int, D: int, rope, ws: torch.Tensor, out=None, stream=None):
+    B, N, C = _proj_args(x, w, out)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check_bf16("out", out, (B, N, H, D))
+    with torch.cuda.device(x.device):
+        _ok(load_library().gla_forward_proj_ws(x.data_ptr(), w.data_ptr(), _rope_ptr(rope),
+                                               out.data_ptr(), B, N, C, H, D, ws.data_ptr(),
+                                               ws.numel() * ws.element_size(),
+                                               _stream_handle(stream, x.device)),
+            "gla_forward_proj_ws")
+    return out

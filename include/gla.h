@@ -296,6 +296,45 @@ int gla_backward_check(const void* q, const void* k, const void* v, const void* 
                        const void* dk, const void* dv, const void* dg, int B, int N, int H,
                        int D);
 
+/* ---------------------------------------------------------------------
+ * Projection prologue fused with the mixer.
+ *
+ * The step before the mixer in a linear layer ("SANA-Video 2.0", NVlabs
+ * Sana docs, section Architecture: hidden size 2,560 with 20 heads x 128 at
+ * 5B, 4,096 with 32 heads x 128 at 14B; section Model zoo: BF16 inference).
+ * The pages give no further detail of the projections; read as four
+ * bias-free linear maps of the hidden states, each stored in bf16:
+ *
+ *     q = bf16(x Wq^T),  k = bf16(x Wk^T),  v = bf16(x Wv^T),  g = bf16(x Wg^T)
+ *
+ * followed by gla_forward on (q, k, v, g).  x: device bf16 [B, N, C]
+ * (C = hidden size, a multiple of 64); w: device bf16 [4][H*D][C], the four
+ * maps stacked in the order q, k, v, g, row j of a map being output feature
+ * j (h*D + d) contiguous over C (the [out, in] layout of a linear layer);
+ * out: device bf16 [B, N, H, D], overlapping neither x nor w; all 16-byte
+ * aligned.  D must be 32, 64 or 128; rope as for gla_forward.  The GEMMs
+ * run on bf16 MFMA with fp32 accumulation; k and v never reach device
+ * memory (the state is contracted from them in the GEMM's epilogue), q and
+ * g go through the workspace.  Limits: N*C*2 and 4*H*D*C*2 below 2 GiB.
+ * Uses a library-owned workspace (grown with hipMalloc, which may
+ * synchronise).  B*N*H == 0 is a no-op.  Results are bitwise reproducible. */
+int gla_forward_proj(const void* x, const void* w, const gla_rope_tables* rope, void* out, int B,
+                     int N, int C, int H, int D, void* stream);
+
+/* Workspace bytes gla_forward_proj_ws needs (the state partials and operand
+ * and the projected q and g), 0 for bad shapes or B*N*H == 0. */
+size_t gla_proj_workspace_bytes(int B, int N, int C, int H, int D);
+
+/* gla_forward_proj with a caller-owned device workspace (>= the size above,
+ * 256-byte aligned, overlapping no tensor).  Never allocates. */
+int gla_forward_proj_ws(const void* x, const void* w, const gla_rope_tables* rope, void* out,
+                        int B, int N, int C, int H, int D, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Argument validation of gla_forward_proj alone (no HIP call). */
+int gla_forward_proj_check(const void* x, const void* w, const gla_rope_tables* rope,
+                           const void* out, int B, int N, int C, int H, int D);
+
 #ifdef __cplusplus
 }
 #endif

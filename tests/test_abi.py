@@ -281,3 +281,38 @@ def test_backward_workspace_size():
         assert ws % 256 == 0
     assert gla.gla_backward_workspace_bytes(1, 0, 2, 128) == 0
     assert gla.gla_backward_workspace_bytes(1, 10, 1, 48) == 0
+
+
+# ---------------------------------------------------------------------------
+# projection prologue: validation without a GPU
+
+
+def pcheck(**kw):
+    args = dict(x=A, w=8 * A, rope=None, out=16 * A, B=1, N=64, C=256, H=2, D=128)
+    args.update(kw)
+    return gla.gla_forward_proj_check(*(args[n] for n in ("x", "w", "rope", "out", "B", "N", "C",
+                                                          "H", "D")))
+
+
+def test_proj_validation():
+    assert pcheck() == 0 and pcheck(D=32) == 0 and pcheck(D=64, C=64) == 0
+    for C in (0, 32, 100, 2561):
+        assert pcheck(C=C) == glamod.GLA_ERR_DIM
+    assert pcheck(D=48) == glamod.GLA_ERR_DIM
+    assert pcheck(x=0) == glamod.GLA_ERR_NULL and pcheck(w=0) == glamod.GLA_ERR_NULL
+    assert pcheck(out=16 * A + 4) == glamod.GLA_ERR_ALIGN
+    assert pcheck(out=A) == glamod.GLA_ERR_ALIAS                 # out is x
+    assert pcheck(out=8 * A + 4 * 2 * 128 * 256 * 2 - 16) == glamod.GLA_ERR_ALIAS  # w's end
+    assert pcheck(N=0) == 0
+    assert pcheck(N=64, rope=_host_rope(4, 4, 4, 128)) == 0
+    assert pcheck(N=64, rope=_host_rope(4, 4, 5, 128)) == glamod.GLA_ERR_ROPE
+    # x slab beyond 2 GiB of 32-bit offsets
+    assert pcheck(N=1 << 20, C=1024) == glamod.GLA_ERR_DIM
+
+
+def test_proj_workspace_size():
+    ws = gla.gla_proj_workspace_bytes(2, 22000, 2560, 20, 128)
+    assert ws >= gla.gla_workspace_bytes(2, 22000, 20, 128) + 2 * (2 * 22000 * 20 * 128 * 2)
+    assert ws % 256 == 0
+    assert gla.gla_proj_workspace_bytes(1, 0, 256, 2, 128) == 0
+    assert gla.gla_proj_workspace_bytes(1, 10, 100, 2, 128) == 0
