@@ -18,7 +18,8 @@ the kernel source differs from the one those counters were taken on.
 
 `--block-frames F` times the block-causal form instead, `--softmax` the
 gated softmax anchor attention (an MFMA-bound roofline in TFLOP/s) and
-`--backward` the mixer's backward pass.
+`--backward` the mixer's backward pass and `--proj` the projection prologue
+fused with the mixer (an MFMA-bound roofline in TFLOP/s).
 """
 from __future__ import annotations
 
@@ -359,6 +360,101 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
     print(json.dumps(result), flush=True)
 
 
+def proj_cpu_baseline(w, x, wt, min_seconds=10.0):
+    """Times the oracle's projections + mixer on single heads of batch
+    element 0 (the projections parallel over tokens) until about
+    `min_seconds` of CPU work, and scales the per-head time to every head."""
+    import oracle
+    grid = oracle.Grid(w.T, w.Hh, w.W, w.theta)
+    xs = x[:1].contiguous()
+    heads = 0
+    t0 = time.perf_counter()
+    while True:
+        t = oracle.projected_heads(xs, wt, w.H, w.D, [heads % w.H])
+        oracle.forward(t["q"], t["k"], t["v"], t["g"], grid)
+        heads += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    per_head = dt / heads
+    return {
+        "value": (w.B * w.N) / (per_head * w.B * w.H),
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{heads} heads of batch 0 (all N={w.N} tokens, C={w.C}) in {dt:.1f} s; "
+                  f"{per_head:.2f} s per head, scaled to {w.B * w.H} heads",
+    }
+
+
+def proj_bench(args, w, gla, dev):
+    """Projection prologue fused with the mixer: K passes of
+    gla_forward_proj_ws.  MFMA-bound: 2*C*4*H*D flops per token for the
+    four maps plus 4*D*D per (token, head) for the state and output
+    contractions, against the dense bf16 peak, over the call's event time."""
+    import torch
+
+    from workloads import make_projection
+    log(f"bench: projection workload {w.name} B={w.B} N={w.N} C={w.C} H={w.H} D={w.D}")
+    x, wt = make_projection(w)
+    xd, wd = x.to(dev), wt.to(dev)
+    rope = gla.gla_rope_create(w.T, w.Hh, w.W, w.D, w.theta)
+    stream = torch.cuda.current_stream(dev)
+    out = torch.empty((w.B, w.N, w.H, w.D), dtype=torch.bfloat16, device=dev)
+    ws = gla.alloc_workspace_proj(w.B, w.N, w.C, w.H, w.D, dev)
+
+    def step():
+        gla.gla_forward_proj_ws(xd, wd, w.H, w.D, rope, ws, out, stream)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    log(f"bench: {args.steps} instrumented steps")
+    for e in evs:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ev_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    tokens = w.B * w.N
+    flops = 2.0 * tokens * w.C * 4 * w.H * w.D + 4.0 * tokens * w.H * w.D * w.D
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    result = {
+        "metric": "projected gated linear-attn layer tokens/s (x -> q,k,v,g -> mixer); "
+                  "achieved bf16 MFMA TFLOP/s vs peak",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "C": w.C, "H": w.H, "D": w.D,
+                   "grid": [w.T, w.Hh, w.W], "parallelism": "single-gpu"},
+        "roofline": {"kernel": "whole layer (kv and qg projection kernels, reduce, output)",
+                     "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "algorithmic_flops": flops, "avg_ms": ev_ms},
+    }
+    rope.close()
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle (cpu_baseline)")
+        result["cpu_baseline"] = proj_cpu_baseline(w, x, wt)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -377,7 +473,12 @@ def main():
                          "instead; the workload defaults to anchor_5b_720p_193f")
     ap.add_argument("--backward", action="store_true",
                     help="time the mixer's backward pass (gla_backward) instead")
+    ap.add_argument("--proj", action="store_true",
+                    help="time the projection prologue fused with the mixer (gla_forward_proj); "
+                         "the workload defaults to proj_5b_720p_193f")
     args = ap.parse_args()
+    if args.proj and args.workload == DEFAULT_WORKLOAD:
+        args.workload = "proj_5b_720p_193f"
     if args.softmax and args.workload == DEFAULT_WORKLOAD:
         args.workload = "anchor_5b_720p_193f"
 
@@ -394,6 +495,9 @@ def main():
     w = BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.proj:
+        proj_bench(args, w, gla, dev)
+        return
     log(f"bench: workload {w.name} B={w.B} N={w.N} H={w.H} D={w.D}; generating inputs")
     q, k, v, g = make_inputs(w)
     qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))

@@ -10,19 +10,21 @@
 //
 // Both kernels run the same GEMM main loop on a tile of TM = 128 tokens of
 // one batch element and the 2 D output features of one head in two maps
-// (k and v, or q and g): 4 waves, wave (wm, wn) computes tokens
-// 64 wm .. + 64 of map wn on v_mfma_f32_32x32x16_bf16 (A = x rows, B = W
-// rows: both operands are contiguous over C).  Per K-step of 64 the x tile
-// (128 x 64) and the W tile (2 D x 64) go through registers into one of two
-// LDS stages while the other stage is multiplied.
+// (k and v, or q and g) on v_mfma_f32_32x32x16_bf16 (A = x rows, B = W rows:
+// both operands are contiguous over C).  At D >= 64 a block has 8 waves, two
+// per SIMD, each computing 64 tokens x 2D/4 features (64 accumulation
+// registers, so the state accumulators of the kv kernel fit beside them);
+// at D = 32, 4 waves of 64 x 32.  Per K-step of 64 the x tile (128 x 64) and
+// the W tile (2 D x 64) go through registers into one of two LDS stages
+// while the other stage is multiplied.
 //
 //   kv kernel  one block per (state chunk, head), looping over the chunk's
 //              tiles; after each tile's GEMM: bf16(k) with ReLU and bf16(v)
 //              to feature-major LDS tiles, the rotation applied in place
-//              (each thread owns four tokens and every eighth pair) while z
+//              (each thread owns four tokens and every sixteenth pair) while z
 //              accumulates the unrotated features, then S += rk^T v over the
-//              tile's tokens on MFMA (each wave owns a quarter of S's 32x32
-//              tiles); at the end the block writes the same fp32 (S_c, z_c)
+//              tile's tokens on MFMA (each wave owns an eighth of S's 32x32
+//              tiles at D = 128); at the end the block writes the same fp32 (S_c, z_c)
 //              partial the state kernel writes, for the same reduce kernel;
 //   qg kernel  one block per (token tile, head): q and g through a
 //              token-major LDS tile to 16-byte row stores.
@@ -43,34 +45,43 @@ struct ProjCfg {
   static constexpr int A_BYTES = TM * AP;
   static constexpr int B_BYTES = 2 * D * AP;
   static constexpr int STAGE = A_BYTES + B_BYTES;
+  // 8 waves (two per SIMD) where a wave still gets 32 columns, else 4
+  static constexpr int NW = D >= 64 ? 8 : 4;
+  static constexpr int NT = 64 * NW;
+  static constexpr int WN = NW / 2;           // column groups (two row groups of 64 tokens)
+  static constexpr int WC = 2 * D / WN;       // columns per wave
   static constexpr int MI = 2;                // 32-row subtiles per wave (64 tokens)
-  static constexpr int NI = D / 32;           // 32-column subtiles per wave (one map)
-  static constexpr int ACH = TM * (KT / 8) / 256;      // 16-byte x chunks per thread
-  static constexpr int BCH = 2 * D * (KT / 8) / 256;   // 16-byte W chunks per thread
+  static constexpr int NI = WC / 32;          // 32-column subtiles per wave
+  static constexpr int ACH = TM * (KT / 8) / NT;       // 16-byte x chunks per thread
+  static constexpr int BCH = 2 * D * (KT / 8) / NT;    // 16-byte W chunks per thread
   // kv epilogue: feature-major tiles [D][TM] of R phi(k) and v
   static constexpr int FP = TM * 2 + 16;
   static constexpr int KV_BYTES = 2 * D * FP;
   static constexpr int ST = (D / 32) * (D / 32);        // 32x32 tiles of S
-  static constexpr int STW = (ST + 3) / 4;              // per wave
+  static constexpr int STW = (ST + NW - 1) / NW;        // per wave
+  static constexpr int PGS = NT / 32;                   // pair groups of the rotation pass
   // qg epilogue: token-major tile [TM][2 D]
   static constexpr int QP = 4 * D + 16;
   static constexpr int QG_BYTES = TM * QP;
   static constexpr int LDS_BYTES = 2 * STAGE;
   static_assert(KV_BYTES <= LDS_BYTES && QG_BYTES <= LDS_BYTES, "epilogue tiles fit the stages");
-  static_assert(ACH >= 1 && BCH >= 1, "one chunk per thread at least");
+  static_assert(ACH >= 1 && BCH >= 1 && NI >= 1, "one chunk per thread, a 32-column subtile");
+  static_assert(D / 2 % PGS == 0, "pairs split evenly over the pair groups");
 };
 
 struct Gemm {
   __amdgpu_buffer_rsrc_t rx, rw;
   uint32_t x_row;      // bytes per x row (C * 2)
   int n_tile_end;      // tokens at or past this one load zeros
-  int wrow[2];         // first W row of the two maps' head slices
+  int wrow0, wrow1;    // first W row of the two maps' head slices
 };
 
 // The main loop: acc[mi][ni] += x[tile rows] W[cols]^T over the whole of C.
+// Wave (wm, wn) computes tokens 64 wm .. + 64 and columns WC wn .. + WC of
+// the tile's 2 D columns (the first D are map 0, the rest map 1).
 template <int D>
 __device__ __forceinline__ void gemm_tile(const Gemm& gm, int tile0, int Cdim, unsigned char* smem,
-                                          f32x16 (&acc)[2][D / 32]) {
+                                          f32x16 (&acc)[2][ProjCfg<D>::NI]) {
   using Cf = ProjCfg<D>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -85,7 +96,7 @@ __device__ __forceinline__ void gemm_tile(const Gemm& gm, int tile0, int Cdim, u
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < Cf::ACH; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = c & 7;
+      const int c = tid + Cf::NT * i, row = c >> 3, col = c & 7;
       const int n = tile0 + row;
       const uint32_t off = n < gm.n_tile_end
                                ? (uint32_t)n * gm.x_row + (uint32_t)(k0 + 8 * col) * 2u
@@ -94,20 +105,20 @@ __device__ __forceinline__ void gemm_tile(const Gemm& gm, int tile0, int Cdim, u
     }
 #pragma unroll
     for (int i = 0; i < Cf::BCH; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = c & 7;
-      const int wr = gm.wrow[row / D] + row % D;
+      const int c = tid + Cf::NT * i, row = c >> 3, col = c & 7;
+      const int wr = (row < D ? gm.wrow0 : gm.wrow1 - D) + row;
       rb[i] = load16(gm.rw, (uint32_t)wr * gm.x_row + (uint32_t)(k0 + 8 * col) * 2u);
     }
   };
   auto lwrite = [&](unsigned char* st) {
 #pragma unroll
     for (int i = 0; i < Cf::ACH; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + Cf::NT * i;
       *reinterpret_cast<u32x4*>(st + (c >> 3) * Cf::AP + 16 * (c & 7)) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < Cf::BCH; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + Cf::NT * i;
       *reinterpret_cast<u32x4*>(st + Cf::A_BYTES + (c >> 3) * Cf::AP + 16 * (c & 7)) = rb[i];
     }
   };
@@ -115,7 +126,7 @@ __device__ __forceinline__ void gemm_tile(const Gemm& gm, int tile0, int Cdim, u
   gload(0);
   lwrite(smem);
   __syncthreads();
-  const int arow = 64 * wm + (lane & 31), brow = D * wn + (lane & 31);
+  const int arow = 64 * wm + (lane & 31), brow = Cf::WC * wn + (lane & 31);
   const int kb = 16 * (lane >> 5);  // byte offset of the lane's 8 k values in a 16-wide step
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) gload((kt + 1) * Cf::KT);
@@ -144,10 +155,11 @@ __device__ __forceinline__ void gemm_tile(const Gemm& gm, int tile0, int Cdim, u
 // ---------------------------------------------------------------------------
 // kv kernel
 template <int D, bool ROPE, bool TLDS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * ProjCfg<D>::NW)
+__attribute__((amdgpu_waves_per_eu(ProjCfg<D>::NW / 4, ProjCfg<D>::NW / 4)))
 void proj_kv_kernel(KArgs a, PArgs pa) {
   using Cf = ProjCfg<D>;
-  constexpr int TM = Cf::TM, FP = Cf::FP, NPG = D / 16;  // pairs per thread
+  constexpr int TM = Cf::TM, FP = Cf::FP, PGS = Cf::PGS, NPG = D / 2 / PGS;  // pairs per thread
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float2* ltab = reinterpret_cast<float2*>(smem + Cf::LDS_BYTES);
   unsigned char* ktile = smem;
@@ -156,12 +168,14 @@ void proj_kv_kernel(KArgs a, PArgs pa) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int c = blockIdx.x, bh = blockIdx.y;
+  // heads vary fastest: with B*H a multiple of the 8 XCDs, each XCD's L2
+  // serves a fixed handful of heads' weight slices
+  const int bh = blockIdx.x, c = blockIdx.y;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
   int n_begin, n_end;
   range_of(a, c, n_begin, n_end);
   TabView tv{};
-  if (ROPE) tv = stage_table<D>(a, ltab, TLDS, n_begin, n_end);
+  if (ROPE) tv = stage_table<D, Cf::NT>(a, ltab, TLDS, n_begin, n_end);
   __syncthreads();
 
   const int HD = a.H * D;
@@ -170,8 +184,8 @@ void proj_kv_kernel(KArgs a, PArgs pa) {
   gm.rw = make_rsrc(pa.w, (uint32_t)((size_t)4 * HD * pa.Cdim * 2));
   gm.x_row = (uint32_t)pa.Cdim * 2u;
   gm.n_tile_end = n_end;
-  gm.wrow[0] = 1 * HD + h * D;  // k
-  gm.wrow[1] = 2 * HD + h * D;  // v
+  gm.wrow0 = 1 * HD + h * D;  // k
+  gm.wrow1 = 2 * HD + h * D;  // v
 
   f32x16 accS[Cf::STW];
 #pragma unroll
@@ -182,26 +196,28 @@ void proj_kv_kernel(KArgs a, PArgs pa) {
 #pragma unroll
   for (int i = 0; i < NPG; ++i) zacc[i][0] = zacc[i][1] = 0.f;
   const int tq = tid & 31, pg = tid >> 5;
+  // this wave's columns: map (0: k, 1: v) and first feature
+  const int wmap = (Cf::WC * wn) / D, wf0 = (Cf::WC * wn) % D;
 
   for (int tile0 = n_begin; tile0 < n_end; tile0 += TM) {
-    f32x16 acc[2][D / 32];
+    f32x16 acc[2][Cf::NI];
     gemm_tile<D>(gm, tile0, pa.Cdim, smem, acc);
     // bf16 phi(k) and bf16 v, feature-major: lane column = feature, four
     // consecutive tokens per accumulator quarter
-    unsigned char* dst = wn ? vtile : ktile;
+    unsigned char* dst = wmap ? vtile : ktile;
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < D / 32; ++ni)
+      for (int ni = 0; ni < Cf::NI; ++ni)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const int f = 32 * ni + (lane & 31);
+          const int f = wf0 + 32 * ni + (lane & 31);
           const int t = 64 * wm + 32 * mi + 8 * rg + 4 * (lane >> 5);
           float y[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float val = acc[mi][ni][4 * rg + j];
-            y[j] = wn ? val : fmaxf(val, 0.f);
+            y[j] = wmap ? val : fmaxf(val, 0.f);
           }
           typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
           *reinterpret_cast<u32x2v*>(dst + f * FP + 2 * t) =
@@ -209,7 +225,7 @@ void proj_kv_kernel(KArgs a, PArgs pa) {
         }
     __syncthreads();
     // z and the rotation: thread (tq, pg) owns tokens 4 tq .. + 3 and pairs
-    // pg, pg + 8, ...
+    // pg, pg + PGS, ...
     {
       RowOff ro[4];
       if (ROPE) {
@@ -222,7 +238,7 @@ void proj_kv_kernel(KArgs a, PArgs pa) {
       }
 #pragma unroll
       for (int i = 0; i < NPG; ++i) {
-        const int p = pg + 8 * i;
+        const int p = pg + PGS * i;
         typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
         u32x2v* r0 = reinterpret_cast<u32x2v*>(ktile + (2 * p) * FP + 8 * tq);
         u32x2v* r1 = reinterpret_cast<u32x2v*>(ktile + (2 * p + 1) * FP + 8 * tq);
@@ -251,7 +267,7 @@ void proj_kv_kernel(KArgs a, PArgs pa) {
     // S += rk^T v over the tile's tokens (k-steps of 16 tokens)
 #pragma unroll
     for (int u = 0; u < Cf::STW; ++u) {
-      const int q = wave + 4 * u;
+      const int q = wave + Cf::NW * u;
       if (q < Cf::ST) {
         const int ti = q / (D / 32), tj = q % (D / 32);
         const unsigned char* ar = ktile + (32 * ti + (lane & 31)) * FP + 16 * (lane >> 5);
@@ -270,7 +286,7 @@ void proj_kv_kernel(KArgs a, PArgs pa) {
   float* dstp = a.part + ((size_t)bh * a.C + c) * (size_t)(D * D + D);
 #pragma unroll
   for (int u = 0; u < Cf::STW; ++u) {
-    const int q = wave + 4 * u;
+    const int q = wave + Cf::NW * u;
     if (q < Cf::ST) {
       const int ti = q / (D / 32), tj = q % (D / 32);
 #pragma unroll
@@ -289,14 +305,15 @@ void proj_kv_kernel(KArgs a, PArgs pa) {
       float s = zacc[i][hf];
 #pragma unroll
       for (int msk = 1; msk < 32; msk *= 2) s += __shfl_xor(s, msk);
-      if (tq == 0) dstp[D * D + 2 * (pg + 8 * i) + hf] = s;
+      if (tq == 0) dstp[D * D + 2 * (pg + PGS * i) + hf] = s;
     }
 }
 
 // ---------------------------------------------------------------------------
 // qg kernel
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * ProjCfg<D>::NW)
+__attribute__((amdgpu_waves_per_eu(ProjCfg<D>::NW / 4, ProjCfg<D>::NW / 4)))
 void proj_qg_kernel(KArgs a, PArgs pa) {
   using Cf = ProjCfg<D>;
   constexpr int TM = Cf::TM, QP = Cf::QP;
@@ -315,20 +332,20 @@ void proj_qg_kernel(KArgs a, PArgs pa) {
   gm.rw = make_rsrc(pa.w, (uint32_t)((size_t)4 * HD * pa.Cdim * 2));
   gm.x_row = (uint32_t)pa.Cdim * 2u;
   gm.n_tile_end = n_end;
-  gm.wrow[0] = 0 * HD + h * D;  // q
-  gm.wrow[1] = 3 * HD + h * D;  // g
+  gm.wrow0 = 0 * HD + h * D;  // q
+  gm.wrow1 = 3 * HD + h * D;  // g
 
-  f32x16 acc[2][D / 32];
+  f32x16 acc[2][Cf::NI];
   gemm_tile<D>(gm, n_begin, pa.Cdim, smem, acc);
   // token-major tile: row t holds q (D bf16) then g (D bf16)
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < D / 32; ++ni)
+    for (int ni = 0; ni < Cf::NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 64 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int f = D * wn + 32 * ni + (lane & 31);
+        const int f = Cf::WC * wn + 32 * ni + (lane & 31);
         const __bf16 y = (__bf16)acc[mi][ni][r];
         *reinterpret_cast<__bf16*>(smem + t * QP + 2 * f) = y;
       }
@@ -338,7 +355,7 @@ void proj_qg_kernel(KArgs a, PArgs pa) {
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(pa.gbuf + boff, a.slab_bytes);
   const uint32_t tokstride = (uint32_t)a.H * D * 2;
   constexpr int CPR = D / 8;  // 16-byte chunks per map row
-  for (int cidx = tid; cidx < TM * 2 * CPR; cidx += 256) {
+  for (int cidx = tid; cidx < TM * 2 * CPR; cidx += Cf::NT) {
     const int t = cidx / (2 * CPR), part = (cidx / CPR) & 1, u = cidx % CPR;
     const u32x4 v = *reinterpret_cast<const u32x4*>(smem + t * QP + 2 * (part * D + 8 * u));
     const int n = n_begin + t;
@@ -355,23 +372,23 @@ hipError_t launch_proj_d(const Plan& p, const KArgs& akv, const KArgs& aqg, cons
   // k, v and the state partials
   const bool tl = akv.cs && table_lds_bytes(akv) <= kMaxLdsTableBytes;
   const size_t lds = Cf::LDS_BYTES + (tl ? table_lds_bytes(akv) : 0);
-  const dim3 g1(p.C, p.BH);
+  const dim3 g1(p.BH, p.C);
   hipError_t e;
   if (!akv.cs) {
     if ((e = allow_lds<proj_kv_kernel<D, false, false>>(lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((proj_kv_kernel<D, false, false>), g1, dim3(256), lds, s, akv, pa);
+    hipLaunchKernelGGL((proj_kv_kernel<D, false, false>), g1, dim3(Cf::NT), lds, s, akv, pa);
   } else if (tl) {
     if ((e = allow_lds<proj_kv_kernel<D, true, true>>(lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((proj_kv_kernel<D, true, true>), g1, dim3(256), lds, s, akv, pa);
+    hipLaunchKernelGGL((proj_kv_kernel<D, true, true>), g1, dim3(Cf::NT), lds, s, akv, pa);
   } else {
     if ((e = allow_lds<proj_kv_kernel<D, true, false>>(lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((proj_kv_kernel<D, true, false>), g1, dim3(256), lds, s, akv, pa);
+    hipLaunchKernelGGL((proj_kv_kernel<D, true, false>), g1, dim3(Cf::NT), lds, s, akv, pa);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // q and g
   if ((e = allow_lds<proj_qg_kernel<D>>(Cf::LDS_BYTES)) != hipSuccess) return e;
   const dim3 g2(p.BH, aqg.CB);
-  hipLaunchKernelGGL((proj_qg_kernel<D>), g2, dim3(256), Cf::LDS_BYTES, s, aqg, pa);
+  hipLaunchKernelGGL((proj_qg_kernel<D>), g2, dim3(Cf::NT), Cf::LDS_BYTES, s, aqg, pa);
   return hipGetLastError();
 }
 
