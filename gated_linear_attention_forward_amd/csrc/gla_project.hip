@@ -69,6 +69,13 @@ struct ProjCfg {
   static_assert(D / 2 % PGS == 0, "pairs split evenly over the pair groups");
 };
 
+// Block barrier for LDS hand-offs: every wave's LDS writes are complete
+// before any wave passes; global loads in flight keep flying (a plain
+// __syncthreads would also wait for them, defeating the prefetch).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 struct Gemm {
   __amdgpu_buffer_rsrc_t rx, rw;
   uint32_t x_row;      // bytes per x row (C * 2)
@@ -92,45 +99,61 @@ __device__ __forceinline__ void gemm_tile(const Gemm& gm, int tile0, int Cdim, u
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  u32x4 ra[Cf::ACH], rb[Cf::BCH];
-  auto gload = [&](int k0) {
+  // two register sets: the loads of K-step kt + 2 are in flight while step
+  // kt is multiplied and step kt + 1 goes into LDS.  Every step issues its
+  // loads and LDS writes unconditionally (past the last K-step the offsets
+  // lie outside the buffers, which load zeros without touching memory), so
+  // the count of loads in flight is the same on every path and each wait is
+  // for the older register set only; an odd step count runs one extra step
+  // over a zero stage, which adds exactly nothing.
+  u32x4 ra[2][Cf::ACH], rb[2][Cf::BCH];
+  auto gload = [&](auto SET, int k0, bool valid) {
+    constexpr int st = decltype(SET)::value;
 #pragma unroll
     for (int i = 0; i < Cf::ACH; ++i) {
       const int c = tid + Cf::NT * i, row = c >> 3, col = c & 7;
       const int n = tile0 + row;
-      const uint32_t off = n < gm.n_tile_end
+      const uint32_t off = (valid && n < gm.n_tile_end)
                                ? (uint32_t)n * gm.x_row + (uint32_t)(k0 + 8 * col) * 2u
                                : kOob;
-      ra[i] = load16(gm.rx, off);
+      ra[st][i] = load16(gm.rx, off);
     }
 #pragma unroll
     for (int i = 0; i < Cf::BCH; ++i) {
       const int c = tid + Cf::NT * i, row = c >> 3, col = c & 7;
       const int wr = (row < D ? gm.wrow0 : gm.wrow1 - D) + row;
-      rb[i] = load16(gm.rw, (uint32_t)wr * gm.x_row + (uint32_t)(k0 + 8 * col) * 2u);
+      const uint32_t off = valid ? (uint32_t)wr * gm.x_row + (uint32_t)(k0 + 8 * col) * 2u : kOob;
+      rb[st][i] = load16(gm.rw, off);
     }
   };
-  auto lwrite = [&](unsigned char* st) {
+  auto lwrite = [&](auto SET, unsigned char* stg) {
+    constexpr int st = decltype(SET)::value;
 #pragma unroll
     for (int i = 0; i < Cf::ACH; ++i) {
       const int c = tid + Cf::NT * i;
-      *reinterpret_cast<u32x4*>(st + (c >> 3) * Cf::AP + 16 * (c & 7)) = ra[i];
+      *reinterpret_cast<u32x4*>(stg + (c >> 3) * Cf::AP + 16 * (c & 7)) = ra[st][i];
     }
 #pragma unroll
     for (int i = 0; i < Cf::BCH; ++i) {
       const int c = tid + Cf::NT * i;
-      *reinterpret_cast<u32x4*>(st + Cf::A_BYTES + (c >> 3) * Cf::AP + 16 * (c & 7)) = rb[i];
+      *reinterpret_cast<u32x4*>(stg + Cf::A_BYTES + (c >> 3) * Cf::AP + 16 * (c & 7)) = rb[st][i];
     }
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   const int nk = Cdim / Cf::KT;
-  gload(0);
-  lwrite(smem);
-  __syncthreads();
+  gload(S0{}, 0, true);
+  gload(S1{}, Cf::KT, nk > 1);
+  lwrite(S0{}, smem);
+  lds_barrier();
   const int arow = 64 * wm + (lane & 31), brow = Cf::WC * wn + (lane & 31);
   const int kb = 16 * (lane >> 5);  // byte offset of the lane's 8 k values in a 16-wide step
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * Cf::KT);
-    const unsigned char* st = smem + (kt & 1) * Cf::STAGE;
+  // step kt (P = kt % 2): refill set P with step kt + 2, multiply stage P,
+  // move set 1 - P (step kt + 1) into stage 1 - P
+  auto step = [&](auto PAR, int kt) {
+    constexpr int P = decltype(PAR)::value;
+    gload(std::integral_constant<int, P>{}, (kt + 2) * Cf::KT, kt + 2 < nk);
+    const unsigned char* st = smem + P * Cf::STAGE;
 #pragma unroll
     for (int ks = 0; ks < Cf::KT / 16; ++ks) {
       bf16x8 A[Cf::MI], Bm[Cf::NI];
@@ -147,8 +170,12 @@ __device__ __forceinline__ void gemm_tile(const Gemm& gm, int tile0, int Cdim, u
         for (int ni = 0; ni < Cf::NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mi], Bm[ni], acc[mi][ni], 0, 0, 0);
     }
-    if (kt + 1 < nk) lwrite(smem + ((kt + 1) & 1) * Cf::STAGE);
-    __syncthreads();
+    lwrite(std::integral_constant<int, 1 - P>{}, smem + (1 - P) * Cf::STAGE);
+    lds_barrier();
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(S0{}, kt);
+    step(S1{}, kt + 1);
   }
 }
 
