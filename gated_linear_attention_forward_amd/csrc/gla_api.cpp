@@ -644,7 +644,7 @@ namespace {
 // operand, then the S rows operand, fp32 z, dz partials and the bf16 a tensor.
 struct BwdLayout {
   Plan p;
-  size_t off_sl2, off_z, off_dzp, off_a, bytes;
+  size_t off_sl2, off_z, off_dzp, off_dz, off_a, bytes;
 };
 
 BwdLayout bwd_layout(int B, int N, int H, int D) {
@@ -657,6 +657,8 @@ BwdLayout bwd_layout(int B, int N, int H, int D) {
   off = gla::align_up(off + (size_t)l.p.BH * D * sizeof(float), 256);
   l.off_dzp = off;
   off = gla::align_up(off + (size_t)l.p.BH * l.p.C2 * D * sizeof(float), 256);
+  l.off_dz = off;
+  off = gla::align_up(off + (size_t)l.p.BH * D * sizeof(float), 256);
   l.off_a = off;
   off = gla::align_up(off + (size_t)B * N * H * D * sizeof(uint16_t), 256);
   l.bytes = off;
@@ -724,6 +726,7 @@ int gla_backward_ws(const void* q, const void* k, const void* v, const void* g, 
   bw.abuf = abuf;
   bw.z = zbuf;
   bw.dzp = dzp;
+  bw.dz = reinterpret_cast<float*>(w + l.off_dz);
   bw.C2 = p.C2;
 
   // 1. S (both operand layouts) and fp32 z from k and v

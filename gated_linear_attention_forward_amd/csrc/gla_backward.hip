@@ -37,7 +37,7 @@ namespace gla {
 namespace {
 
 constexpr int kQueryWaves = 8;
-constexpr int kKeyWaves = 4;
+constexpr int kKeyWaves = 8;
 
 template <int D>
 struct BwdCfg {
@@ -347,14 +347,33 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
 }
 
 // ---------------------------------------------------------------------------
-// Key kernel.  Block = 4 waves, one (token range, head); grid (B H, C2).
-// LDS holds the head's dS^T and dS row operands and fp32 dz, which each block
-// sums from the query kernel's range partials in range order (every block of
-// a head gets the same bits).  Per 16-token step: R phi(k) against dS^T gives
+// dz of each head: the query kernel's range partials summed in range order
+// (one thread per feature; loads eight ranges ahead of the sum).
+template <int D>
+__global__ __launch_bounds__(D) void dz_sum_kernel(BArgs bw) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* p = bw.dzp + (size_t)bh * bw.C2 * D + d;
+  float sum = 0.f;
+  int c = 0;
+  for (; c + 8 <= bw.C2; c += 8) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = p[(size_t)(c + i) * D];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum += x[i];
+  }
+  for (; c < bw.C2; ++c) sum += p[(size_t)c * D];
+  bw.dz[(size_t)bh * D + d] = sum;
+}
+
+// Key kernel.  Block = 8 waves (the two operands take about half the LDS,
+// so one block per compute unit: 8 waves make two per SIMD), one (token
+// range, head); grid (B H, C2).
+// LDS holds the head's dS^T and dS row operands and fp32 dz.  Per 16-token step: R phi(k) against dS^T gives
 // dv; v (as loaded) against dS rows gives dS v, rotated back by R^T, plus dz,
 // masked by k > 0: dk.
 template <int D, bool ROPE, bool TLDS>
-__global__ __launch_bounds__(64 * kKeyWaves) __attribute__((amdgpu_waves_per_eu(2, 4)))
+__global__ __launch_bounds__(64 * kKeyWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_key_kernel(KArgs a, BArgs bw) {
   using Cf = BwdCfg<D>;
   constexpr int KS = Cf::KS, MB = Cf::MB, OB = Cf::OB, PU = Cf::PU;
@@ -378,12 +397,7 @@ void bwd_key_kernel(KArgs a, BArgs bw) {
 
   stage_rows<D, NT>(sD, a.sl + (size_t)bh * (D + 2) * D, D);
   stage_rows<D, NT>(sR, a.sl2 + (size_t)bh * D * D, D);
-  if (tid < D) {
-    const float* p = bw.dzp + (size_t)bh * bw.C2 * D + tid;
-    float sum = p[0];
-    for (int c = 1; c < bw.C2; ++c) sum += p[(size_t)c * D];
-    zf[tid] = sum;
-  }
+  for (int i = tid; i < D; i += NT) zf[i] = bw.dz[(size_t)bh * D + i];
   TabView tv{};
   if (ROPE) tv = stage_table<D, NT>(a, ltab, TLDS, n_begin, n_end);
   __syncthreads();
@@ -509,6 +523,9 @@ hipError_t launch_bwd_query_d(const Plan& p, const KArgs& a, const BArgs& b, hip
 
 template <int D>
 hipError_t launch_bwd_key_d(const Plan& p, const KArgs& a, const BArgs& b, hipStream_t s) {
+  hipLaunchKernelGGL((dz_sum_kernel<D>), dim3(p.BH), dim3(D), 0, s, b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;
   const size_t lds = BwdCfg<D>::K_BYTES + (tl ? table_lds_bytes(a) : 0);
   constexpr int T = 64 * kKeyWaves;
