@@ -73,15 +73,18 @@ __global__ __launch_bounds__(256) void softmax_prep_kernel(KArgs a, uint16_t* qr
 // Flash kernel.
 //
 // Block = 4 waves, 128 consecutive queries of one head (32 per wave).  For
-// each 64-key tile (K and V staged in LDS, double-buffered, the next tile's
-// global loads in flight during the current one):
+// each 64-key tile (K and V loaded straight into LDS, double-buffered, the
+// next tile's loads in flight during the current one):
 //   scores    S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with the keys as the A
 //             operand (K rows read straight from LDS) and the wave's queries
 //             as the B operand (held in registers for the whole block).  The
 //             accumulator then gives each lane one query (l % 32) and 16 of
 //             the 32 keys of a sub-tile (rows 8 (r/4) + 4 (l/32) + r % 4),
 //             so a query's maximum and sum need one cross-lane step (l^32);
-//   softmax   online in fp32 on exp2 (q carries the log2(e) / sqrt(D) scale);
+//   softmax   online in fp32 on exp2 (q carries the log2(e) / sqrt(D) scale),
+//             with a running maximum that may trail the true one by up to
+//             kLazyMax (the same stale maximum scales the weights and their
+//             sum, so the result is the same softmax);
 //   values    O^T += V^T P^T with P^T as the B operand straight from the
 //             score registers: in k-step s the lane's 8 keys are
 //             16 s + 8 (k / 4) + 4 (l / 32) + k % 4, and the V operand is
@@ -101,10 +104,12 @@ struct FaCfg {
   static constexpr int VP = tile_pitch(2 * D);
   static constexpr int K_BYTES = KT * KP;
   static constexpr int STAGE = K_BYTES + KT * VP;
-  static constexpr int LDS_BYTES = 2 * STAGE;
-  static constexpr int CHUNKS = KT * D / 8;    // 16-byte chunks per tile and tensor
-  static constexpr int LPT = CHUNKS / 256;     // of them per thread
   static_assert((KP / 4) % 64 == 4 || (KP / 4) % 64 == 36, "K pitch");
+  static_assert(K_BYTES % 1024 == 0 && (KT * VP) % 1024 == 0, "whole 64-slot DMA groups");
+  // a running maximum that trails a tile's maximum by at most this much (in
+  // log2 units) is kept: the weights stay below 2^8, and the accumulators
+  // are rescaled only when the maximum really moves
+  static constexpr float kLazyMax = 8.f;
 };
 
 // Transposing read of the V operand: rows 16 s + 4 G + j (first read) and
@@ -122,12 +127,39 @@ __device__ __forceinline__ bf16x8 frag_tr_keys(const unsigned char* tile, int pi
   return __builtin_bit_cast(bf16x8, v);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One KT x D tile of a [B, N, H, D] tensor into LDS rows of PITCH bytes by
+// buffer loads that write LDS directly: load I of the tile fills the 64
+// 16-byte slots 64 I .. 64 I + 63 (lane i writes slot 64 I + i, at the
+// uniform base the instruction takes); a slot past a row's D / 8 chunks is
+// row padding and rows past N load zeros.  Completion is tracked by vmcnt.
+template <int D, int PITCH>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int n0, int N,
+                                         uint32_t tokstride, uint32_t headoff, int wave,
+                                         int lane) {
+  constexpr int SPR = PITCH / 16;                 // slots per row
+  constexpr int LOADS = FaCfg<D>::KT * SPR / 64;  // 64-slot groups per tile
+#pragma unroll
+  for (int I = wave; I < LOADS; I += 4) {
+    const int slot = 64 * I + lane;
+    const int row = slot / SPR, ch = slot - (slot / SPR) * SPR;
+    const int n = n0 + row;
+    const uint32_t off = (ch < D / 8 && n < N) ? (uint32_t)n * tokstride + headoff + 16u * ch : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 1024 * I), 16, off, 0, 0, 0);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
   using Cf = FaCfg<D>;
   constexpr int KS = Cf::KS, ND = Cf::ND;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // two stage buffers as distinct objects: the compiler then sees that a
+  // tile's reads never touch the buffer the next tile is loading into, and
+  // does not wait for those loads before reading
+  __shared__ __attribute__((aligned(16))) unsigned char stage0[Cf::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char stage1[Cf::STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -150,29 +182,11 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
 #pragma unroll
   for (int s = 0; s < KS; ++s) Qf[s] = __builtin_bit_cast(bf16x8, load16(rq, qoff + 32u * s));
 
-  // tile loads: thread tid takes chunks tid + 256 i of the 64 x D tile
-  u32x4 kreg[Cf::LPT], vreg[Cf::LPT];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < Cf::LPT; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), ch = c % (D / 8);
-      const int n = j * Cf::KT + row;
-      const uint32_t off = n < a.N ? (uint32_t)n * tokstride + headoff + 16u * ch : kOob;
-      kreg[i] = load16(rk, off);
-      vreg[i] = load16(rv, off);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* kt = smem + buf * Cf::STAGE;
-    unsigned char* vt = kt + Cf::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < Cf::LPT; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), ch = c % (D / 8);
-      *reinterpret_cast<u32x4*>(kt + row * Cf::KP + 16 * ch) = kreg[i];
-      *reinterpret_cast<u32x4*>(vt + row * Cf::VP + 16 * ch) = vreg[i];
-    }
+  // K and V tiles go straight to LDS (no staging registers): the next tile's
+  // loads are issued at the start of a tile and waited for at its end
+  auto load_tile = [&](int j, unsigned char* st) {
+    dma_tile<D, Cf::KP>(rk, st, j * Cf::KT, a.N, tokstride, headoff, wave, lane);
+    dma_tile<D, Cf::VP>(rv, st + Cf::K_BYTES, j * Cf::KT, a.N, tokstride, headoff, wave, lane);
   };
 
   f32x16 acc_o[ND];
@@ -182,28 +196,32 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
     for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int ntiles = (a.N + Cf::KT - 1) / Cf::KT;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const unsigned char* kt = smem + (j & 1) * Cf::STAGE;
+  auto tile = [&](int j, const unsigned char* kt, unsigned char* next) {
     const unsigned char* vt = kt + Cf::K_BYTES;
-    if (j + 1 < ntiles) load_tile(j + 1);
+    load_tile(j + 1, next);   // past the last tile: zeros, never read
 
-    // scores of keys 32 t + (8 (r/4) + 4 G + r % 4), t = 0, 1
+    // scores of keys 32 t + (8 (r/4) + 4 G + r % 4), t = 0, 1; the K
+    // fragments of k-step s + 1 are read while step s multiplies
     f32x16 s_acc[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s_acc[t][r] = 0.f;
+    bf16x8 kf[2][2];
+    auto read_k = [&](int s, bf16x8 (&dst)[2]) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(kt + (32 * t + col) * Cf::KP + 32 * s + 16 * G);
-        s_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[s], s_acc[t], 0, 0, 0);
-      }
-    }
+      for (int t = 0; t < 2; ++t)
+        dst[t] = *reinterpret_cast<const bf16x8*>(kt + (32 * t + col) * Cf::KP + 32 * s + 16 * G);
+    };
+    read_k(0, kf[0]);
+    static_for<KS>([&](auto S) {
+      constexpr int s = decltype(S)::value;
+      if constexpr (s + 1 < KS) read_k(s + 1, kf[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        s_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][t], Qf[s], s_acc[t], 0, 0, 0);
+    });
     // keys past N take no weight
     const int kbase = j * Cf::KT;
     if (kbase + Cf::KT > a.N) {
@@ -219,9 +237,18 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s_acc[t][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    // the running maximum moves (and the accumulators are rescaled) only
+    // when some query's tile maximum passes it by more than kLazyMax
+    if (__any(mt > m_run + Cf::kLazyMax)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[i][r] *= alpha;
+    }
     float psum = 0.f;
     bf16x8 Pb[4];
 #pragma unroll
@@ -230,18 +257,14 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
       uint32_t w[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float p0 = __builtin_amdgcn_exp2f(s_acc[t][r0 + 2 * k] - m_new);
-        const float p1 = __builtin_amdgcn_exp2f(s_acc[t][r0 + 2 * k + 1] - m_new);
+        const float p0 = __builtin_amdgcn_exp2f(s_acc[t][r0 + 2 * k] - m_run);
+        const float p1 = __builtin_amdgcn_exp2f(s_acc[t][r0 + 2 * k + 1] - m_run);
         psum += p0 + p1;
         w[k] = pack_bf16(p0, p1);
       }
       Pb[s2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < ND; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[i][r] *= alpha;
+    l_run += psum;
 
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
@@ -250,9 +273,19 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
         const bf16x8 vf = frag_tr_keys(vt, Cf::VP, i, s2, lane);
         acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, Pb[s2], acc_o[i], 0, 0, 0);
       }
-
-    if (j + 1 < ntiles) store_tile((j + 1) & 1);
+    // the next tile is in LDS and every wave is done with this one (the
+    // compiler sees this wait, so it does not wait again before reading)
     __syncthreads();
+  };
+
+  const int ntiles = (a.N + Cf::KT - 1) / Cf::KT;
+  load_tile(0, stage0);
+  __syncthreads();
+  // two tiles per trip, so each names its buffers statically; an odd count
+  // runs one more tile whose keys all lie past N (masked: no weight)
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(j, stage0, stage1);
+    tile(j + 1, stage1, stage0);
   }
 
   // o = sigmoid(g) * O / l: lane holds query qn at dims 32 i + 8 (r/4) + 4 G + r % 4
@@ -294,10 +327,8 @@ hipError_t launch_softmax_d(const Plan& p, KArgs a, uint16_t* qr, uint16_t* kr,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   using Cf = FaCfg<D>;
-  e = allow_lds<flash_kernel<D>>(Cf::LDS_BYTES);
-  if (e != hipSuccess) return e;
   const dim3 gf((p.N + Cf::QB - 1) / Cf::QB, p.BH);
-  hipLaunchKernelGGL((flash_kernel<D>), gf, dim3(256), Cf::LDS_BYTES, stream, a, qr, kr);
+  hipLaunchKernelGGL((flash_kernel<D>), gf, dim3(256), 0, stream, a, qr, kr);
   return hipGetLastError();
 }
 
