@@ -91,63 +91,69 @@ __global__ __launch_bounds__(256) void softmax_prep_kernel(KArgs a, uint16_t* qr
 //             read with ds_read_b64_tr_b16 from exactly those rows.  O^T's
 //             accumulator again gives each lane one query, so the softmax
 //             rescale is one scalar per lane.
-// K rows are padded to 4 (mod 64) dwords (16 rows of one 16-byte column hit
-// distinct banks); V rows to 16 or 48 (mod 64) dwords, as the transposing
-// reads want.
+//
+// LDS layout of a 64-key tile.  One buffer-load-to-LDS instruction fills
+// 1 KB: RPG whole rows (RPG = 64 lanes / (D / 8) 16-byte chunks per row).
+// Such a group of rows is padded, and row q of a group stores its chunk c at
+// position c ^ (SW q), so that the reads below hit distinct banks:
+//   K  (16-byte reads of 16 consecutive rows, one chunk):  groups padded by
+//      16 bytes, SW = 16 / RPG;
+//   V  (transposing 8-byte reads of 4 consecutive rows, 64 bytes each):
+//      SW = 4, groups padded to 128 (mod 256) bytes when a group is 2 rows.
+// The XOR keeps every read offset a compile-time constant from one of RPG
+// per-lane bases (the swizzled bits of c are known at compile time).
 template <int D>
 struct FaCfg {
   static constexpr int QB = 128;   // queries per block
   static constexpr int KT = 64;    // keys per tile
   static constexpr int KS = D / 16;  // k-steps of the scores
   static constexpr int ND = D / 32;  // 32-dim tiles of O^T
-  static constexpr int KP = 2 * D + 16;
-  static constexpr int VP = tile_pitch(2 * D);
-  static constexpr int K_BYTES = KT * KP;
-  static constexpr int STAGE = K_BYTES + KT * VP;
-  static_assert((KP / 4) % 64 == 4 || (KP / 4) % 64 == 36, "K pitch");
-  static_assert(K_BYTES % 1024 == 0 && (KT * VP) % 1024 == 0, "whole 64-slot DMA groups");
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  static constexpr int RPG = 64 / CPR;  // rows per 1 KB load group
+  static constexpr int GROUPS = KT / RPG;
+  static constexpr int GPW = GROUPS / 4;  // load groups per wave and tensor
+  static constexpr int KSW = 16 / RPG;
+  static constexpr int VSW = 4;
+  static constexpr int KG = RPG * 2 * D + 16;
+  static constexpr int VG = RPG * 2 * D + (RPG == 2 ? 128 : 0);
+  static constexpr int K_BYTES = GROUPS * KG;
+  static constexpr int STAGE = K_BYTES + GROUPS * VG;
+  static_assert(GROUPS % 4 == 0 && KG % 16 == 0 && VG % 16 == 0, "load groups");
   // a running maximum that trails a tile's maximum by at most this much (in
   // log2 units) is kept: the weights stay below 2^8, and the accumulators
   // are rescaled only when the maximum really moves
   static constexpr float kLazyMax = 8.f;
+  // how far (log2 units) a tile's maximum may pass the fixed reference of
+  // the main pass: weights up to 2^64, sums over < 2^31 keys stay far below
+  // the fp32 range
+  static constexpr float kFixedSpan = 64.f;
 };
-
-// Transposing read of the V operand: rows 16 s + 4 G + j (first read) and
-// 16 s + 8 + 4 G + j (second), G = l / 32, j < 4; columns 32 i + l % 32.
-__device__ __forceinline__ bf16x8 frag_tr_keys(const unsigned char* tile, int pitch, int i, int s2,
-                                               int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  const int f = 32 * i + 16 * (g & 1) + 4 * (s & 3);
-  const int row = 16 * s2 + 4 * (g >> 1) + (s >> 2);
-  const unsigned char* p0 = tile + row * pitch + 2 * f;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * pitch));
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One KT x D tile of a [B, N, H, D] tensor into LDS rows of PITCH bytes by
-// buffer loads that write LDS directly: load I of the tile fills the 64
-// 16-byte slots 64 I .. 64 I + 63 (lane i writes slot 64 I + i, at the
-// uniform base the instruction takes); a slot past a row's D / 8 chunks is
-// row padding and rows past N load zeros.  Completion is tracked by vmcnt.
-template <int D, int PITCH>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int n0, int N,
-                                         uint32_t tokstride, uint32_t headoff, int wave,
-                                         int lane) {
-  constexpr int SPR = PITCH / 16;                 // slots per row
-  constexpr int LOADS = FaCfg<D>::KT * SPR / 64;  // 64-slot groups per tile
+// This lane's part of the global offset of the chunk it loads in every group:
+// row q = lane / CPR of the group, chunk (lane % CPR) ^ (SW q).
+template <int D, int SW>
+__device__ __forceinline__ uint32_t dma_lane_offset(int lane, uint32_t tokstride, uint32_t headoff) {
+  constexpr int CPR = FaCfg<D>::CPR;
+  const int q = lane / CPR, pc = lane % CPR;
+  return (uint32_t)q * tokstride + headoff + 16u * (uint32_t)(pc ^ (SW * q));
+}
+
+// The wave's GPW groups of one tensor's tile (keys n0 ..): group I holds rows
+// RPG I .. RPG I + RPG - 1 at dst + I * GP.  Rows past N lie outside the
+// slab and load zeros.  Completion is tracked by vmcnt.
+template <int D, int GP>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t lane_off,
+                                         int n0, uint32_t tokstride, int wave) {
+  using Cf = FaCfg<D>;
+  const int I0 = wave * Cf::GPW;
+  const uint32_t row_off = (uint32_t)(n0 + Cf::RPG * I0) * tokstride;
 #pragma unroll
-  for (int I = wave; I < LOADS; I += 4) {
-    const int slot = 64 * I + lane;
-    const int row = slot / SPR, ch = slot - (slot / SPR) * SPR;
-    const int n = n0 + row;
-    const uint32_t off = (ch < D / 8 && n < N) ? (uint32_t)n * tokstride + headoff + 16u * ch : kOob;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 1024 * I), 16, off, 0, 0, 0);
-  }
+  for (int ii = 0; ii < Cf::GPW; ++ii)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_void*)(dst + (I0 + ii) * GP), 16,
+        lane_off + row_off + (uint32_t)(ii * Cf::RPG) * tokstride, 0, 0, 0);
 }
 
 template <int D>
@@ -184,34 +190,62 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
 
   // K and V tiles go straight to LDS (no staging registers): the next tile's
   // loads are issued at the start of a tile and waited for at its end
+  const uint32_t klane = dma_lane_offset<D, Cf::KSW>(lane, tokstride, headoff);
+  const uint32_t vlane = dma_lane_offset<D, Cf::VSW>(lane, tokstride, headoff);
   auto load_tile = [&](int j, unsigned char* st) {
-    dma_tile<D, Cf::KP>(rk, st, j * Cf::KT, a.N, tokstride, headoff, wave, lane);
-    dma_tile<D, Cf::VP>(rv, st + Cf::K_BYTES, j * Cf::KT, a.N, tokstride, headoff, wave, lane);
+    dma_tile<D, Cf::KG>(rk, st, klane, j * Cf::KT, tokstride, wave);
+    dma_tile<D, Cf::VG>(rv, st + Cf::K_BYTES, vlane, j * Cf::KT, tokstride, wave);
   };
 
-  f32x16 acc_o[ND];
+  // LDS read bases.  K: row col (+ 32 t), chunk 2 s + G; base m serves the
+  // chunks whose swizzled bits (c / KSW) % RPG equal m.
+  constexpr int RPG = Cf::RPG;
+  int kb[RPG];
+  {
+    const int q = col % RPG;
 #pragma unroll
-  for (int i = 0; i < ND; ++i)
+    for (int m = 0; m < RPG; ++m)
+      kb[m] = (col / RPG) * Cf::KG + q * 2 * D + 16 * (G + Cf::KSW * (m ^ q));
+  }
+  // V, read transposed: this lane's 4 dims 32 i + 16 (g & 1) + 4 (l & 3) of
+  // rows 16 s2 + 4 (g >> 1) + (l & 15) / 4 (and 8 rows on), g = l / 16;
+  // base m serves the 32-dim tiles i with i % RPG == m.
+  int vb[RPG];
+  {
+    const int g = lane >> 4, sl = lane & 15;
+    const int r0 = 4 * (g >> 1) + (sl >> 2), q = r0 % RPG;
+    const int clo = 2 * (g & 1) + ((sl >> 1) & 1);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int m = 0; m < RPG; ++m)
+      vb[m] = (r0 / RPG) * Cf::VG + q * 2 * D + 8 * (sl & 1) + 16 * (clo + Cf::VSW * (m ^ q));
+  }
 
-  auto tile = [&](int j, const unsigned char* kt, unsigned char* next) {
-    const unsigned char* vt = kt + Cf::K_BYTES;
-    load_tile(j + 1, next);   // past the last tile: zeros, never read
+  auto read_v = [&](const unsigned char* vt, int i, int s2) {
+    const unsigned char* p0 =
+        vt + vb[i % RPG] + (16 * s2 / RPG) * Cf::VG + 16 * Cf::VSW * RPG * (i / RPG);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + (8 / RPG) * Cf::VG));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
-    // scores of keys 32 t + (8 (r/4) + 4 G + r % 4), t = 0, 1; the K
-    // fragments of k-step s + 1 are read while step s multiplies
-    f32x16 s_acc[2];
+  // scores of keys 32 t + (8 (r/4) + 4 G + r % 4), t = 0, 1, of the tile at
+  // kt (key j * KT first); keys past N score -inf.  Returns the query's
+  // maximum over the tile.
+  auto scores = [&](int j, const unsigned char* kt, f32x16 (&s_acc)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s_acc[t][r] = 0.f;
+    // the K fragments of k-step s + 1 are read while step s multiplies
     bf16x8 kf[2][2];
     auto read_k = [&](int s, bf16x8 (&dst)[2]) {
+      const int c = 2 * s;  // the lane adds G
+      const int off = 16 * (c % Cf::KSW + Cf::KSW * RPG * (c / (Cf::KSW * RPG)));
+      const int base = kb[(c / Cf::KSW) % RPG];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        dst[t] = *reinterpret_cast<const bf16x8*>(kt + (32 * t + col) * Cf::KP + 32 * s + 16 * G);
+        dst[t] = *reinterpret_cast<const bf16x8*>(kt + base + t * (32 / RPG) * Cf::KG + off);
     };
     read_k(0, kf[0]);
     static_for<KS>([&](auto S) {
@@ -222,7 +256,6 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
       for (int t = 0; t < 2; ++t)
         s_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][t], Qf[s], s_acc[t], 0, 0, 0);
     });
-    // keys past N take no weight
     const int kbase = j * Cf::KT;
     if (kbase + Cf::KT > a.N) {
 #pragma unroll
@@ -236,19 +269,12 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s_acc[t][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // the running maximum moves (and the accumulators are rescaled) only
-    // when some query's tile maximum passes it by more than kLazyMax
-    if (__any(mt > m_run + Cf::kLazyMax)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < ND; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[i][r] *= alpha;
-    }
+    return fmaxf(mt, __shfl_xor(mt, 32));
+  };
+
+  // weights exp2(s - m) into O^T += V^T P^T; returns their sum over the
+  // lane's 32 keys
+  auto weigh = [&](const unsigned char* vt, const f32x16 (&s_acc)[2], float m, f32x16 (&acc)[ND]) {
     float psum = 0.f;
     bf16x8 Pb[4];
 #pragma unroll
@@ -257,35 +283,91 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
       uint32_t w[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float p0 = __builtin_amdgcn_exp2f(s_acc[t][r0 + 2 * k] - m_run);
-        const float p1 = __builtin_amdgcn_exp2f(s_acc[t][r0 + 2 * k + 1] - m_run);
+        const float p0 = __builtin_amdgcn_exp2f(s_acc[t][r0 + 2 * k] - m);
+        const float p1 = __builtin_amdgcn_exp2f(s_acc[t][r0 + 2 * k + 1] - m);
         psum += p0 + p1;
         w[k] = pack_bf16(p0, p1);
       }
       Pb[s2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
     }
-    l_run += psum;
-
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-      for (int i = 0; i < ND; ++i) {
-        const bf16x8 vf = frag_tr_keys(vt, Cf::VP, i, s2, lane);
-        acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, Pb[s2], acc_o[i], 0, 0, 0);
-      }
+      for (int i = 0; i < ND; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(vt, i, s2), Pb[s2], acc[i], 0, 0, 0);
+    return psum;
+  };
+
+  const int ntiles = (a.N + Cf::KT - 1) / Cf::KT;
+  f32x16 acc_o[ND];
+  float m_run, l_run;
+
+  // Main pass: every tile's weights are taken against one reference, tile
+  // 0's maximum of the query, so the accumulators are never rescaled.  A
+  // tile whose maximum passes the reference by more than kFixedSpan (weights
+  // past 2^64) flags the block, which then runs the online-rescale pass.
+  load_tile(0, stage0);
+  __syncthreads();
+  {
+    f32x16 s_acc[2];
+    m_run = scores(0, stage0, s_acc);
+  }
+#pragma unroll
+  for (int i = 0; i < ND; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.f;
+  l_run = 0.f;
+  bool over = false;
+  auto fixed_tile = [&](int j, const unsigned char* kt, unsigned char* next) {
+    load_tile(j + 1, next);   // past the last tile: zeros, never read
+    f32x16 s_acc[2];
+    const float mt = scores(j, kt, s_acc);
+    over |= mt > m_run + Cf::kFixedSpan;
+    l_run += weigh(kt + Cf::K_BYTES, s_acc, m_run, acc_o);
     // the next tile is in LDS and every wave is done with this one (the
     // compiler sees this wait, so it does not wait again before reading)
     __syncthreads();
   };
-
-  const int ntiles = (a.N + Cf::KT - 1) / Cf::KT;
-  load_tile(0, stage0);
-  __syncthreads();
   // two tiles per trip, so each names its buffers statically; an odd count
   // runs one more tile whose keys all lie past N (masked: no weight)
   for (int j = 0; j < ntiles; j += 2) {
-    tile(j, stage0, stage1);
-    tile(j + 1, stage1, stage0);
+    fixed_tile(j, stage0, stage1);
+    fixed_tile(j + 1, stage1, stage0);
+  }
+
+  if (__syncthreads_or(over)) {
+    // Online-rescale pass: the running maximum moves (and the accumulators
+    // are rescaled) only when some query's tile maximum passes it by more
+    // than kLazyMax.
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+    auto lazy_tile = [&](int j, const unsigned char* kt, unsigned char* next) {
+      load_tile(j + 1, next);
+      f32x16 s_acc[2];
+      const float mt = scores(j, kt, s_acc);
+      if (__any(mt > m_run + Cf::kLazyMax)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[i][r] *= alpha;
+      }
+      l_run += weigh(kt + Cf::K_BYTES, s_acc, m_run, acc_o);
+      __syncthreads();
+    };
+    load_tile(0, stage0);
+    __syncthreads();
+    for (int j = 0; j < ntiles; j += 2) {
+      lazy_tile(j, stage0, stage1);
+      lazy_tile(j + 1, stage1, stage0);
+    }
   }
 
   // o = sigmoid(g) * O / l: lane holds query qn at dims 32 i + 8 (r/4) + 4 G + r % 4

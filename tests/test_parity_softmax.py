@@ -94,6 +94,29 @@ def test_softmax_constant_values_closed_form():
     assert_close(got, ref, "out")
 
 
+@pytest.mark.parametrize("D", [256, 128])
+@pytest.mark.parametrize("amp", [1.2, 2.0, 3.0])
+def test_softmax_score_spikes(D, amp):
+    """Every other query equals u (entries +-amp) and key 200, past the first
+    key tile, equals u too: that key's score passes every score of tile 0 by
+    about 29, 85 and 200 log2 units at D = 256 for amp 1.2, 2.0 and 3.0
+    (about 20, 58 and 140 at D = 128).  Up to 64 the kernel keeps its fixed
+    reference (weights up to 2^64); past it (amp 2.0 at D = 256, amp 3.0)
+    the block runs the online-rescale pass.  The other queries are random."""
+    B, N, H = 1, 300, 2
+    say(f"case softmax spike D={D} amp={amp}")
+    q, k, v, g = random_inputs(B, N, H, D, seed=3200 + D)
+    rng = np.random.default_rng(3201)
+    u = torch.from_numpy(amp * np.sign(rng.standard_normal(D))).to(torch.bfloat16)
+    q = q.clone()
+    k = k.clone()
+    q[0, ::2, :, :] = u
+    k[0, 200, :, :] = u
+    got = gpu_softmax(q, k, v, g, None).double().cpu().numpy()
+    ref = oracle.softmax_forward(q, k, v, g, None)
+    assert_close(got, ref, "out")
+
+
 def test_softmax_deterministic():
     w = BY_NAME["anchor_5b_480p_81f"]
     say("case softmax determinism")
