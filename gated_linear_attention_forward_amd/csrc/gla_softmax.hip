@@ -117,7 +117,7 @@ struct FaCfg {
   static constexpr int KG = RPG * 2 * D + 16;
   static constexpr int VG = RPG * 2 * D + (RPG == 2 ? 128 : 0);
   static constexpr int K_BYTES = GROUPS * KG;
-  static constexpr int STAGE = K_BYTES + GROUPS * VG;
+  static constexpr int V_BYTES = GROUPS * VG;
   static_assert(GROUPS % 4 == 0 && KG % 16 == 0 && VG % 16 == 0, "load groups");
   // a running maximum that trails a tile's maximum by at most this much (in
   // log2 units) is kept: the weights stay below 2^8, and the accumulators
@@ -161,11 +161,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
   using Cf = FaCfg<D>;
   constexpr int KS = Cf::KS, ND = Cf::ND;
-  // two stage buffers as distinct objects: the compiler then sees that a
-  // tile's reads never touch the buffer the next tile is loading into, and
-  // does not wait for those loads before reading
-  __shared__ __attribute__((aligned(16))) unsigned char stage0[Cf::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char stage1[Cf::STAGE];
+  // two K and two V buffers as distinct objects: the compiler then sees that
+  // a tile's reads never touch a buffer that a load is filling, and does not
+  // wait for those loads before reading
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf0[Cf::K_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf1[Cf::K_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf0[Cf::V_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf1[Cf::V_BYTES];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -188,13 +190,14 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
 #pragma unroll
   for (int s = 0; s < KS; ++s) Qf[s] = __builtin_bit_cast(bf16x8, load16(rq, qoff + 32u * s));
 
-  // K and V tiles go straight to LDS (no staging registers): the next tile's
-  // loads are issued at the start of a tile and waited for at its end
+  // K and V tiles go straight to LDS (no staging registers)
   const uint32_t klane = dma_lane_offset<D, Cf::KSW>(lane, tokstride, headoff);
   const uint32_t vlane = dma_lane_offset<D, Cf::VSW>(lane, tokstride, headoff);
-  auto load_tile = [&](int j, unsigned char* st) {
-    dma_tile<D, Cf::KG>(rk, st, klane, j * Cf::KT, tokstride, wave);
-    dma_tile<D, Cf::VG>(rv, st + Cf::K_BYTES, vlane, j * Cf::KT, tokstride, wave);
+  auto load_k = [&](int j, unsigned char* dst) {
+    dma_tile<D, Cf::KG>(rk, dst, klane, j * Cf::KT, tokstride, wave);
+  };
+  auto load_v = [&](int j, unsigned char* dst) {
+    dma_tile<D, Cf::VG>(rv, dst, vlane, j * Cf::KT, tokstride, wave);
   };
 
   // LDS read bases.  K: row col (+ 32 t), chunk 2 s + G; base m serves the
@@ -230,13 +233,8 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
   };
 
   // scores of keys 32 t + (8 (r/4) + 4 G + r % 4), t = 0, 1, of the tile at
-  // kt (key j * KT first); keys past N score -inf.  Returns the query's
-  // maximum over the tile.
-  auto scores = [&](int j, const unsigned char* kt, f32x16 (&s_acc)[2]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s_acc[t][r] = 0.f;
+  // kt (key j * KT first), plus c0; keys past N score -inf
+  auto scores = [&](int j, const unsigned char* kt, const f32x16& c0, f32x16 (&s_acc)[2]) {
     // the K fragments of k-step s + 1 are read while step s multiplies
     bf16x8 kf[2][2];
     auto read_k = [&](int s, bf16x8 (&dst)[2]) {
@@ -254,7 +252,8 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        s_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][t], Qf[s], s_acc[t], 0, 0, 0);
+        s_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][t], Qf[s], s == 0 ? c0 : s_acc[t],
+                                                           0, 0, 0);
     });
     const int kbase = j * Cf::KT;
     if (kbase + Cf::KT > a.N) {
@@ -264,6 +263,10 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
         for (int r = 0; r < 16; ++r)
           if (kbase + 32 * t + 8 * (r >> 2) + 4 * G + (r & 3) >= a.N) s_acc[t][r] = -INFINITY;
     }
+  };
+
+  // the query's maximum over the tile (both lanes of the query)
+  auto tile_max = [&](const f32x16 (&s_acc)[2]) {
     float mt = s_acc[0][0];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -272,11 +275,10 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
     return fmaxf(mt, __shfl_xor(mt, 32));
   };
 
-  // weights exp2(s - m) into O^T += V^T P^T; returns their sum over the
-  // lane's 32 keys
-  auto weigh = [&](const unsigned char* vt, const f32x16 (&s_acc)[2], float m, f32x16 (&acc)[ND]) {
+  // weights exp2(s - m) as the B operands of the value MFMAs; returns their
+  // sum over the lane's 32 keys
+  auto weights = [&](const f32x16 (&s_acc)[2], float m, bf16x8 (&Pb)[4]) {
     float psum = 0.f;
-    bf16x8 Pb[4];
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
       const int t = s2 >> 1, r0 = 8 * (s2 & 1);
@@ -290,65 +292,91 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
       }
       Pb[s2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
     }
+    return psum;
+  };
+
+  f32x16 acc_o[ND];
+  // O^T += V^T P^T over the tile's values at vt
+  auto values = [&](const unsigned char* vt, const bf16x8 (&Pb)[4]) {
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
       for (int i = 0; i < ND; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(vt, i, s2), Pb[s2], acc[i], 0, 0, 0);
-    return psum;
+        acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(vt, i, s2), Pb[s2], acc_o[i], 0, 0, 0);
   };
 
   const int ntiles = (a.N + Cf::KT - 1) / Cf::KT;
-  f32x16 acc_o[ND];
-  float m_run, l_run;
+  f32x16 zero16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
+  float l_run;
 
-  // Main pass: every tile's weights are taken against one reference, tile
-  // 0's maximum of the query, so the accumulators are never rescaled.  A
-  // tile whose maximum passes the reference by more than kFixedSpan (weights
-  // past 2^64) flags the block, which then runs the online-rescale pass.
-  load_tile(0, stage0);
+  // Main pass.  Every tile's weights are taken against one reference, tile
+  // 0's maximum of the query, which enters the score MFMAs as their initial
+  // accumulator, so the accumulators are never rescaled.  A tile whose
+  // weights pass 2^64 on some lane (only possible when its maximum passes the
+  // reference by more than 64 log2 units) flags the block, which then runs
+  // the online-rescale pass.
+  //   Tile j's value MFMAs run in tile j + 1, beside that tile's
+  // exponentials.  K(j + 1) is loaded at the start of tile j, V(j + 1) after
+  // its closing barrier, into the buffer V(j - 1) has just left.
+  load_k(0, kbuf0);
+  load_v(0, vbuf0);
+  dma_tile<D, Cf::VG>(rv, vbuf1, kOob, 0, tokstride, wave);  // V(-1): zeros
   __syncthreads();
+  f32x16 cref;
   {
     f32x16 s_acc[2];
-    m_run = scores(0, stage0, s_acc);
+    scores(0, kbuf0, zero16, s_acc);
+    const float m_ref = tile_max(s_acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cref[r] = -m_ref;
   }
 #pragma unroll
-  for (int i = 0; i < ND; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.f;
+  for (int i = 0; i < ND; ++i) acc_o[i] = zero16;
   l_run = 0.f;
   bool over = false;
-  auto fixed_tile = [&](int j, const unsigned char* kt, unsigned char* next) {
-    load_tile(j + 1, next);   // past the last tile: zeros, never read
+  bf16x8 Pp[4];  // the previous tile's weights (none before tile 0)
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) Pp[s2] = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
+  auto fixed_tile = [&](int j, const unsigned char* kcur, unsigned char* knext, unsigned char* vprev) {
+    load_k(j + 1, knext);   // past the last tile: zeros, never read
     f32x16 s_acc[2];
-    const float mt = scores(j, kt, s_acc);
-    over |= mt > m_run + Cf::kFixedSpan;
-    l_run += weigh(kt + Cf::K_BYTES, s_acc, m_run, acc_o);
-    // the next tile is in LDS and every wave is done with this one (the
-    // compiler sees this wait, so it does not wait again before reading)
+    scores(j, kcur, cref, s_acc);
+    values(vprev, Pp);
+    const float ps = weights(s_acc, 0.f, Pp);
+    over |= !(ps <= 0x1p64f);
+    l_run += ps;
+    // K(j + 1) and V(j) are in LDS, and every wave is done with K(j) and
+    // V(j - 1) (the compiler sees this wait, so it does not wait again
+    // before reading)
     __syncthreads();
+    load_v(j + 1, vprev);
   };
   // two tiles per trip, so each names its buffers statically; an odd count
   // runs one more tile whose keys all lie past N (masked: no weight)
   for (int j = 0; j < ntiles; j += 2) {
-    fixed_tile(j, stage0, stage1);
-    fixed_tile(j + 1, stage1, stage0);
+    fixed_tile(j, kbuf0, kbuf1, vbuf1);
+    fixed_tile(j + 1, kbuf1, kbuf0, vbuf0);
   }
+  values(vbuf1, Pp);  // the last tile's values (odd index: V buffer 1)
+  __syncthreads();    // no load in flight
 
   if (__syncthreads_or(over)) {
     // Online-rescale pass: the running maximum moves (and the accumulators
     // are rescaled) only when some query's tile maximum passes it by more
     // than kLazyMax.
 #pragma unroll
-    for (int i = 0; i < ND; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.f;
-    m_run = -INFINITY;
+    for (int i = 0; i < ND; ++i) acc_o[i] = zero16;
+    float m_run = -INFINITY;
     l_run = 0.f;
-    auto lazy_tile = [&](int j, const unsigned char* kt, unsigned char* next) {
-      load_tile(j + 1, next);
+    auto lazy_tile = [&](int j, const unsigned char* kt, const unsigned char* vt, unsigned char* knext,
+                         unsigned char* vnext) {
+      load_k(j + 1, knext);
+      load_v(j + 1, vnext);
       f32x16 s_acc[2];
-      const float mt = scores(j, kt, s_acc);
+      scores(j, kt, zero16, s_acc);
+      const float mt = tile_max(s_acc);
       if (__any(mt > m_run + Cf::kLazyMax)) {
         const float m_new = fmaxf(m_run, mt);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -359,14 +387,17 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc_o[i][r] *= alpha;
       }
-      l_run += weigh(kt + Cf::K_BYTES, s_acc, m_run, acc_o);
+      bf16x8 Pb[4];
+      l_run += weights(s_acc, m_run, Pb);
+      values(vt, Pb);
       __syncthreads();
     };
-    load_tile(0, stage0);
+    load_k(0, kbuf0);
+    load_v(0, vbuf0);
     __syncthreads();
     for (int j = 0; j < ntiles; j += 2) {
-      lazy_tile(j, stage0, stage1);
-      lazy_tile(j + 1, stage1, stage0);
+      lazy_tile(j, kbuf0, vbuf0, kbuf1, vbuf1);
+      lazy_tile(j + 1, kbuf1, vbuf1, kbuf0, vbuf0);
     }
   }
 
