@@ -140,20 +140,25 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int lane, uint32_t tokstride
   return (uint32_t)q * tokstride + headoff + 16u * (uint32_t)(pc ^ (SW * q));
 }
 
-// The wave's GPW groups of one tensor's tile (keys n0 ..): group I holds rows
-// RPG I .. RPG I + RPG - 1 at dst + I * GP.  Rows past N lie outside the
-// slab and load zeros.  Completion is tracked by vmcnt.
+// Group ii of the wave's GPW groups of one tensor's tile (keys n0 ..):
+// group I = wave GPW + ii holds rows RPG I .. RPG I + RPG - 1 at dst + I GP.
+// Rows past N lie outside the slab and load zeros.  Completion is tracked
+// by vmcnt.
+template <int D, int GP>
+__device__ __forceinline__ void dma_group(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t lane_off,
+                                          int n0, uint32_t tokstride, int wave, int ii) {
+  using Cf = FaCfg<D>;
+  const int I = wave * Cf::GPW + ii;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + I * GP), 16,
+                                           lane_off + (uint32_t)(n0 + Cf::RPG * I) * tokstride, 0, 0, 0);
+}
+
+// All of the wave's groups of one tensor's tile.
 template <int D, int GP>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t lane_off,
                                          int n0, uint32_t tokstride, int wave) {
-  using Cf = FaCfg<D>;
-  const int I0 = wave * Cf::GPW;
-  const uint32_t row_off = (uint32_t)(n0 + Cf::RPG * I0) * tokstride;
 #pragma unroll
-  for (int ii = 0; ii < Cf::GPW; ++ii)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (lds_void*)(dst + (I0 + ii) * GP), 16,
-        lane_off + row_off + (uint32_t)(ii * Cf::RPG) * tokstride, 0, 0, 0);
+  for (int ii = 0; ii < FaCfg<D>::GPW; ++ii) dma_group<D, GP>(r, dst, lane_off, n0, tokstride, wave, ii);
 }
 
 template <int D>
@@ -233,8 +238,9 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
   };
 
   // scores of keys 32 t + (8 (r/4) + 4 G + r % 4), t = 0, 1, of the tile at
-  // kt (key j * KT first), plus c0; keys past N score -inf
-  auto scores = [&](int j, const unsigned char* kt, const f32x16& c0, f32x16 (&s_acc)[2]) {
+  // kt (key j * KT first), plus c0; keys past N score -inf.  io(s) runs at
+  // k-step s (it issues loads).
+  auto scores = [&](int j, const unsigned char* kt, const f32x16& c0, f32x16 (&s_acc)[2], auto&& io) {
     // the K fragments of k-step s + 1 are read while step s multiplies
     bf16x8 kf[2][2];
     auto read_k = [&](int s, bf16x8 (&dst)[2]) {
@@ -249,6 +255,7 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
     static_for<KS>([&](auto S) {
       constexpr int s = decltype(S)::value;
       if constexpr (s + 1 < KS) read_k(s + 1, kf[(s + 1) & 1]);
+      io(S);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -318,16 +325,18 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
   // reference by more than 64 log2 units) flags the block, which then runs
   // the online-rescale pass.
   //   Tile j's value MFMAs run in tile j + 1, beside that tile's
-  // exponentials.  K(j + 1) is loaded at the start of tile j, V(j + 1) after
-  // its closing barrier, into the buffer V(j - 1) has just left.
+  // exponentials.  Tile j loads K(j + 1) and V(j), one 1 KB group per score
+  // k-step: K(j + 1) into the buffer K(j - 1) left in tile j - 1, V(j) into
+  // the one V(j - 2) left there; its closing barrier waits for both.
+  static_assert(KS == 2 * Cf::GPW, "one load group per score k-step");
+  auto no_io = [](auto) {};
   load_k(0, kbuf0);
-  load_v(0, vbuf0);
   dma_tile<D, Cf::VG>(rv, vbuf1, kOob, 0, tokstride, wave);  // V(-1): zeros
   __syncthreads();
   f32x16 cref;
   {
     f32x16 s_acc[2];
-    scores(0, kbuf0, zero16, s_acc);
+    scores(0, kbuf0, zero16, s_acc, no_io);
     const float m_ref = tile_max(s_acc);
 #pragma unroll
     for (int r = 0; r < 16; ++r) cref[r] = -m_ref;
@@ -339,25 +348,36 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
   bf16x8 Pp[4];  // the previous tile's weights (none before tile 0)
 #pragma unroll
   for (int s2 = 0; s2 < 4; ++s2) Pp[s2] = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
-  auto fixed_tile = [&](int j, const unsigned char* kcur, unsigned char* knext, unsigned char* vprev) {
-    load_k(j + 1, knext);   // past the last tile: zeros, never read
+  auto fixed_tile = [&](int j, const unsigned char* kcur, unsigned char* knext, unsigned char* vcur,
+                        const unsigned char* vprev) {
+    // past the last tile the loads read zeros, never used
+    auto io = [&](auto S) {
+      constexpr int st = decltype(S)::value;
+      if constexpr (st < Cf::GPW)
+        dma_group<D, Cf::KG>(rk, knext, klane, (j + 1) * Cf::KT, tokstride, wave, st);
+      else
+        dma_group<D, Cf::VG>(rv, vcur, vlane, j * Cf::KT, tokstride, wave, st - Cf::GPW);
+    };
     f32x16 s_acc[2];
-    scores(j, kcur, cref, s_acc);
+    scores(j, kcur, cref, s_acc, io);
     values(vprev, Pp);
     const float ps = weights(s_acc, 0.f, Pp);
     over |= !(ps <= 0x1p64f);
     l_run += ps;
+    // the weights are due before the barrier, beside the value MFMAs (else
+    // the compiler sinks them to their use in the next tile)
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) asm volatile("" ::"v"(Pp[s2]));
     // K(j + 1) and V(j) are in LDS, and every wave is done with K(j) and
     // V(j - 1) (the compiler sees this wait, so it does not wait again
     // before reading)
     __syncthreads();
-    load_v(j + 1, vprev);
   };
   // two tiles per trip, so each names its buffers statically; an odd count
   // runs one more tile whose keys all lie past N (masked: no weight)
   for (int j = 0; j < ntiles; j += 2) {
-    fixed_tile(j, kbuf0, kbuf1, vbuf1);
-    fixed_tile(j + 1, kbuf1, kbuf0, vbuf0);
+    fixed_tile(j, kbuf0, kbuf1, vbuf0, vbuf1);
+    fixed_tile(j + 1, kbuf1, kbuf0, vbuf1, vbuf0);
   }
   values(vbuf1, Pp);  // the last tile's values (odd index: V buffer 1)
   __syncthreads();    // no load in flight
@@ -375,7 +395,7 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
       load_k(j + 1, knext);
       load_v(j + 1, vnext);
       f32x16 s_acc[2];
-      scores(j, kt, zero16, s_acc);
+      scores(j, kt, zero16, s_acc, no_io);
       const float mt = tile_max(s_acc);
       if (__any(mt > m_run + Cf::kLazyMax)) {
         const float m_new = fmaxf(m_run, mt);
