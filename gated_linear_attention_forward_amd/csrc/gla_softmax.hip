@@ -191,9 +191,19 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
   // the wave's queries as the B operand: query q0 + col, dims 16 s + 8 G
   const int qn = blockIdx.x * Cf::QB + 32 * wave + col;
   const uint32_t qoff = qn < a.N ? (uint32_t)qn * tokstride + headoff + 16u * G : kOob;
+  // they stay in accumulation registers (the MFMA reads its B operand from
+  // there), which leaves the vector registers to the fragments in flight
   bf16x8 Qf[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) Qf[s] = __builtin_bit_cast(bf16x8, load16(rq, qoff + 32u * s));
+  for (int s = 0; s < KS; ++s) {
+    const u32x4 v = load16(rq, qoff + 32u * s);
+    uint32_t w0, w1, w2, w3;
+    asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w0) : "v"(v[0]));
+    asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w1) : "v"(v[1]));
+    asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w2) : "v"(v[2]));
+    asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(w3) : "v"(v[3]));
+    Qf[s] = __builtin_bit_cast(bf16x8, (u32x4){w0, w1, w2, w3});
+  }
 
   // K and V tiles go straight to LDS (no staging registers)
   const uint32_t klane = dma_lane_offset<D, Cf::KSW>(lane, tokstride, headoff);
@@ -256,6 +266,7 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
       constexpr int s = decltype(S)::value;
       if constexpr (s + 1 < KS) read_k(s + 1, kf[(s + 1) & 1]);
       io(S);
+      asm volatile("" : "+a"(Qf[s]));  // read in place from the accumulation registers
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
