@@ -122,6 +122,7 @@ struct FaCfg {
   // a running maximum that trails a tile's maximum by at most this much (in
   // log2 units) is kept: the weights stay below 2^8, and the accumulators
   // are rescaled only when the maximum really moves
+  static constexpr int KPF = 2;    // k-steps the K fragment reads run ahead
   static constexpr float kLazyMax = 8.f;
   // how far (log2 units) a tile's maximum may pass the fixed reference of
   // the main pass: weights up to 2^64, sums over < 2^31 keys stay far below
@@ -251,8 +252,9 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
   // kt (key j * KT first), plus c0; keys past N score -inf.  io(s) runs at
   // k-step s (it issues loads).
   auto scores = [&](int j, const unsigned char* kt, const f32x16& c0, f32x16 (&s_acc)[2], auto&& io) {
-    // the K fragments of k-step s + 1 are read while step s multiplies
-    bf16x8 kf[2][2];
+    // the K fragments of k-step s + KPF are read while step s multiplies
+    constexpr int KPF = Cf::KPF;
+    bf16x8 kf[KPF + 1][2];
     auto read_k = [&](int s, bf16x8 (&dst)[2]) {
       const int c = 2 * s;  // the lane adds G
       const int off = 16 * (c % Cf::KSW + Cf::KSW * RPG * (c / (Cf::KSW * RPG)));
@@ -261,16 +263,16 @@ void flash_kernel(KArgs a, const uint16_t* qr, const uint16_t* kr) {
       for (int t = 0; t < 2; ++t)
         dst[t] = *reinterpret_cast<const bf16x8*>(kt + base + t * (32 / RPG) * Cf::KG + off);
     };
-    read_k(0, kf[0]);
+    static_for<KPF>([&](auto S) { read_k(decltype(S)::value, kf[decltype(S)::value]); });
     static_for<KS>([&](auto S) {
       constexpr int s = decltype(S)::value;
-      if constexpr (s + 1 < KS) read_k(s + 1, kf[(s + 1) & 1]);
+      if constexpr (s + KPF < KS) read_k(s + KPF, kf[(s + KPF) % (KPF + 1)]);
       io(S);
       asm volatile("" : "+a"(Qf[s]));  // read in place from the accumulation registers
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        s_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][t], Qf[s], s == 0 ? c0 : s_acc[t],
+        s_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % (KPF + 1)][t], Qf[s], s == 0 ? c0 : s_acc[t],
                                                            0, 0, 0);
     });
     const int kbase = j * Cf::KT;
