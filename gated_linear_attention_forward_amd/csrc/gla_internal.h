@@ -118,7 +118,7 @@ struct PArgs {
 hipError_t launch_proj(const Plan& p, KArgs akv, KArgs aqg, PArgs pa, hipStream_t stream);
 // The reduce kernel alone over the state partials in a.part.
 hipError_t launch_reduce_state(const Plan& p, KArgs a, hipStream_t stream);
-constexpr int kProjTileTokens = 128;
+constexpr int kProjTileTokens = 256;
 
 // Tile sizes the plan has to respect.
 constexpr int kOutputTileTokens = 64;

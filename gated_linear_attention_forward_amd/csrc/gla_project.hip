@@ -8,20 +8,19 @@
 // row j of a map is output feature j, contiguous over C).  Each map is
 // y = x W^T, rounded to bf16 as a BF16 model stores it.
 //
-// Both kernels run the same GEMM main loop on a tile of TM = 128 tokens of
+// Both kernels run the same GEMM main loop on a tile of TM = 256 tokens of
 // one batch element and the 2 D output features of one head in two maps
 // (k and v, or q and g) on v_mfma_f32_32x32x16_bf16 (A = x rows, B = W rows:
 // both operands are contiguous over C).  At D >= 64 a block has 8 waves, two
-// per SIMD, each computing 64 tokens x 2D/4 features (64 accumulation
-// registers, so the state accumulators of the kv kernel fit beside them);
-// at D = 32, 4 waves of 64 x 32.  Per K-step of 64 the x tile (128 x 64) and
-// the W tile (2 D x 64) go through registers into one of two LDS stages
-// while the other stage is multiplied.
+// per SIMD, each computing 128 tokens x 2D/4 features (128 accumulation
+// registers at D = 128); at D = 32, 4 waves of 128 x 32.  Per K-step of 64
+// the x tile (256 x 64) and the W tile (2 D x 64) load straight into one of
+// two LDS stages while the other stage is multiplied.
 //
 //   kv kernel  one block per (state chunk, head), looping over the chunk's
 //              tiles; after each tile's GEMM: bf16(k) with ReLU and bf16(v)
 //              to feature-major LDS tiles, the rotation applied in place
-//              (each thread owns four tokens and every sixteenth pair) while z
+//              (each thread owns four tokens and every PGS-th pair) while z
 //              accumulates the unrotated features, then S += rk^T v over the
 //              tile's tokens on MFMA (each wave owns an eighth of S's 32x32
 //              tiles at D = 128); at the end the block writes the same fp32 (S_c, z_c)
@@ -40,41 +39,43 @@ namespace {
 template <int D>
 struct ProjCfg {
   static constexpr int TM = kProjTileTokens;  // tokens per tile
-  static constexpr int KT = 64;               // K per stage
-  static constexpr int AP = KT * 2 + 16;      // stage row pitch (bytes)
-  static constexpr int A_BYTES = TM * AP;
-  static constexpr int B_BYTES = 2 * D * AP;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int KT = 64;               // K per stage (128 bytes of a row)
+  // A stage holds the x tile (TM rows) and the W tile (2 D rows) in 1 KB
+  // load groups of 8 rows of 128 bytes, each group padded by 64 bytes; row q
+  // of a group stores its 16-byte chunk c at position c ^ (q / 2).  The 16
+  // rows a 16-lane fragment read touches then fall in 16 distinct bank
+  // groups, and one buffer-load-to-LDS instruction fills one group.
+  static constexpr int GP = 1024 + 64;
+  static constexpr int AG = TM / 8;           // x groups per stage
+  static constexpr int BG = 2 * D / 8;        // W groups per stage
+  static constexpr int A_BYTES = AG * GP;
+  static constexpr int STAGE = (AG + BG) * GP;
   // 8 waves (two per SIMD) where a wave still gets 32 columns, else 4
   static constexpr int NW = D >= 64 ? 8 : 4;
   static constexpr int NT = 64 * NW;
-  static constexpr int WN = NW / 2;           // column groups (two row groups of 64 tokens)
+  static constexpr int WN = NW / 2;           // column groups (two row groups of TM / 2 tokens)
   static constexpr int WC = 2 * D / WN;       // columns per wave
-  static constexpr int MI = 2;                // 32-row subtiles per wave (64 tokens)
+  static constexpr int WT = TM / 2;           // tokens per wave
+  static constexpr int MI = WT / 32;          // 32-row subtiles per wave
   static constexpr int NI = WC / 32;          // 32-column subtiles per wave
-  static constexpr int ACH = TM * (KT / 8) / NT;       // 16-byte x chunks per thread
-  static constexpr int BCH = 2 * D * (KT / 8) / NT;    // 16-byte W chunks per thread
+  static constexpr int GPW = (AG + BG) / NW;  // load groups per wave and stage
   // kv epilogue: feature-major tiles [D][TM] of R phi(k) and v
   static constexpr int FP = TM * 2 + 16;
   static constexpr int KV_BYTES = 2 * D * FP;
   static constexpr int ST = (D / 32) * (D / 32);        // 32x32 tiles of S
   static constexpr int STW = (ST + NW - 1) / NW;        // per wave
-  static constexpr int PGS = NT / 32;                   // pair groups of the rotation pass
+  static constexpr int TQ = TM / 4;                     // token quads of the rotation pass
+  static constexpr int PGS = NT / TQ;                   // pair groups of the rotation pass
   // qg epilogue: token-major tile [TM][2 D]
   static constexpr int QP = 4 * D + 16;
   static constexpr int QG_BYTES = TM * QP;
   static constexpr int LDS_BYTES = 2 * STAGE;
   static_assert(KV_BYTES <= LDS_BYTES && QG_BYTES <= LDS_BYTES, "epilogue tiles fit the stages");
-  static_assert(ACH >= 1 && BCH >= 1 && NI >= 1, "one chunk per thread, a 32-column subtile");
-  static_assert(D / 2 % PGS == 0, "pairs split evenly over the pair groups");
+  static_assert((AG + BG) % NW == 0, "whole load groups per wave");
+  static_assert(NI >= 1 && MI >= 1 && D % 8 == 0, "a 32-column subtile, whole groups per map");
+  static_assert(TQ <= 64 && NT % TQ == 0 && D / 2 % PGS == 0, "pairs split evenly over the pair groups");
+  static_assert(LDS_BYTES + kMaxLdsTableBytes <= 160 * 1024, "stages and the RoPE table fit the LDS");
 };
-
-// Block barrier for LDS hand-offs: every wave's LDS writes are complete
-// before any wave passes; global loads in flight keep flying (a plain
-// __syncthreads would also wait for them, defeating the prefetch).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 struct Gemm {
   __amdgpu_buffer_rsrc_t rx, rw;
@@ -83,99 +84,90 @@ struct Gemm {
   int wrow0, wrow1;    // first W row of the two maps' head slices
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 // The main loop: acc[mi][ni] += x[tile rows] W[cols]^T over the whole of C.
-// Wave (wm, wn) computes tokens 64 wm .. + 64 and columns WC wn .. + WC of
-// the tile's 2 D columns (the first D are map 0, the rest map 1).
+// Wave (wm, wn) computes tokens WT wm .. + WT and columns WC wn .. + WC of
+// the tile's 2 D columns (the first D are map 0, the rest map 1).  The next
+// stage's groups load straight into LDS while this stage is multiplied
+// (spread over its 16-wide k-steps); past the last K-step the offsets lie
+// outside the buffers and load zeros, and an odd step count runs one extra
+// step over a zero stage, which adds exactly nothing.
 template <int D>
 __device__ __forceinline__ void gemm_tile(const Gemm& gm, int tile0, int Cdim, unsigned char* smem,
-                                          f32x16 (&acc)[2][ProjCfg<D>::NI]) {
+                                          f32x16 (&acc)[ProjCfg<D>::MI][ProjCfg<D>::NI]) {
   using Cf = ProjCfg<D>;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int MI = Cf::MI, NI = Cf::NI, GP = Cf::GP;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
-  for (int mi = 0; mi < Cf::MI; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < Cf::NI; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  // two register sets: the loads of K-step kt + 2 are in flight while step
-  // kt is multiplied and step kt + 1 goes into LDS.  Every step issues its
-  // loads and LDS writes unconditionally (past the last K-step the offsets
-  // lie outside the buffers, which load zeros without touching memory), so
-  // the count of loads in flight is the same on every path and each wait is
-  // for the older register set only; an odd step count runs one extra step
-  // over a zero stage, which adds exactly nothing.
-  u32x4 ra[2][Cf::ACH], rb[2][Cf::BCH];
-  auto gload = [&](auto SET, int k0, bool valid) {
-    constexpr int st = decltype(SET)::value;
-#pragma unroll
-    for (int i = 0; i < Cf::ACH; ++i) {
-      const int c = tid + Cf::NT * i, row = c >> 3, col = c & 7;
-      const int n = tile0 + row;
-      const uint32_t off = (valid && n < gm.n_tile_end)
-                               ? (uint32_t)n * gm.x_row + (uint32_t)(k0 + 8 * col) * 2u
-                               : kOob;
-      ra[st][i] = load16(gm.rx, off);
-    }
-#pragma unroll
-    for (int i = 0; i < Cf::BCH; ++i) {
-      const int c = tid + Cf::NT * i, row = c >> 3, col = c & 7;
-      const int wr = (row < D ? gm.wrow0 : gm.wrow1 - D) + row;
-      const uint32_t off = valid ? (uint32_t)wr * gm.x_row + (uint32_t)(k0 + 8 * col) * 2u : kOob;
-      rb[st][i] = load16(gm.rw, off);
-    }
+  // load side: lane i fills row q = i / 8 of a group with chunk (i % 8) ^ (q / 2)
+  const int lq = lane >> 3;
+  const uint32_t lchunk = 16u * (uint32_t)((lane & 7) ^ (lq >> 1));
+  auto issue = [&](int i, int k0, bool valid, unsigned char* stg) {
+    const int g = wave * Cf::GPW + i;  // wave-uniform
+    const bool isx = g < Cf::AG;
+    const int n = tile0 + 8 * g + lq;
+    const int row = 8 * (g - Cf::AG) + lq;
+    const int wr = (row < D ? gm.wrow0 : gm.wrow1 - D) + row;
+    const uint32_t xo = (valid && n < gm.n_tile_end) ? (uint32_t)n * gm.x_row : kOob;
+    const uint32_t wo = valid ? (uint32_t)wr * gm.x_row : kOob;
+    const uint32_t off = (isx ? xo : wo) + (uint32_t)k0 * 2u + lchunk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isx ? gm.rx : gm.rw, (lds_void*)(stg + g * GP), 16, off,
+                                             0, 0, 0);
   };
-  auto lwrite = [&](auto SET, unsigned char* stg) {
-    constexpr int st = decltype(SET)::value;
-#pragma unroll
-    for (int i = 0; i < Cf::ACH; ++i) {
-      const int c = tid + Cf::NT * i;
-      *reinterpret_cast<u32x4*>(stg + (c >> 3) * Cf::AP + 16 * (c & 7)) = ra[st][i];
-    }
-#pragma unroll
-    for (int i = 0; i < Cf::BCH; ++i) {
-      const int c = tid + Cf::NT * i;
-      *reinterpret_cast<u32x4*>(stg + Cf::A_BYTES + (c >> 3) * Cf::AP + 16 * (c & 7)) = rb[st][i];
-    }
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
+  // read side: row r, chunk c at (r / 8) GP + (r % 8) 128 + 16 (c ^ (r % 8 / 2)).
+  // The lane's rows have r % 8 = l % 8; its chunk is 2 ks + l / 32, so the
+  // swizzle moves it by +-2 chunks depending on the parity of ks: two bases.
+  const int q = lane & 7, sw = q >> 1, kh = lane >> 5;
+  const int lo = kh ^ (sw & 1), hi = sw >> 1;
+  const int rbase = q * 128 + 16 * lo;
+  const int base_even = rbase + 32 * hi, base_odd = rbase - 32 * hi;
+  const int arow = Cf::WT * wm + (lane & 31), brow = Cf::WC * wn + (lane & 31);
+  const int a_grp = (arow >> 3) * GP, b_grp = Cf::A_BYTES + (brow >> 3) * GP;
+
   const int nk = Cdim / Cf::KT;
-  gload(S0{}, 0, true);
-  gload(S1{}, Cf::KT, nk > 1);
-  lwrite(S0{}, smem);
-  lds_barrier();
-  const int arow = 64 * wm + (lane & 31), brow = Cf::WC * wn + (lane & 31);
-  const int kb = 16 * (lane >> 5);  // byte offset of the lane's 8 k values in a 16-wide step
-  // step kt (P = kt % 2): refill set P with step kt + 2, multiply stage P,
-  // move set 1 - P (step kt + 1) into stage 1 - P
+#pragma unroll
+  for (int i = 0; i < Cf::GPW; ++i) issue(i, 0, true, smem);
+  __syncthreads();
+  // step kt (P = kt % 2): multiply stage P while stage 1 - P loads step kt + 1
   auto step = [&](auto PAR, int kt) {
     constexpr int P = decltype(PAR)::value;
-    gload(std::integral_constant<int, P>{}, (kt + 2) * Cf::KT, kt + 2 < nk);
     const unsigned char* st = smem + P * Cf::STAGE;
+    unsigned char* nx = smem + (1 - P) * Cf::STAGE;
+    const bool valid = kt + 1 < nk;
+    static_for<Cf::KT / 16>([&](auto KS) {
+      constexpr int ks = decltype(KS)::value;
+      constexpr int g0 = ks * Cf::GPW / (Cf::KT / 16), g1 = (ks + 1) * Cf::GPW / (Cf::KT / 16);
 #pragma unroll
-    for (int ks = 0; ks < Cf::KT / 16; ++ks) {
-      bf16x8 A[Cf::MI], Bm[Cf::NI];
+      for (int i = g0; i < g1; ++i) issue(i, (kt + 1) * Cf::KT, valid, nx);
+      const int kbase = ((ks & 1) ? base_odd : base_even) + 32 * ks;
+      bf16x8 A[MI], Bm[NI];
 #pragma unroll
-      for (int mi = 0; mi < Cf::MI; ++mi)
-        A[mi] = *reinterpret_cast<const bf16x8*>(st + (arow + 32 * mi) * Cf::AP + 32 * ks + kb);
+      for (int mi = 0; mi < MI; ++mi)
+        A[mi] = *reinterpret_cast<const bf16x8*>(st + a_grp + 4 * mi * GP + kbase);
 #pragma unroll
-      for (int ni = 0; ni < Cf::NI; ++ni)
-        Bm[ni] = *reinterpret_cast<const bf16x8*>(st + Cf::A_BYTES + (brow + 32 * ni) * Cf::AP +
-                                                  32 * ks + kb);
+      for (int ni = 0; ni < NI; ++ni)
+        Bm[ni] = *reinterpret_cast<const bf16x8*>(st + b_grp + 4 * ni * GP + kbase);
 #pragma unroll
-      for (int mi = 0; mi < Cf::MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < Cf::NI; ++ni)
+        for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mi], Bm[ni], acc[mi][ni], 0, 0, 0);
-    }
-    lwrite(std::integral_constant<int, 1 - P>{}, smem + (1 - P) * Cf::STAGE);
-    lds_barrier();
+    });
+    // the next stage has landed and every wave is done with this one
+    __syncthreads();
   };
   for (int kt = 0; kt < nk; kt += 2) {
-    step(S0{}, kt);
-    step(S1{}, kt + 1);
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
   }
 }
 
@@ -222,24 +214,24 @@ void proj_kv_kernel(KArgs a, PArgs pa) {
   float zacc[NPG][2];
 #pragma unroll
   for (int i = 0; i < NPG; ++i) zacc[i][0] = zacc[i][1] = 0.f;
-  const int tq = tid & 31, pg = tid >> 5;
+  const int tq = tid % Cf::TQ, pg = tid / Cf::TQ;
   // this wave's columns: map (0: k, 1: v) and first feature
   const int wmap = (Cf::WC * wn) / D, wf0 = (Cf::WC * wn) % D;
 
   for (int tile0 = n_begin; tile0 < n_end; tile0 += TM) {
-    f32x16 acc[2][Cf::NI];
+    f32x16 acc[Cf::MI][Cf::NI];
     gemm_tile<D>(gm, tile0, pa.Cdim, smem, acc);
     // bf16 phi(k) and bf16 v, feature-major: lane column = feature, four
     // consecutive tokens per accumulator quarter
     unsigned char* dst = wmap ? vtile : ktile;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < Cf::MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < Cf::NI; ++ni)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int f = wf0 + 32 * ni + (lane & 31);
-          const int t = 64 * wm + 32 * mi + 8 * rg + 4 * (lane >> 5);
+          const int t = Cf::WT * wm + 32 * mi + 8 * rg + 4 * (lane >> 5);
           float y[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -324,14 +316,14 @@ void proj_kv_kernel(KArgs a, PArgs pa) {
       }
     }
   }
-  // z: the 32 threads of a pair group hold the same features
+  // z: the TQ threads of a pair group hold the same features
 #pragma unroll
   for (int i = 0; i < NPG; ++i)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       float s = zacc[i][hf];
 #pragma unroll
-      for (int msk = 1; msk < 32; msk *= 2) s += __shfl_xor(s, msk);
+      for (int msk = 1; msk < Cf::TQ; msk *= 2) s += __shfl_xor(s, msk);
       if (tq == 0) dstp[D * D + 2 * (pg + PGS * i) + hf] = s;
     }
 }
@@ -362,16 +354,16 @@ void proj_qg_kernel(KArgs a, PArgs pa) {
   gm.wrow0 = 0 * HD + h * D;  // q
   gm.wrow1 = 3 * HD + h * D;  // g
 
-  f32x16 acc[2][Cf::NI];
+  f32x16 acc[Cf::MI][Cf::NI];
   gemm_tile<D>(gm, n_begin, pa.Cdim, smem, acc);
   // token-major tile: row t holds q (D bf16) then g (D bf16)
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < Cf::MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < Cf::NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = 64 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int t = Cf::WT * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int f = Cf::WC * wn + 32 * ni + (lane & 31);
         const __bf16 y = (__bf16)acc[mi][ni][r];
         *reinterpret_cast<__bf16*>(smem + t * QP + 2 * f) = y;
