@@ -111,17 +111,23 @@ __device__ __forceinline__ void gemm_tile(const Gemm& gm, int tile0, int Cdim, u
   // load side: lane i fills row q = i / 8 of a group with chunk (i % 8) ^ (q / 2)
   const int lq = lane >> 3;
   const uint32_t lchunk = 16u * (uint32_t)((lane & 7) ^ (lq >> 1));
-  auto issue = [&](int i, int k0, bool valid, unsigned char* stg) {
-    const int g = wave * Cf::GPW + i;  // wave-uniform
-    const bool isx = g < Cf::AG;
+  // the lane's offset of its chunk at K = 0 in each of the wave's groups
+  // (rows past the tile's end lie outside the buffer)
+  uint32_t goff[Cf::GPW];
+#pragma unroll
+  for (int i = 0; i < Cf::GPW; ++i) {
+    const int g = wave * Cf::GPW + i;
     const int n = tile0 + 8 * g + lq;
     const int row = 8 * (g - Cf::AG) + lq;
     const int wr = (row < D ? gm.wrow0 : gm.wrow1 - D) + row;
-    const uint32_t xo = (valid && n < gm.n_tile_end) ? (uint32_t)n * gm.x_row : kOob;
-    const uint32_t wo = valid ? (uint32_t)wr * gm.x_row : kOob;
-    const uint32_t off = (isx ? xo : wo) + (uint32_t)k0 * 2u + lchunk;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(isx ? gm.rx : gm.rw, (lds_void*)(stg + g * GP), 16, off,
-                                             0, 0, 0);
+    const uint32_t xo = n < gm.n_tile_end ? (uint32_t)n * gm.x_row : kOob;
+    goff[i] = (g < Cf::AG ? xo : (uint32_t)wr * gm.x_row) + lchunk;
+  }
+  auto issue = [&](int i, int k0, bool valid, unsigned char* stg) {
+    const int g = wave * Cf::GPW + i;  // wave-uniform
+    const uint32_t off = valid ? goff[i] + (uint32_t)k0 * 2u : kOob;
+    const __amdgpu_buffer_rsrc_t r = g < Cf::AG ? gm.rx : gm.rw;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(stg + g * GP), 16, off, 0, 0, 0);
   };
   // read side: row r, chunk c at (r / 8) GP + (r % 8) 128 + 16 (c ^ (r % 8 / 2)).
   // The lane's rows have r % 8 = l % 8; its chunk is 2 ks + l / 32, so the
