@@ -45,7 +45,7 @@ struct BwdCfg {
   static constexpr int MB = D / 16;   // 16-column blocks
   static constexpr int OB = 2 * MB;   // bytes a lane owns of one token row
   static constexpr int PU = D / 32;   // rotation pairs in those bytes
-  static constexpr int PITCH = 2 * D + 16;
+  static constexpr int PITCH = 2 * D;  // row tiles are unpadded and swizzled (row_tile_offset)
   // query kernel LDS: S^T rows + z rows, S rows, fp32 z, per-wave a tiles
   static constexpr int Q_SR = (D + 2) * PITCH;
   static constexpr int Q_ZF = Q_SR + D * PITCH;
@@ -59,13 +59,13 @@ struct BwdCfg {
   static_assert(kQueryWaves * D * 4 <= kQueryWaves * 16 * PITCH, "dz scratch fits the a tiles");
 };
 
-// Copies `rows` dense rows of D bf16 into LDS rows of PITCH bytes.
+// Copies `rows` dense rows of D bf16 into an LDS row tile.
 template <int D, int NT>
 __device__ __forceinline__ void stage_rows(unsigned char* dst, const uint16_t* src, int rows) {
   const uint4* s = reinterpret_cast<const uint4*>(src);
   for (int i = threadIdx.x; i < rows * D / 8; i += NT) {
     const int row = i / (D / 8), u = i % (D / 8);
-    *reinterpret_cast<uint4*>(dst + row * BwdCfg<D>::PITCH + 16 * u) = s[i];
+    *reinterpret_cast<uint4*>(dst + row_tile_offset<D>(row, 16 * u)) = s[i];
   }
 }
 
@@ -102,12 +102,12 @@ __device__ __forceinline__ float row_sum16(float x) {
 template <int D>
 __device__ __forceinline__ void contract_rows(const unsigned char* op, const bf16x8 (&A)[D / 32],
                                               int col, int m, f32x4 (&acc)[D / 16]) {
-  constexpr int KS = D / 32, MB = D / 16, PITCH = BwdCfg<D>::PITCH;
+  constexpr int KS = D / 32, MB = D / 16;
   bf16x8 Bf[2][KS];
   auto read_b = [&](int j, bf16x8 (&dst)[KS]) {
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2)
-      dst[s2] = *reinterpret_cast<const bf16x8*>(op + (16 * j + col) * PITCH + 16 * (4 * s2 + m));
+      dst[s2] = *reinterpret_cast<const bf16x8*>(op + row_tile_offset<D>(16 * j + col, 16 * (4 * s2 + m)));
   };
   read_b(0, Bf[0]);
   static_for<MB>([&](auto J) {
@@ -233,8 +233,8 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
     for (int s2 = 0; s2 < KS; ++s2) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) fq[s2][u] = relu2(qv[s2][u]);
-      const bf16x8 Bz =
-          *reinterpret_cast<const bf16x8*>(sS + (D + (col & 1)) * PITCH + 16 * (4 * s2 + m));
+      const bf16x8 Bz = *reinterpret_cast<const bf16x8*>(
+          sS + row_tile_offset<D>(D + (col & 1), 16 * (4 * s2 + m)));
       accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fq[s2]), Bz, accd,
                                                     0, 0, 0);
     }
@@ -280,7 +280,7 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
       const uint32_t o = r_offset(base, i);
       store_chunk_nt<OB>(rdg, o, wg);
       store_chunk_nt<OB>(ra, o, wa);
-      *reinterpret_cast<OChunk*>(at + (4 * m + i) * PITCH + OB * col) = wa;
+      *reinterpret_cast<OChunk*>(at + row_tile_offset<D>(4 * m + i, OB * col)) = wa;
     }
     issue_gd(next);
     __builtin_amdgcn_sched_barrier(0);
@@ -294,7 +294,7 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
     bf16x8 Aa[KS];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2)
-      Aa[s2] = *reinterpret_cast<const bf16x8*>(at + col * PITCH + 16 * (4 * s2 + m));
+      Aa[s2] = *reinterpret_cast<const bf16x8*>(at + row_tile_offset<D>(col, 16 * (4 * s2 + m)));
     f32x4 acc2[MB];
     contract_rows<D>(sR, Aa, col, m, acc2);
 

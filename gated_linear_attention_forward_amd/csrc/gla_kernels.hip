@@ -771,7 +771,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(KArgs a) {
 //
 // Block = 256 threads (4 waves), one (token range, head).  The head's S^T
 // (bf16, D rows of D) and the two z rows are staged in LDS once per block,
-// rows padded by 16 bytes.  Each wave computes 16 tokens per step as
+// as a swizzled row tile (row_tile_offset).  Each wave computes 16 tokens per step as
 // num = (R phi(q)) S on v_mfma_f32_16x16x32_bf16 with the tokens as the A
 // operand: lane l holds token l % 16 and, for k-step s, features
 // 32 s + 8 (l / 16) .. + 7 of it (one 16-byte global load).  The B operand
@@ -791,12 +791,11 @@ void output_kernel(KArgs a) {
   constexpr int MB = D / 16;       // 16-column blocks of the value dimension
   constexpr int OB = 2 * MB;       // output bytes per lane and token
   constexpr int OW = OB / 4;       // ... in dwords
-  constexpr int PITCH = D * 2 + 16;
   constexpr int ROWS = D + 2;
   using OChunk = typename Chunk<OB>::T;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char* sS = smem;
-  float2* ltab = reinterpret_cast<float2*>(smem + ROWS * PITCH);
+  float2* ltab = reinterpret_cast<float2*>(smem + ROWS * 2 * D);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -817,7 +816,7 @@ void output_kernel(KArgs a) {
       reinterpret_cast<const uint4*>(a.sl + ((size_t)bh * a.NB + blk) * ROWS * D);
   for (int i = tid; i < ROWS * D / 8; i += 256) {
     const int row = i / (D / 8), u = i % (D / 8);
-    *reinterpret_cast<uint4*>(sS + row * PITCH + 16 * u) = src[i];
+    *reinterpret_cast<uint4*>(sS + row_tile_offset<D>(row, 16 * u)) = src[i];
   }
   TabView tv{};
   if (ROPE) tv = stage_table<D>(a, ltab, TLDS, n_begin, n_end);
@@ -868,8 +867,8 @@ void output_kernel(KArgs a) {
     for (int s2 = 0; s2 < KS; ++s2) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) fq[s2][u] = relu2(qv[s2][u]);
-      const bf16x8 Bz =
-          *reinterpret_cast<const bf16x8*>(sS + (D + (col & 1)) * PITCH + 16 * (4 * s2 + m));
+      const bf16x8 Bz = *reinterpret_cast<const bf16x8*>(
+          sS + row_tile_offset<D>(D + (col & 1), 16 * (4 * s2 + m)));
       accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fq[s2]), Bz, accd,
                                                     0, 0, 0);
     }
@@ -886,7 +885,7 @@ void output_kernel(KArgs a) {
     auto read_b = [&](int j, bf16x8 (&dst)[KS]) {
 #pragma unroll
       for (int s2 = 0; s2 < KS; ++s2)
-        dst[s2] = *reinterpret_cast<const bf16x8*>(sS + (16 * j + col) * PITCH + 16 * (4 * s2 + m));
+        dst[s2] = *reinterpret_cast<const bf16x8*>(sS + row_tile_offset<D>(16 * j + col, 16 * (4 * s2 + m)));
     };
     read_b(0, Bf[0]);
     static_for<MB>([&](auto J) {
@@ -952,7 +951,7 @@ constexpr int state_lds_bytes() {
 }
 template <int D>
 constexpr int output_lds_bytes() {
-  return (D + 2) * (D * 2 + 16);
+  return (D + 2) * D * 2;
 }
 
 
