@@ -76,31 +76,37 @@ def cpu_baseline(w, q, k, v, g, min_seconds=10.0):
 COUNTERS = os.path.join(ROOT, "profiles", "counters_5b_720p_193f.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_linear_attention_forward_amd", "csrc", f)
                   for f in ("gla_kernels.hip", "gla_device.h", "gla_api.cpp", "gla_internal.h")]
+BWD_COUNTERS = os.path.join(ROOT, "profiles", "backward_counters_5b_720p_193f.md")
+BWD_SOURCES = [os.path.join(ROOT, "gated_linear_attention_forward_amd", "csrc", f)
+               for f in ("gla_backward.hip", "gla_kernels.hip", "gla_device.h", "gla_api.cpp",
+                         "gla_internal.h")]
 
 
-def kernel_source_digest():
+def kernel_source_digest(sources=KERNEL_SOURCES):
     """sha256 over the sources that decide the kernels and their launch shapes."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in sources:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def counter_traffic(workload_name):
-    """HBM bytes per launch of the output kernel from the committed counters,
-    if they were taken on this workload and on the current kernel source."""
-    if workload_name != "5b_720p_193f" or not os.path.exists(COUNTERS):
+def counter_traffic(workload_name, path=COUNTERS, field="output_kernel_traffic_bytes",
+                    sources=KERNEL_SOURCES):
+    """HBM bytes (FETCH_SIZE + WRITE_SIZE, scaled by a calibration copy) from
+    a committed counter summary, if it was taken on this workload (5B
+    720p/193f) and on the current kernel sources."""
+    if workload_name != "5b_720p_193f" or not os.path.exists(path):
         return None, "no counters for this workload"
     fields = {}
-    with open(COUNTERS) as f:
+    with open(path) as f:
         for line in f:
             key, sep, val = line.partition(":")
-            if sep and key.strip() in ("kernel_source_sha256", "output_kernel_traffic_bytes"):
+            if sep and key.strip() in ("kernel_source_sha256", field):
                 fields[key.strip()] = val.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_digest():
+    if fields.get("kernel_source_sha256") != kernel_source_digest(sources):
         return None, "kernel source changed since the counters were taken"
-    return float(fields["output_kernel_traffic_bytes"]), os.path.relpath(COUNTERS, ROOT)
+    return float(fields[field]), os.path.relpath(path, ROOT)
 
 
 def copy_calibration(dev, nbytes=1 << 30):
@@ -333,6 +339,8 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
     units = w.B * w.N * w.H
     nbytes = 18 * w.D * units
     achieved = nbytes / (ev_ms * 1e-3) / 1e9
+    traffic, traffic_src = counter_traffic(w.name, BWD_COUNTERS, "backward_pass_traffic_bytes",
+                                           BWD_SOURCES)
     result = {
         "metric": "gated linear-attn backward tokens/s per layer; achieved HBM GB/s vs peak",
         "value": w.B * w.N / (ms_step * 1e-3),
@@ -350,7 +358,9 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
                    "grid": [w.T, w.Hh, w.W], "parallelism": "single-gpu"},
         "roofline": {"kernel": "whole backward (state, query, gradient state, key kernels)",
                      "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "traffic_source": traffic_src,
+                     "traffic_over_algorithmic": traffic / nbytes if traffic else None,
                      "algorithmic_bytes": nbytes, "avg_ms": ev_ms},
     }
     if not args.no_cpu_baseline:
