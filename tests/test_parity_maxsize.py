@@ -1,23 +1,32 @@
-"""GPU parity at the largest size the library accepts: a batch element's
-[N, H, D] slab just under 2 GiB (N H D 2 < 2^31), so the kernels' 32-bit
-byte offsets reach the top of their range.
+"""GPU parity at the largest sizes the library accepts: a batch element's
+[N, H, D] slab just under 2 GiB (N H D 2 < 2^31), an [N, C] slab of hidden
+states of the same size, and a stacked projection weight just under 2 GiB,
+so the kernels' 32-bit byte offsets reach the top of their range.
 
 The inputs are zero except at a few tokens spread over the sequence, the
 first and last ones included.  The ReLU features of a zero token vanish, so
 it adds nothing to the state, the normaliser, dS or dz, and its output and
 all four gradients are exactly zero (the q > 0 and k > 0 masks are off and
-dout is zero there).  The nonzero tokens then see exactly the small problem
-made of them alone; without RoPE their positions do not enter, so the
-oracle solves that small problem.  Bar: as in the other parity tests,
-relative L2 <= 5e-3 and max abs <= 3e-2 on the nonzero tokens, and exact
-zeros on sampled zero tokens."""
+dout is zero there); a zero row of hidden states projects to zero q, k, v
+and g.  The nonzero tokens then see exactly the small problem made of them
+alone; without RoPE their positions do not enter, so the oracle solves that
+small problem.  The block-causal case keeps the same count of nonzero tokens
+in every block that has any, so the small problem has uniform blocks too.
+The softmax anchor is the exception: a zero key scores 0, not minus
+infinity, so each query also spreads weight over the zero keys; the inputs
+make every nonzero query's own key score far above that (checked on the
+host), so the small problem holds up to a relative 1e-4, and a zero query
+spreads its weight evenly over all N keys, whose values sum to those of the
+nonzero tokens.  Bar: as in the other parity tests, relative L2 <= 5e-3 and
+max abs <= 3e-2 on the nonzero tokens, and exact zeros on sampled zero
+tokens."""
 import numpy as np
 import pytest
 import torch
 
 import gated_linear_attention_forward_amd as gla
 import oracle
-from workloads import random_grad, random_inputs
+from workloads import random_grad, random_inputs, random_projection
 
 pytestmark = pytest.mark.gpu
 
@@ -58,8 +67,9 @@ def zero_positions(N, pos, seed, count=4096):
 
 
 def scatter(small, B, N, idx):
-    """[B, N, 1, D] bf16 zeros on the device with the rows of small at idx."""
-    big = torch.zeros((B, N, 1, D), dtype=torch.bfloat16, device=DEV)
+    """bf16 zeros on the device, [B, N] plus the trailing shape of small, with
+    the rows of small at idx."""
+    big = torch.zeros((B, N, *small.shape[2:]), dtype=torch.bfloat16, device=DEV)
     big[:, idx] = small.to(DEV)
     return big
 
@@ -104,3 +114,130 @@ def test_backward_at_the_slab_limit():
         assert_close(a, r, f"nonzero tokens {name}")
     for name, c in zip(NAMES, nonzero):
         assert c == 0, f"{c} nonzero {name} at zero tokens"
+
+
+def test_blocks_at_the_slab_limit():
+    """Block-causal pass with a carried state; blocks of L tokens, the last
+    one ragged, and nonzero tokens in the first, a middle and the last block
+    only (M of them in each, the block's first and last tokens included)."""
+    B, N, L, M = 1, N_MAX, 1_000_003, 8
+    nblk = (N + L - 1) // L
+    say(f"case blocks max slab B={B} N={N} H=1 D={D} L={L} blocks={nblk}")
+    rng = np.random.default_rng(31)
+    pos = []
+    for blk in (0, nblk // 2, nblk - 1):
+        lo, hi = blk * L, min(N, (blk + 1) * L)
+        inner = rng.choice(np.arange(lo + 1, hi - 1), M - 2, replace=False)
+        pos.append(np.sort(np.concatenate([[lo, hi - 1], inner])))
+    pos = np.concatenate(pos)
+    idx = torch.from_numpy(pos).to(DEV)
+    small = random_inputs(B, len(pos), 1, D, seed=4300)
+    gen = torch.Generator().manual_seed(4301)
+    S_in = torch.randn((B, 1, D, D), generator=gen, dtype=torch.float32)
+    z_in = torch.rand((B, 1, D), generator=gen, dtype=torch.float32) * 50.0
+    q, k, v, g = (scatter(t, B, N, idx) for t in small)
+    S_out = torch.empty((B, 1, D, D), dtype=torch.float32, device=DEV)
+    z_out = torch.empty((B, 1, D), dtype=torch.float32, device=DEV)
+    out = gla.gla_forward_blocks(q, k, v, g, None, L, S_in.to(DEV), z_in.to(DEV), S_out, z_out)
+    torch.cuda.synchronize()
+    got = out[:, idx].double().cpu().numpy()
+    zeros = out[:, zero_positions(N, pos, 32)]
+    nonzero = int(torch.count_nonzero(zeros))
+    S_got, z_got = S_out.double().cpu().numpy(), z_out.double().cpu().numpy()
+    del q, k, v, g, out
+    torch.cuda.empty_cache()
+    ref, S_ref, z_ref = oracle.forward_blocks(*small, None, M, S_in.numpy(), z_in.numpy())
+    assert_close(got, ref, "nonzero tokens")
+    s_rel = float(np.linalg.norm(S_got - S_ref) / np.linalg.norm(S_ref))
+    z_rel = float(np.linalg.norm(z_got - z_ref) / np.linalg.norm(z_ref))
+    say(f"  S_out rel_l2={s_rel:.3e} z_out rel_l2={z_rel:.3e}")
+    assert s_rel <= 3e-3 and z_rel <= 1e-6
+    assert nonzero == 0, f"{nonzero} nonzero outputs at zero tokens"
+
+
+def test_projection_at_the_slab_limit():
+    """Projection prologue with C = H D, so the [N, C] hidden-state slab and
+    the [N, H, D] slabs of q, k, v, g and the output all sit just under
+    2 GiB."""
+    B, N, C = 1, N_MAX, D
+    say(f"case projection max slab B={B} N={N} C={C} H=1 D={D}")
+    pos = positions(N, 60, 41)
+    idx = torch.from_numpy(pos).to(DEV)
+    x_small, w = random_projection(B, len(pos), C, 1, D, seed=4400)
+    x = scatter(x_small, B, N, idx)
+    out = gla.gla_forward_proj(x, w.to(DEV), 1, D)
+    torch.cuda.synchronize()
+    got = out[:, idx].double().cpu().numpy()
+    zeros = out[:, zero_positions(N, pos, 42)]
+    nonzero = int(torch.count_nonzero(zeros))
+    del x, out
+    torch.cuda.empty_cache()
+    ref = oracle.projected_forward(x_small, w, 1, D, None)
+    assert_close(got, ref, "nonzero tokens")
+    assert nonzero == 0, f"{nonzero} nonzero outputs at zero tokens"
+
+
+def test_projection_at_the_weight_limit():
+    """Stacked weight [4, H D, C] just under 2 GiB (4 H D C 2 < 2^31) at
+    H = 255, D = 64, C = 16384, over a ragged 300 tokens.  Only three heads,
+    the first, a middle and the last, have nonzero weight rows, so the last
+    rows read sit at the top of the weight; the other heads project to zero
+    and must give exact zeros."""
+    B, N, C, H, Dh = 1, 300, 16384, 255, 64
+    heads = [0, H // 2, H - 1]
+    say(f"case projection max weight B={B} N={N} C={C} H={H} D={Dh} "
+        f"({4 * H * Dh * C * 2} weight bytes)")
+    x, w_small = random_projection(B, N, C, len(heads), Dh, seed=4500)
+    rows = torch.tensor([m * H * Dh + h * Dh + d for m in range(4) for h in heads
+                         for d in range(Dh)], device=DEV)
+    w = torch.zeros((4 * H * Dh, C), dtype=torch.bfloat16, device=DEV)
+    w[rows] = w_small.reshape(-1, C).to(DEV)
+    out = gla.gla_forward_proj(x.to(DEV), w.view(4, H * Dh, C), H, Dh)
+    torch.cuda.synchronize()
+    got = out[:, :, heads].double().cpu().numpy()
+    others = torch.ones(H, dtype=torch.bool, device=DEV)
+    others[heads] = False
+    nonzero = int(torch.count_nonzero(out[:, :, others]))
+    del w, out
+    torch.cuda.empty_cache()
+    ref = oracle.projected_forward(x, w_small, len(heads), Dh, None)
+    assert_close(got, ref, "weighted heads")
+    assert nonzero == 0, f"{nonzero} nonzero outputs in zero-weight heads"
+
+
+@pytest.mark.parametrize("Ds,qk_scale", [(256, 1.5), (128, 2.0)])
+def test_softmax_at_the_slab_limit(Ds, qk_scale):
+    """Softmax anchor with k = q on the nonzero tokens, which fall into 16
+    groups spread over the sequence that share one q: a nonzero query scores
+    about qk_scale^2 sqrt(D) against the keys of its group, far above the
+    other keys, so it averages the values of tokens up to N apart."""
+    B, N = 1, ((1 << 31) - 1) // (2 * Ds)
+    say(f"case softmax max slab B={B} N={N} H=1 D={Ds}")
+    pos = positions(N, 60, 51)
+    n = len(pos)
+    idx = torch.from_numpy(pos).to(DEV)
+    q_s, _, v_s, g_s = random_inputs(B, n, 1, Ds, seed=4600, qk_scale=qk_scale)
+    q_s = q_s[:, torch.arange(n) % 16].contiguous()
+    k_s = q_s.clone()
+    qf = q_s[0, :, 0].double().numpy()
+    scores = qf @ qf.T / np.sqrt(Ds)
+    top = scores.max(axis=1)
+    ref0 = np.maximum(scores[:, pos < 64].max(axis=1), 0.0)   # first key tile's maximum
+    mass = (N - n) * np.exp(-top)
+    say(f"  zero-key mass bound {mass.max():.2e}; queries past 2^64 of the first tile's "
+        f"maximum: {int(np.sum(top - ref0 > 64 * np.log(2)))} of {n}")
+    assert mass.max() <= 1e-4
+    q, k, v, g = (scatter(t, B, N, idx) for t in (q_s, k_s, v_s, g_s))
+    zidx = zero_positions(N, pos, 52)
+    out = gla.gla_softmax_forward(q, k, v, g, None)
+    torch.cuda.synchronize()
+    got = out[:, idx].double().cpu().numpy()
+    got_zero = out[:, zidx].double().cpu().numpy()
+    del q, k, v, g, out
+    torch.cuda.empty_cache()
+    ref = oracle.softmax_forward(q_s, k_s, v_s, g_s, None)
+    assert_close(got, ref, "nonzero tokens")
+    # a zero query: every score is 0, the weights are uniform over N keys
+    # and the gate is sigmoid(0) = 1/2
+    even = 0.5 * v_s[0, :, 0].double().numpy().sum(axis=0) / N
+    assert_close(got_zero, np.broadcast_to(even, got_zero.shape), "zero tokens")
