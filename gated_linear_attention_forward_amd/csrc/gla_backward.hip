@@ -59,16 +59,6 @@ struct BwdCfg {
   static_assert(kQueryWaves * D * 4 <= kQueryWaves * 16 * PITCH, "dz scratch fits the a tiles");
 };
 
-// Copies `rows` dense rows of D bf16 into an LDS row tile.
-template <int D, int NT>
-__device__ __forceinline__ void stage_rows(unsigned char* dst, const uint16_t* src, int rows) {
-  const uint4* s = reinterpret_cast<const uint4*>(src);
-  for (int i = threadIdx.x; i < rows * D / 8; i += NT) {
-    const int row = i / (D / 8), u = i % (D / 8);
-    *reinterpret_cast<uint4*>(dst + row_tile_offset<D>(row, 16 * u)) = s[i];
-  }
-}
-
 // (cos, sin) of the PU rotation pairs PU col + u (u < PU) of token n: the
 // pairs of the MB contiguous features the accumulator layout gives lane
 // column col.
@@ -162,12 +152,28 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
   int n_begin, n_end;
   range_of(a, c, n_begin, n_end);
 
-  stage_rows<D, NT>(sS, a.sl + (size_t)bh * (D + 2) * D, D + 2);
-  stage_rows<D, NT>(sR, a.sl2 + (size_t)bh * D * D, D);
-  for (int i = tid; i < D; i += NT) zf[i] = bw.z[(size_t)bh * D + i];
   TabView tv{};
-  if (ROPE) tv = stage_table<D, NT>(a, ltab, TLDS, n_begin, n_end);
+  {
+    RowStage<D, D, NT> st_s;      // S^T rows
+    RowStage<D, 2, NT, D> st_z;   // z hi and lo rows
+    RowStage<D, D, NT> st_r;      // S rows
+    const uint16_t* sl = a.sl + (size_t)bh * (D + 2) * D;
+    st_s.load(sl);
+    st_z.load(sl);
+    st_r.load(a.sl2 + (size_t)bh * D * D);
+    const float zv = tid < D ? bw.z[(size_t)bh * D + tid] : 0.f;
+    if (ROPE) tv = stage_table<D, NT>(a, ltab, TLDS, n_begin, n_end);
+    st_s.store(sS);
+    st_z.store(sS);
+    st_r.store(sR);
+    if (tid < D) zf[tid] = zv;
+  }
   __syncthreads();
+  // the lane's own z features, for dden z (registers: the masked sums below
+  // then compile to selects instead of a branch around each LDS read)
+  float zl[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) zl[j] = zf[MB * col + j];
 
   const size_t boff = (size_t)b * a.N * a.H * D;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + boff, a.slab_bytes);
@@ -217,6 +223,7 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
   issue_q(base);
   issue_gd(base);
   issue_qc(base);
+  wait_vmem_all();
   for (; base < n_end; base += 16 * NW) {
     const int next = base + 16 * NW;
     __builtin_amdgcn_sched_barrier(0);
@@ -313,8 +320,8 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
           yr = y * cs[u].x - x * cs[u].y;
         }
         const float q0 = bf_lo(qc[i][u]), q1 = bf_hi(qc[i][u]);
-        const float g0 = q0 > 0.f ? xr + dden[i] * zf[MB * col + 2 * u] : 0.f;
-        const float g1 = q1 > 0.f ? yr + dden[i] * zf[MB * col + 2 * u + 1] : 0.f;
+        const float g0 = q0 > 0.f ? xr + dden[i] * zl[2 * u] : 0.f;
+        const float g1 = q1 > 0.f ? yr + dden[i] * zl[2 * u + 1] : 0.f;
         dzacc[2 * u] += dden[i] * fmaxf(q0, 0.f);
         dzacc[2 * u + 1] += dden[i] * fmaxf(q1, 0.f);
         wq[u] = pack_bf16(g0, g1);
@@ -395,12 +402,23 @@ void bwd_key_kernel(KArgs a, BArgs bw) {
   int n_begin, n_end;
   range_of(a, blockIdx.y, n_begin, n_end);
 
-  stage_rows<D, NT>(sD, a.sl + (size_t)bh * (D + 2) * D, D);
-  stage_rows<D, NT>(sR, a.sl2 + (size_t)bh * D * D, D);
-  for (int i = tid; i < D; i += NT) zf[i] = bw.dz[(size_t)bh * D + i];
   TabView tv{};
-  if (ROPE) tv = stage_table<D, NT>(a, ltab, TLDS, n_begin, n_end);
+  {
+    RowStage<D, D, NT> st_d;   // dS^T rows
+    RowStage<D, D, NT> st_r;   // dS rows
+    st_d.load(a.sl + (size_t)bh * (D + 2) * D);
+    st_r.load(a.sl2 + (size_t)bh * D * D);
+    const float zv = tid < D ? bw.dz[(size_t)bh * D + tid] : 0.f;
+    if (ROPE) tv = stage_table<D, NT>(a, ltab, TLDS, n_begin, n_end);
+    st_d.store(sD);
+    st_r.store(sR);
+    if (tid < D) zf[tid] = zv;
+  }
   __syncthreads();
+  // the lane's own dz features (registers, as in the query kernel)
+  float zl[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) zl[j] = zf[MB * col + j];
 
   const size_t boff = (size_t)b * a.N * a.H * D;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + boff, a.slab_bytes);
@@ -441,6 +459,7 @@ void bwd_key_kernel(KArgs a, BArgs bw) {
   issue_k(base);
   issue_v(base);
   issue_kc(base);
+  wait_vmem_all();
   for (; base < n_end; base += 16 * NW) {
     const int next = base + 16 * NW;
     __builtin_amdgcn_sched_barrier(0);
@@ -492,8 +511,8 @@ void bwd_key_kernel(KArgs a, BArgs bw) {
           yr = y * cs[u].x - x * cs[u].y;
         }
         const float k0 = bf_lo(kc[i][u]), k1 = bf_hi(kc[i][u]);
-        const float g0 = k0 > 0.f ? xr + zf[MB * col + 2 * u] : 0.f;
-        const float g1 = k1 > 0.f ? yr + zf[MB * col + 2 * u + 1] : 0.f;
+        const float g0 = k0 > 0.f ? xr + zl[2 * u] : 0.f;
+        const float g1 = k1 > 0.f ? yr + zl[2 * u + 1] : 0.f;
         wk[u] = pack_bf16(g0, g1);
       }
       store_chunk_nt<OB>(rdk, r_offset(base, i), wk);

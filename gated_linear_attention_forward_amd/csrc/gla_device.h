@@ -101,6 +101,26 @@ struct TabView {
   int t_last;  // last t of the block's tokens (positions past the range clamp to it)
 };
 
+// Copies n float2 from global memory to LDS with a block of NT threads,
+// four loads in flight per thread before their LDS writes (one wait for
+// memory per four loads, not one per load).  Caller synchronises.
+template <int NT>
+__device__ __forceinline__ void copy_to_lds(float2* dst, const float2* src, int n) {
+  for (int b0 = threadIdx.x; b0 < n; b0 += 4 * NT) {
+    float2 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = b0 + k * NT;
+      if (i < n) v[k] = src[i];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = b0 + k * NT;
+      if (i < n) dst[i] = v[k];
+    }
+  }
+}
+
 // Copies the table rows a block of NT threads needs into LDS.  Caller
 // synchronises.
 template <int D, int NT = 256>
@@ -112,11 +132,9 @@ __device__ __forceinline__ TabView stage_table(const KArgs& a, float2* ltab, boo
   tv.t_last = (int)fast_div((uint32_t)(n_end - 1), a.div_hw);
   if (in_lds) {
     const int nt_blk = tv.t_last - t_first + 1;
-    const float2* src_t = a.cs + (size_t)t_first * X::Pt;
-    for (int i = threadIdx.x; i < nt_blk * X::Pt; i += NT) ltab[i] = src_t[i];
-    const float2* src_yx = a.cs + (size_t)a.T * X::Pt;
-    const int nyx = a.Hh * X::Py + a.W * X::Px;
-    for (int i = threadIdx.x; i < nyx; i += NT) ltab[a.nt * X::Pt + i] = src_yx[i];
+    copy_to_lds<NT>(ltab, a.cs + (size_t)t_first * X::Pt, nt_blk * X::Pt);
+    copy_to_lds<NT>(ltab + a.nt * X::Pt, a.cs + (size_t)a.T * X::Pt,
+                    a.Hh * X::Py + a.W * X::Px);
     tv.tab = ltab;
     tv.tbase = t_first;
     tv.ntr = a.nt;
@@ -279,6 +297,43 @@ template <int D>
 __device__ __forceinline__ int row_tile_offset(int row, int byte) {
   return row * 2 * D + 16 * ((byte >> 4) ^ row_swizzle<D>(row)) + (byte & 15);
 }
+
+// Stages ROWS dense rows of D bf16, rows ROW0 .. ROW0 + ROWS - 1 of src,
+// into the same rows of an LDS row tile (row_tile_offset) with a block of NT
+// threads.  load() issues all of a thread's global loads before store()
+// writes any of them to LDS, so a block's staging waits for memory once
+// rather than once per row chunk.  Caller synchronises.
+template <int D, int ROWS, int NT, int ROW0 = 0>
+struct RowStage {
+  static constexpr int TOTAL = ROWS * D / 8;  // 16-byte chunks
+  static constexpr int IT = (TOTAL + NT - 1) / NT;
+  u32x4 v[IT];
+  __device__ __forceinline__ void load(const uint16_t* src) {
+    const u32x4* s = reinterpret_cast<const u32x4*>(src) + ROW0 * D / 8;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (TOTAL % NT == 0 || i < TOTAL) v[k] = s[i];
+    }
+  }
+  __device__ __forceinline__ void store(unsigned char* dst) const {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (TOTAL % NT == 0 || i < TOTAL)
+        *reinterpret_cast<u32x4*>(dst + row_tile_offset<D>(ROW0 + i / (D / 8), 16 * (i % (D / 8)))) =
+            v[k];
+    }
+  }
+};
+
+// Waits until every vector memory access of the wave is done (s_waitcnt
+// with vmcnt 0 and the expcnt and lgkmcnt fields at their no-wait maxima).
+// Placed after a loop's prologue loads, it leaves nothing in flight on the
+// entry path, so the compiler sizes the loop-head waits from the loop body
+// alone instead of merging the prologue's different issue order into a wait
+// for everything.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 constexpr int tile_pitch(int row_bytes) {
   int dw = row_bytes / 4;

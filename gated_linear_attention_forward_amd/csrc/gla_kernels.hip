@@ -810,17 +810,7 @@ void output_kernel(KArgs a) {
   int n_begin, n_end;
   range_of(a, blockIdx.y, n_begin, n_end);
   const int blk = blockIdx.y / a.CB;  // attention block of the range
-
-  // stage the block's S^T rows and z rows
-  const uint4* src =
-      reinterpret_cast<const uint4*>(a.sl + ((size_t)bh * a.NB + blk) * ROWS * D);
-  for (int i = tid; i < ROWS * D / 8; i += 256) {
-    const int row = i / (D / 8), u = i % (D / 8);
-    *reinterpret_cast<uint4*>(sS + row_tile_offset<D>(row, 16 * u)) = src[i];
-  }
-  TabView tv{};
-  if (ROPE) tv = stage_table<D>(a, ltab, TLDS, n_begin, n_end);
-  __syncthreads();
+  TabView tv{};                       // the RoPE table view, set when staged
 
   const size_t boff = (size_t)b * a.N * a.H * D;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + boff, a.slab_bytes);
@@ -922,11 +912,27 @@ void output_kernel(KArgs a) {
     }
   };
 
-  // two register sets: the next step's q and g are in flight during a step
+  // two register sets: the next step's q and g are in flight during a step.
+  // The first step's loads go out before the staging below, so the two wait
+  // for memory together.
   u32x4 qa[KS], qb[KS];
   OChunk ga[4], gb[4];
   int base = n_begin + 16 * wave;
   if (base < n_end) load_qg(base, qa, ga);
+
+  // stage the block's S^T rows and z rows
+  {
+    RowStage<D, D, 256> st_s;
+    RowStage<D, 2, 256, D> st_z;
+    const uint16_t* sl = a.sl + ((size_t)bh * a.NB + blk) * ROWS * D;
+    st_s.load(sl);
+    st_z.load(sl);
+    if (ROPE) tv = stage_table<D>(a, ltab, TLDS, n_begin, n_end);
+    st_s.store(sS);
+    st_z.store(sS);
+  }
+  __syncthreads();
+
   for (; base < n_end; base += 128) {
     load_qg(base + 64, qb, gb);
     step(base, qa, ga);
