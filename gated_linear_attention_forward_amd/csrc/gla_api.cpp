@@ -43,7 +43,7 @@ DivMagic make_div_magic(uint32_t d) {
 // chunk adds one fp32 (D*D + D) partial per head.  The output kernel reads
 // only a bf16 copy of the state per block, so it takes more, smaller blocks.
 // Chunks and output ranges never straddle an attention block.
-Plan make_plan(int B, int N, int H, int D, int block_tokens) {
+Plan make_plan(int B, int N, int H, int D, int block_tokens, int output_blocks) {
   Plan p{};
   p.B = B; p.N = N; p.H = H; p.D = D;
   p.BH = B * H;
@@ -64,7 +64,7 @@ Plan make_plan(int B, int N, int H, int D, int block_tokens) {
   p.C = p.NB * p.CB;
 
   const int its = ceil_div(p.BT, kOutputTileTokens);
-  long long sub = (kOutputBlocks + heads_blocks - 1) / heads_blocks;
+  long long sub = (output_blocks + heads_blocks - 1) / heads_blocks;
   if (sub > its) sub = its;
   if (sub < 1) sub = 1;
   p.L2 = ceil_div(its, (int)sub) * kOutputTileTokens;
@@ -649,7 +649,7 @@ struct BwdLayout {
 
 BwdLayout bwd_layout(int B, int N, int H, int D) {
   BwdLayout l{};
-  l.p = gla::make_plan(B, N, H, D);
+  l.p = gla::make_plan(B, N, H, D, 0, gla::kBackwardBlocks);
   size_t off = l.p.ws_bytes;
   l.off_sl2 = off;
   off = gla::align_up(off + (size_t)l.p.BH * D * D * sizeof(uint16_t), 256);
@@ -690,7 +690,7 @@ int gla_backward_check(const void* q, const void* k, const void* v, const void* 
   for (int i = 0; i < 4; ++i)
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j], bytes)) return GLA_ERR_ALIAS;
-  return check_plan_limits(gla::make_plan(B, N, H, D));
+  return check_plan_limits(gla::make_plan(B, N, H, D, 0, gla::kBackwardBlocks));
 }
 
 int gla_backward_ws(const void* q, const void* k, const void* v, const void* g, const void* dout,
@@ -801,7 +801,11 @@ int check_proj_shape(int B, int N, int C, int H, int D, size_t* out_bytes) {
   if (C < 64 || C % 64 != 0) return GLA_ERR_DIM;
   if ((long long)N * C * 2 >= (1LL << 31)) return GLA_ERR_DIM;           // x slab offsets
   if (4LL * H * D * C * 2 >= (1LL << 31)) return GLA_ERR_DIM;            // weight offsets
-  if ((long long)(N + gla::kProjTileTokens - 1) / gla::kProjTileTokens > 65535) return GLA_ERR_DIM;
+  const long long tiles = (N + gla::kProjTileTokens - 1) / gla::kProjTileTokens;
+  if (tiles > 65535) return GLA_ERR_DIM;
+  // the qg kernel's 1-D grid: B H tiles blocks of up to 512 threads, whose
+  // work-item count must fit in 32 bits
+  if ((long long)B * H * tiles * 512 > 0xFFFFFFFFLL) return GLA_ERR_DIM;
   return GLA_OK;
 }
 

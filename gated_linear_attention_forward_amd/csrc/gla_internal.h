@@ -71,8 +71,27 @@ struct Plan {
   size_t off_part, off_sl, ws_bytes;
 };
 
+// Tile sizes the plan has to respect.
+constexpr int kOutputTileTokens = 64;
+constexpr int kMaxChunks = 256;
+// Blocks of the state kernel the plan aims for: one per compute unit (256
+// compute units); a block's waves together hold a full D x D accumulator.
+constexpr int kStateBlocks = 256;
+// Each wave of a state block should see at least this many 16-token tiles.
+constexpr int kStateMinTilesPerWave = 2;
+constexpr int kOutputBlocks = 2048;
+// The backward pass's query and key kernels (8 waves, one block per compute
+// unit) take their token ranges from a plan made for this many blocks: a few
+// rounds of long ranges, each block staging its head's operands once.
+constexpr int kBackwardBlocks = 768;
+// Largest RoPE table slice (bytes) a block stages in LDS; larger grids read
+// the table from global memory instead.
+constexpr int kMaxLdsTableBytes = 24 * 1024;
+
 // block_tokens <= 0 or >= N: one attention block (the bidirectional mixer).
-Plan make_plan(int B, int N, int H, int D, int block_tokens = 0);
+// output_blocks: the block count the output-side ranges (SUB, L2) aim at.
+Plan make_plan(int B, int N, int H, int D, int block_tokens = 0,
+               int output_blocks = kOutputBlocks);
 
 // Kernel launchers (gla_kernels.hip).  Return the hipError_t of the launch.
 hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream);
@@ -120,17 +139,5 @@ hipError_t launch_proj(const Plan& p, KArgs akv, KArgs aqg, PArgs pa, hipStream_
 hipError_t launch_reduce_state(const Plan& p, KArgs a, hipStream_t stream);
 constexpr int kProjTileTokens = 256;
 
-// Tile sizes the plan has to respect.
-constexpr int kOutputTileTokens = 64;
-constexpr int kMaxChunks = 256;
-// Blocks of the state kernel the plan aims for: one per compute unit (256
-// compute units); a block's waves together hold a full D x D accumulator.
-constexpr int kStateBlocks = 256;
-// Each wave of a state block should see at least this many 16-token tiles.
-constexpr int kStateMinTilesPerWave = 2;
-constexpr int kOutputBlocks = 2048;
-// Largest RoPE table slice (bytes) a block stages in LDS; larger grids read
-// the table from global memory instead.
-constexpr int kMaxLdsTableBytes = 24 * 1024;
 
 }  // namespace gla

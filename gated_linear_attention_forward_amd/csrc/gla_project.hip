@@ -36,6 +36,9 @@
 namespace gla {
 namespace {
 
+// Token tiles per group of the qg kernel's XCD-aware block numbering.
+constexpr int kQgGroupTiles = 4;
+
 template <int D>
 struct ProjCfg {
   static constexpr int TM = kProjTileTokens;  // tokens per tile
@@ -346,10 +349,26 @@ void proj_qg_kernel(KArgs a, PArgs pa) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int bh = blockIdx.x;
+  // Blocks go to the 8 XCDs in turn (block i to XCD i % 8), and each XCD has
+  // its own L2.  The 1-D grid is renumbered so that XCD x takes a contiguous
+  // run of logical tiles, ordered in groups of kQgGroupTiles token tiles
+  // across all heads, token tiles fastest.  The blocks an XCD holds at once
+  // then cover a few token tiles (x rows) times a few heads (weight rows),
+  // and both are reused from its L2.
+  int bh, tile;
+  {
+    const int T = gridDim.x, BHn = T / a.CB, pb = blockIdx.x;
+    const int xcd = pb & 7, per = T >> 3, rem = T & 7;
+    const int lg = xcd * per + min(xcd, rem) + (pb >> 3);
+    const int grp = lg / (kQgGroupTiles * BHn), first = grp * kQgGroupTiles;
+    const int gsz = min(a.CB - first, kQgGroupTiles);
+    const int r = lg - grp * kQgGroupTiles * BHn;
+    tile = first + r % gsz;
+    bh = r / gsz;
+  }
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
   int n_begin, n_end;
-  range_of(a, blockIdx.y, n_begin, n_end);
+  range_of(a, tile, n_begin, n_end);
 
   const int HD = a.H * D;
   Gemm gm;
@@ -412,7 +431,7 @@ hipError_t launch_proj_d(const Plan& p, const KArgs& akv, const KArgs& aqg, cons
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // q and g
   if ((e = allow_lds<proj_qg_kernel<D>>(Cf::LDS_BYTES)) != hipSuccess) return e;
-  const dim3 g2(p.BH, aqg.CB);
+  const dim3 g2(p.BH * aqg.CB);  // renumbered in the kernel (XCD groups)
   hipLaunchKernelGGL((proj_qg_kernel<D>), g2, dim3(Cf::NT), Cf::LDS_BYTES, s, aqg, pa);
   return hipGetLastError();
 }

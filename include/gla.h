@@ -315,7 +315,8 @@ int gla_backward_check(const void* q, const void* k, const void* v, const void* 
  * aligned.  D must be 32, 64 or 128; rope as for gla_forward.  The GEMMs
  * run on bf16 MFMA with fp32 accumulation; k and v never reach device
  * memory (the state is contracted from them in the GEMM's epilogue), q and
- * g go through the workspace.  Limits: N*C*2 and 4*H*D*C*2 below 2 GiB.
+ * g go through the workspace.  Limits (GLA_ERR_DIM): N*C*2 and 4*H*D*C*2
+ * below 2 GiB, ceil(N / 256) <= 65535 and B*H*ceil(N / 256) <= 8,388,607.
  * Uses a library-owned workspace (grown with hipMalloc, which may
  * synchronise).  B*N*H == 0 is a no-op.  Results are bitwise reproducible. */
 int gla_forward_proj(const void* x, const void* w, const gla_rope_tables* rope, void* out, int B,

@@ -308,6 +308,11 @@ def test_proj_validation():
     assert pcheck(N=64, rope=_host_rope(4, 4, 5, 128)) == glamod.GLA_ERR_ROPE
     # x slab beyond 2 GiB of 32-bit offsets
     assert pcheck(N=1 << 20, C=1024) == glamod.GLA_ERR_DIM
+    # the qg kernel's 1-D grid: B H ceil(N / 256) blocks of 512 work-items
+    # must stay within 2^32 work-items
+    big = dict(N=65535 * 256, C=64, H=1, D=32)
+    assert pcheck(B=129, **big) == glamod.GLA_ERR_DIM
+    assert pcheck(B=128, **big) != glamod.GLA_ERR_DIM
 
 
 def test_proj_workspace_size():
