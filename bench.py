@@ -306,7 +306,9 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
     """Backward pass: K passes of gla_backward_ws (state, query, gradient
     state and key kernels).  The roofline is the whole pass against the
     algorithmic minimum of 18*D bytes per (token, head): q, k, v, g and dout
-    read, dq, dk, dv and dg written, once each."""
+    read, dq, dk, dv and dg written, once each.  "saved_state" times the same
+    pass given the forward's fp32 state (gla_backward_saved_ws), against the
+    same minimum."""
     import torch
 
     from workloads import random_grad
@@ -363,6 +365,30 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
                      "traffic_over_algorithmic": traffic / nbytes if traffic else None,
                      "algorithmic_bytes": nbytes, "avg_ms": ev_ms},
     }
+    # The same pass given the forward's saved state (gla_backward_saved_ws):
+    # the forward's S and z replace the first state pass over k and v.
+    S = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    z = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev)
+    gla.gla_forward_blocks(qd, kd, vd, gd, rope, w.N, None, None, S, z, stream=stream)
+
+    def step_saved():
+        gla.gla_backward_saved_ws(qd, kd, vd, gd, dout, S, z, rope, ws, *grads, stream=stream)
+
+    log(f"bench: backward with the saved state; {args.warmup} + {args.steps} steps")
+    for _ in range(args.warmup):
+        step_saved()
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record(stream)
+        step_saved()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    sv_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    sv_achieved = nbytes / (sv_ms * 1e-3) / 1e9
+    result["saved_state"] = {
+        "entry": "gla_backward_saved_ws", "value": w.B * w.N / (sv_ms * 1e-3), "unit": "tokens/s",
+        "avg_ms": sv_ms, "achieved": sv_achieved, "peak": PEAK_HBM_GBPS, "unit_roofline": "GB/s",
+        "frac": sv_achieved / PEAK_HBM_GBPS, "algorithmic_bytes": nbytes}
     if not args.no_cpu_baseline:
         log("bench: timing the oracle (cpu_baseline)")
         q, k, v, g = (t.cpu() for t in tensors)

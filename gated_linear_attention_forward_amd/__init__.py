@@ -17,6 +17,9 @@ from .gla import (  # noqa: F401
     alloc_workspace_softmax,
     gla_backward,
     gla_backward_check,
+    gla_backward_saved,
+    gla_backward_saved_check,
+    gla_backward_saved_ws,
     gla_backward_workspace_bytes,
     gla_backward_ws,
     gla_forward,

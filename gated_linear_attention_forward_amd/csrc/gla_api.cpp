@@ -665,6 +665,85 @@ BwdLayout bwd_layout(int B, int N, int H, int D) {
   return l;
 }
 
+// The backward pass after argument validation.  S_saved and z_saved: the
+// forward's fp32 state, or NULL to recompute it from k and v.
+int backward_run(const void* q, const void* k, const void* v, const void* g, const void* dout,
+                 const gla_rope_tables* rope, const float* S_saved, const float* z_saved,
+                 void* dq, void* dk, void* dv, void* dg, int B, int N, int H, int D,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = GLA_OK;
+  size_t bytes = 0;
+  check_shape(B, N, H, D, &bytes);
+  if (bytes == 0) return GLA_OK;
+  const BwdLayout l = bwd_layout(B, N, H, D);
+  if (!workspace) return GLA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < l.bytes)
+    return GLA_ERR_WORKSPACE;
+  for (const void* t : {q, k, v, g, dout, static_cast<const void*>(dq),
+                        static_cast<const void*>(dk), static_cast<const void*>(dv),
+                        static_cast<const void*>(dg)})
+    if (overlap2(workspace, l.bytes, t, bytes)) return GLA_ERR_ALIAS;
+  if (S_saved && (overlap2(workspace, l.bytes, S_saved, (size_t)B * H * D * D * sizeof(float)) ||
+                  overlap2(workspace, l.bytes, z_saved, (size_t)B * H * D * sizeof(float))))
+    return GLA_ERR_ALIAS;
+  if ((rc = rope_device_ok(rope))) return rc;
+  const Plan& p = l.p;
+  char* w = static_cast<char*>(workspace);
+  uint16_t* sl2 = reinterpret_cast<uint16_t*>(w + l.off_sl2);
+  float* zbuf = reinterpret_cast<float*>(w + l.off_z);
+  float* dzp = reinterpret_cast<float*>(w + l.off_dzp);
+  uint16_t* abuf = reinterpret_cast<uint16_t*>(w + l.off_a);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  gla::BArgs bw{};
+  bw.dout = static_cast<const uint16_t*>(dout);
+  bw.dq = static_cast<uint16_t*>(dq);
+  bw.dk = static_cast<uint16_t*>(dk);
+  bw.dv = static_cast<uint16_t*>(dv);
+  bw.dg = static_cast<uint16_t*>(dg);
+  bw.abuf = abuf;
+  bw.z = zbuf;
+  bw.dzp = dzp;
+  bw.dz = reinterpret_cast<float*>(w + l.off_dz);
+  bw.C2 = p.C2;
+
+  // 1. S (both operand layouts) and fp32 z: from k and v, or from the saved
+  //    state by the reduce kernel alone (no chunk partials: its window is
+  //    empty and reads zero, so it writes the saved fp32 values' operands)
+  gla::KArgs a1 = kernel_args(p, rope, p.L, p.CB, workspace);
+  a1.sl2 = sl2;
+  a1.z_out = zbuf;
+  if (S_saved) {
+    a1.C = 0;
+    a1.CB = 0;
+    a1.S_in = S_saved;
+    a1.z_in = z_saved;
+    if ((rc = status_of(gla::launch_reduce_state(p, a1, s)))) return rc;
+  } else {
+    a1.k = static_cast<const uint16_t*>(k);
+    a1.v = static_cast<const uint16_t*>(v);
+    if ((rc = status_of(gla::launch_state(p, a1, s)))) return rc;
+  }
+  // 2. query side: dq, dg, a, dz partials
+  gla::KArgs a2 = kernel_args(p, rope, p.L2, p.SUB, workspace);
+  a2.q = static_cast<const uint16_t*>(q);
+  a2.g = static_cast<const uint16_t*>(g);
+  a2.sl2 = sl2;
+  if ((rc = status_of(gla::launch_bwd_query(p, a2, bw, s)))) return rc;
+  // 3. dS (both operand layouts) from q and a: the state pass with q, a in
+  //    the places of k, v
+  gla::KArgs a3 = kernel_args(p, rope, p.L, p.CB, workspace);
+  a3.k = static_cast<const uint16_t*>(q);
+  a3.v = abuf;
+  a3.sl2 = sl2;
+  if ((rc = status_of(gla::launch_state(p, a3, s)))) return rc;
+  // 4. key side: dk, dv
+  gla::KArgs a4 = kernel_args(p, rope, p.L2, p.SUB, workspace);
+  a4.k = static_cast<const uint16_t*>(k);
+  a4.v = static_cast<const uint16_t*>(v);
+  a4.sl2 = sl2;
+  return status_of(gla::launch_bwd_key(p, a4, bw, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -698,63 +777,8 @@ int gla_backward_ws(const void* q, const void* k, const void* v, const void* g, 
                     int N, int H, int D, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = gla_backward_check(q, k, v, g, dout, rope, dq, dk, dv, dg, B, N, H, D);
   if (rc) return rc;
-  size_t bytes = 0;
-  check_shape(B, N, H, D, &bytes);
-  if (bytes == 0) return GLA_OK;
-  const BwdLayout l = bwd_layout(B, N, H, D);
-  if (!workspace) return GLA_ERR_NULL;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < l.bytes)
-    return GLA_ERR_WORKSPACE;
-  for (const void* t : {q, k, v, g, dout, static_cast<const void*>(dq),
-                        static_cast<const void*>(dk), static_cast<const void*>(dv),
-                        static_cast<const void*>(dg)})
-    if (overlap2(workspace, l.bytes, t, bytes)) return GLA_ERR_ALIAS;
-  if ((rc = rope_device_ok(rope))) return rc;
-  const Plan& p = l.p;
-  char* w = static_cast<char*>(workspace);
-  uint16_t* sl2 = reinterpret_cast<uint16_t*>(w + l.off_sl2);
-  float* zbuf = reinterpret_cast<float*>(w + l.off_z);
-  float* dzp = reinterpret_cast<float*>(w + l.off_dzp);
-  uint16_t* abuf = reinterpret_cast<uint16_t*>(w + l.off_a);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  gla::BArgs bw{};
-  bw.dout = static_cast<const uint16_t*>(dout);
-  bw.dq = static_cast<uint16_t*>(dq);
-  bw.dk = static_cast<uint16_t*>(dk);
-  bw.dv = static_cast<uint16_t*>(dv);
-  bw.dg = static_cast<uint16_t*>(dg);
-  bw.abuf = abuf;
-  bw.z = zbuf;
-  bw.dzp = dzp;
-  bw.dz = reinterpret_cast<float*>(w + l.off_dz);
-  bw.C2 = p.C2;
-
-  // 1. S (both operand layouts) and fp32 z from k and v
-  gla::KArgs a1 = kernel_args(p, rope, p.L, p.CB, workspace);
-  a1.k = static_cast<const uint16_t*>(k);
-  a1.v = static_cast<const uint16_t*>(v);
-  a1.sl2 = sl2;
-  a1.z_out = zbuf;
-  if ((rc = status_of(gla::launch_state(p, a1, s)))) return rc;
-  // 2. query side: dq, dg, a, dz partials
-  gla::KArgs a2 = kernel_args(p, rope, p.L2, p.SUB, workspace);
-  a2.q = static_cast<const uint16_t*>(q);
-  a2.g = static_cast<const uint16_t*>(g);
-  a2.sl2 = sl2;
-  if ((rc = status_of(gla::launch_bwd_query(p, a2, bw, s)))) return rc;
-  // 3. dS (both operand layouts) from q and a: the state pass with q, a in
-  //    the places of k, v
-  gla::KArgs a3 = kernel_args(p, rope, p.L, p.CB, workspace);
-  a3.k = static_cast<const uint16_t*>(q);
-  a3.v = abuf;
-  a3.sl2 = sl2;
-  if ((rc = status_of(gla::launch_state(p, a3, s)))) return rc;
-  // 4. key side: dk, dv
-  gla::KArgs a4 = kernel_args(p, rope, p.L2, p.SUB, workspace);
-  a4.k = static_cast<const uint16_t*>(k);
-  a4.v = static_cast<const uint16_t*>(v);
-  a4.sl2 = sl2;
-  return status_of(gla::launch_bwd_key(p, a4, bw, s));
+  return backward_run(q, k, v, g, dout, rope, nullptr, nullptr, dq, dk, dv, dg, B, N, H, D,
+                      workspace, workspace_bytes, stream);
 }
 
 int gla_backward(const void* q, const void* k, const void* v, const void* g, const void* dout,
@@ -767,6 +791,46 @@ int gla_backward(const void* q, const void* k, const void* v, const void* g, con
   void* ws = nullptr;
   if ((rc = get_workspace(need, stream, &ws))) return rc;
   return gla_backward_ws(q, k, v, g, dout, rope, dq, dk, dv, dg, B, N, H, D, ws, need, stream);
+}
+
+int gla_backward_saved_check(const void* q, const void* k, const void* v, const void* g,
+                             const void* dout, const gla_rope_tables* rope, const float* S,
+                             const float* z, const void* dq, const void* dk, const void* dv,
+                             const void* dg, int B, int N, int H, int D) {
+  int rc = gla_backward_check(q, k, v, g, dout, rope, dq, dk, dv, dg, B, N, H, D);
+  if (rc) return rc;
+  size_t bytes = 0;
+  check_shape(B, N, H, D, &bytes);
+  if (bytes == 0) return GLA_OK;
+  if (!S || !z) return GLA_ERR_NULL;
+  if (!aligned16(S) || !aligned16(z)) return GLA_ERR_ALIGN;
+  const size_t sb = (size_t)B * H * D * D * sizeof(float), zb = (size_t)B * H * D * sizeof(float);
+  for (const void* o : {dq, dk, dv, dg})
+    if (overlap2(S, sb, o, bytes) || overlap2(z, zb, o, bytes)) return GLA_ERR_ALIAS;
+  return GLA_OK;
+}
+
+int gla_backward_saved_ws(const void* q, const void* k, const void* v, const void* g,
+                          const void* dout, const gla_rope_tables* rope, const float* S,
+                          const float* z, void* dq, void* dk, void* dv, void* dg, int B, int N,
+                          int H, int D, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = gla_backward_saved_check(q, k, v, g, dout, rope, S, z, dq, dk, dv, dg, B, N, H, D);
+  if (rc) return rc;
+  return backward_run(q, k, v, g, dout, rope, S, z, dq, dk, dv, dg, B, N, H, D, workspace,
+                      workspace_bytes, stream);
+}
+
+int gla_backward_saved(const void* q, const void* k, const void* v, const void* g,
+                       const void* dout, const gla_rope_tables* rope, const float* S,
+                       const float* z, void* dq, void* dk, void* dv, void* dg, int B, int N, int H,
+                       int D, void* stream) {
+  int rc = gla_backward_saved_check(q, k, v, g, dout, rope, S, z, dq, dk, dv, dg, B, N, H, D);
+  if (rc) return rc;
+  const size_t need = gla_backward_workspace_bytes(B, N, H, D);
+  if (need == 0) return GLA_OK;
+  void* ws = nullptr;
+  if ((rc = get_workspace(need, stream, &ws))) return rc;
+  return backward_run(q, k, v, g, dout, rope, S, z, dq, dk, dv, dg, B, N, H, D, ws, need, stream);
 }
 
 }  // extern "C"

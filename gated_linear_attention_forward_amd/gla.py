@@ -35,6 +35,7 @@ EXPORTS = (
     "gla_forward_blocks_check", "gla_softmax_forward", "gla_softmax_forward_ws",
     "gla_softmax_workspace_bytes", "gla_softmax_forward_check", "gla_backward",
     "gla_backward_ws", "gla_backward_workspace_bytes", "gla_backward_check",
+    "gla_backward_saved", "gla_backward_saved_ws", "gla_backward_saved_check",
     "gla_forward_proj", "gla_forward_proj_ws", "gla_proj_workspace_bytes",
     "gla_forward_proj_check",
 )
@@ -98,6 +99,9 @@ def load_library():
         "gla_backward_ws": ([vp] * 5 + [rp] + [vp] * 4 + [i32] * 4 + [vp, sz, vp], i32),
         "gla_backward_workspace_bytes": ([i32] * 4, sz),
         "gla_backward_check": ([vp] * 5 + [rp] + [vp] * 4 + [i32] * 4, i32),
+        "gla_backward_saved": ([vp] * 5 + [rp] + [vp] * 6 + [i32] * 4 + [vp], i32),
+        "gla_backward_saved_ws": ([vp] * 5 + [rp] + [vp] * 6 + [i32] * 4 + [vp, sz, vp], i32),
+        "gla_backward_saved_check": ([vp] * 5 + [rp] + [vp] * 6 + [i32] * 4, i32),
         "gla_forward_proj": ([vp, vp, rp, vp] + [i32] * 5 + [vp], i32),
         "gla_forward_proj_ws": ([vp, vp, rp, vp] + [i32] * 5 + [vp, sz, vp], i32),
         "gla_proj_workspace_bytes": ([i32] * 5, sz),
@@ -503,6 +507,51 @@ def gla_backward_ws(q, k, v, g, dout, rope, ws: torch.Tensor, dq=None, dk=None, 
                                            ws.data_ptr(), ws.numel() * ws.element_size(),
                                            _stream_handle(stream, q.device)),
             "gla_backward_ws")
+    return tuple(grads)
+
+
+def gla_backward_saved_check(q, k, v, g, dout, rope, S, z, dq, dk, dv, dg, B, N, H, D) -> int:
+    """Status of the library's argument validation (pointers as integers)."""
+    return load_library().gla_backward_saved_check(q, k, v, g, dout, _rope_ptr(rope), S, z, dq,
+                                                   dk, dv, dg, B, N, H, D)
+
+
+def _saved_state_ptrs(q, S, z):
+    B, N, H, D = q.shape
+    if S is None or z is None:
+        raise ValueError("S and z are required (the forward's fp32 state)")
+    return (_check_state("S", S, (B, H, D, D), q.device),
+            _check_state("z", z, (B, H, D), q.device))
+
+
+def gla_backward_saved(q, k, v, g, dout, S, z, rope=None, dq=None, dk=None, dv=None, dg=None,
+                       stream=None):
+    """gla_backward with the forward's fp32 state S [B, H, D, D] and z [B, H, D]
+    (S_out and z_out of gla_forward_blocks with block_tokens >= N)."""
+    grads = _backward_args(q, k, v, g, dout, (dq, dk, dv, dg))
+    sp, zp = _saved_state_ptrs(q, S, z)
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_backward_saved(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                              g.data_ptr(), dout.data_ptr(), _rope_ptr(rope), sp,
+                                              zp, *(t.data_ptr() for t in grads), B, N, H, D,
+                                              _stream_handle(stream, q.device)),
+            "gla_backward_saved")
+    return tuple(grads)
+
+
+def gla_backward_saved_ws(q, k, v, g, dout, S, z, rope, ws: torch.Tensor, dq=None, dk=None,
+                          dv=None, dg=None, stream=None):
+    grads = _backward_args(q, k, v, g, dout, (dq, dk, dv, dg))
+    sp, zp = _saved_state_ptrs(q, S, z)
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_backward_saved_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                 g.data_ptr(), dout.data_ptr(), _rope_ptr(rope),
+                                                 sp, zp, *(t.data_ptr() for t in grads), B, N, H,
+                                                 D, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                                 _stream_handle(stream, q.device)),
+            "gla_backward_saved_ws")
     return tuple(grads)
 
 

@@ -271,8 +271,9 @@ int gla_softmax_forward_check(const void* q, const void* k, const void* v, const
  * (written in full), each 16-byte aligned, overlapping no input and no
  * other output.  D must be 32, 64 or 128; rope as for gla_forward (NULL:
  * RoPE off).  S and z are recomputed from k and v (no saved state is
- * needed).  The contractions run on bf16 MFMA with fp32 accumulation: S, dS,
- * the rotated features and a_n are rounded to bf16 as MFMA operands.  Uses
+ * needed; gla_backward_saved below takes the forward's).  The contractions
+ * run on bf16 MFMA with fp32 accumulation: S, dS, the rotated features and
+ * a_n are rounded to bf16 as MFMA operands.  Uses
  * a library-owned workspace (grown with hipMalloc, which may synchronise).
  * B*N*H == 0 is a no-op.  Results are bitwise reproducible. */
 int gla_backward(const void* q, const void* k, const void* v, const void* g, const void* dout,
@@ -295,6 +296,35 @@ int gla_backward_check(const void* q, const void* k, const void* v, const void* 
                        const void* dout, const gla_rope_tables* rope, const void* dq,
                        const void* dk, const void* dv, const void* dg, int B, int N, int H,
                        int D);
+
+/* gla_backward with the forward's state passed in instead of recomputed.
+ * S: device fp32 [B*H][D][D], S = sum_n R_n phi(k_n) v_n^T per head; z:
+ * device fp32 [B*H][D], z = sum_n phi(k_n): exactly what
+ * gla_forward_blocks returns in S_out and z_out with block_tokens >= N
+ * (one attention block: the bidirectional mixer, whose output equals
+ * gla_forward's) for the same q, k, v, g and rope.  Both are read only,
+ * 16-byte aligned, and overlap no output.  With that state the results are
+ * bitwise those of gla_backward (which forms the same fp32 sums itself);
+ * the pass skips the read of k and v that forms them.  Any other S and z
+ * give the gradients at that state.  Workspace as for gla_backward. */
+int gla_backward_saved(const void* q, const void* k, const void* v, const void* g,
+                       const void* dout, const gla_rope_tables* rope, const float* S,
+                       const float* z, void* dq, void* dk, void* dv, void* dg, int B, int N, int H,
+                       int D, void* stream);
+
+/* gla_backward_saved with a caller-owned device workspace of
+ * gla_backward_workspace_bytes (256-byte aligned, overlapping no tensor, S
+ * or z).  Never allocates. */
+int gla_backward_saved_ws(const void* q, const void* k, const void* v, const void* g,
+                          const void* dout, const gla_rope_tables* rope, const float* S,
+                          const float* z, void* dq, void* dk, void* dv, void* dg, int B, int N,
+                          int H, int D, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Argument validation of gla_backward_saved alone (no HIP call). */
+int gla_backward_saved_check(const void* q, const void* k, const void* v, const void* g,
+                             const void* dout, const gla_rope_tables* rope, const float* S,
+                             const float* z, const void* dq, const void* dk, const void* dv,
+                             const void* dg, int B, int N, int H, int D);
 
 /* ---------------------------------------------------------------------
  * Projection prologue fused with the mixer.

@@ -273,6 +273,33 @@ def test_backward_alias_detection():
     assert bcheck_bwd(dg=10 * A) == 0
 
 
+def scheck_bwd(**kw):
+    args = dict(q=A, k=2 * A, v=3 * A, g=4 * A, dout=5 * A, rope=None, S=11 * A, z=12 * A,
+                dq=6 * A, dk=7 * A, dv=8 * A, dg=9 * A, B=1, N=64, H=2, D=128)
+    args.update(kw)
+    return gla.gla_backward_saved_check(*(args[n] for n in (
+        "q", "k", "v", "g", "dout", "rope", "S", "z", "dq", "dk", "dv", "dg", "B", "N", "H", "D")))
+
+
+def test_backward_saved_validation():
+    assert scheck_bwd() == 0 and scheck_bwd(D=32) == 0
+    # the gradient tensors are validated as for gla_backward
+    assert scheck_bwd(D=48) == glamod.GLA_ERR_DIM
+    assert scheck_bwd(dq=A) == glamod.GLA_ERR_ALIAS
+    # the saved state: present, 16-byte aligned, overlapping no output
+    assert scheck_bwd(S=0) == glamod.GLA_ERR_NULL and scheck_bwd(z=0) == glamod.GLA_ERR_NULL
+    assert scheck_bwd(S=11 * A + 8) == glamod.GLA_ERR_ALIGN
+    assert scheck_bwd(z=12 * A + 4) == glamod.GLA_ERR_ALIGN
+    sbytes = 2 * 128 * 128 * 4
+    assert scheck_bwd(S=6 * A - sbytes + 16) == glamod.GLA_ERR_ALIAS   # S's end in dq
+    assert scheck_bwd(z=9 * A + 16) == glamod.GLA_ERR_ALIAS            # z inside dg
+    assert scheck_bwd(S=6 * A - sbytes) == 0                           # S right before dq
+    # reading the state where an input lies is allowed (both are read only)
+    assert scheck_bwd(S=A, z=2 * A) == 0
+    # nothing to do: no state needed
+    assert scheck_bwd(N=0, S=0, z=0) == 0
+
+
 def test_backward_workspace_size():
     for (B, N, H, D) in ((1, 256, 2, 32), (2, 22000, 20, 128)):
         ws = gla.gla_backward_workspace_bytes(B, N, H, D)
