@@ -64,7 +64,9 @@ Plan make_plan(int B, int N, int H, int D, int block_tokens, int output_blocks) 
   p.C = p.NB * p.CB;
 
   const int its = ceil_div(p.BT, kOutputTileTokens);
-  long long sub = (output_blocks + heads_blocks - 1) / heads_blocks;
+  // at most output_blocks blocks: a target of whole rounds of resident
+  // blocks is then never overshot into a nearly empty extra round
+  long long sub = output_blocks / heads_blocks;
   if (sub > its) sub = its;
   if (sub < 1) sub = 1;
   p.L2 = ceil_div(its, (int)sub) * kOutputTileTokens;

@@ -81,15 +81,15 @@ constexpr int kStateBlocks = 256;
 constexpr int kStateMinTilesPerWave = 2;
 constexpr int kOutputBlocks = 2048;
 // The backward pass's query and key kernels (8 waves, one block per compute
-// unit) take their token ranges from a plan made for this many blocks: a few
-// rounds of long ranges, each block staging its head's operands once.
+// unit) take their token ranges from a plan of at most this many blocks:
+// three rounds of long ranges, each block staging its head's operands once.
 constexpr int kBackwardBlocks = 768;
 // Largest RoPE table slice (bytes) a block stages in LDS; larger grids read
 // the table from global memory instead.
 constexpr int kMaxLdsTableBytes = 24 * 1024;
 
 // block_tokens <= 0 or >= N: one attention block (the bidirectional mixer).
-// output_blocks: the block count the output-side ranges (SUB, L2) aim at.
+// output_blocks: the most blocks the output-side ranges (SUB, L2) may take.
 Plan make_plan(int B, int N, int H, int D, int block_tokens = 0,
                int output_blocks = kOutputBlocks);
 
