@@ -643,10 +643,11 @@ int gla_softmax_forward(const void* q, const void* k, const void* v, const void*
 namespace {
 
 // Workspace of the backward pass: the forward plan's partials and S^T
-// operand, then the S rows operand, fp32 z, dz partials and the bf16 a tensor.
+// operand, then the S rows operand, fp32 z, the query kernel's dS and dz
+// partials (one D*D + D set per range) and the fp32 dz they reduce to.
 struct BwdLayout {
   Plan p;
-  size_t off_sl2, off_z, off_dzp, off_dz, off_a, bytes;
+  size_t off_sl2, off_z, off_dsp, off_dz, bytes;
 };
 
 BwdLayout bwd_layout(int B, int N, int H, int D) {
@@ -657,12 +658,10 @@ BwdLayout bwd_layout(int B, int N, int H, int D) {
   off = gla::align_up(off + (size_t)l.p.BH * D * D * sizeof(uint16_t), 256);
   l.off_z = off;
   off = gla::align_up(off + (size_t)l.p.BH * D * sizeof(float), 256);
-  l.off_dzp = off;
-  off = gla::align_up(off + (size_t)l.p.BH * l.p.C2 * D * sizeof(float), 256);
+  l.off_dsp = off;
+  off = gla::align_up(off + (size_t)l.p.BH * l.p.C2 * (D * D + D) * sizeof(float), 256);
   l.off_dz = off;
   off = gla::align_up(off + (size_t)l.p.BH * D * sizeof(float), 256);
-  l.off_a = off;
-  off = gla::align_up(off + (size_t)B * N * H * D * sizeof(uint16_t), 256);
   l.bytes = off;
   return l;
 }
@@ -693,8 +692,8 @@ int backward_run(const void* q, const void* k, const void* v, const void* g, con
   char* w = static_cast<char*>(workspace);
   uint16_t* sl2 = reinterpret_cast<uint16_t*>(w + l.off_sl2);
   float* zbuf = reinterpret_cast<float*>(w + l.off_z);
-  float* dzp = reinterpret_cast<float*>(w + l.off_dzp);
-  uint16_t* abuf = reinterpret_cast<uint16_t*>(w + l.off_a);
+  float* dsp = reinterpret_cast<float*>(w + l.off_dsp);
+  float* dzbuf = reinterpret_cast<float*>(w + l.off_dz);
   hipStream_t s = static_cast<hipStream_t>(stream);
   gla::BArgs bw{};
   bw.dout = static_cast<const uint16_t*>(dout);
@@ -702,10 +701,9 @@ int backward_run(const void* q, const void* k, const void* v, const void* g, con
   bw.dk = static_cast<uint16_t*>(dk);
   bw.dv = static_cast<uint16_t*>(dv);
   bw.dg = static_cast<uint16_t*>(dg);
-  bw.abuf = abuf;
   bw.z = zbuf;
-  bw.dzp = dzp;
-  bw.dz = reinterpret_cast<float*>(w + l.off_dz);
+  bw.dsp = dsp;
+  bw.dz = dzbuf;
   bw.C2 = p.C2;
 
   // 1. S (both operand layouts) and fp32 z: from k and v, or from the saved
@@ -725,19 +723,23 @@ int backward_run(const void* q, const void* k, const void* v, const void* g, con
     a1.v = static_cast<const uint16_t*>(v);
     if ((rc = status_of(gla::launch_state(p, a1, s)))) return rc;
   }
-  // 2. query side: dq, dg, a, dz partials
+  // 2. query side: dq, dg and the dS and dz partials of each range
   gla::KArgs a2 = kernel_args(p, rope, p.L2, p.SUB, workspace);
   a2.q = static_cast<const uint16_t*>(q);
   a2.g = static_cast<const uint16_t*>(g);
   a2.sl2 = sl2;
   if ((rc = status_of(gla::launch_bwd_query(p, a2, bw, s)))) return rc;
-  // 3. dS (both operand layouts) from q and a: the state pass with q, a in
-  //    the places of k, v
-  gla::KArgs a3 = kernel_args(p, rope, p.L, p.CB, workspace);
-  a3.k = static_cast<const uint16_t*>(q);
-  a3.v = abuf;
+  // 3. dS (both operand layouts) and fp32 dz: the reduce kernel over the C2
+  //    range partials of each head
+  Plan p3 = p;
+  p3.CB = p.C2;
+  p3.C = p.C2;
+  p3.NB = 1;
+  gla::KArgs a3 = kernel_args(p3, rope, p.L2, p.C2, workspace);
+  a3.part = dsp;
   a3.sl2 = sl2;
-  if ((rc = status_of(gla::launch_state(p, a3, s)))) return rc;
+  a3.z_out = dzbuf;
+  if ((rc = status_of(gla::launch_reduce_state(p3, a3, s)))) return rc;
   // 4. key side: dk, dv
   gla::KArgs a4 = kernel_args(p, rope, p.L2, p.SUB, workspace);
   a4.k = static_cast<const uint16_t*>(k);

@@ -14,12 +14,14 @@
 // The pass runs as:
 //   1. the forward's state and reduce kernels on (k, v): S and z, with S in
 //      two bf16 operand layouts (rows of S^T, as the output kernel takes it,
-//      and rows of S) and z in fp32;
+//      and rows of S) and z in fp32 (or the reduce kernel alone on a state
+//      the caller saved from the forward);
 //   2. the query kernel here: per token num and den as in the output kernel,
-//      then dg, a (bf16, written out for step 3), dden, S a on MFMA, and dq;
-//      each block also sums its tokens' dden fq into a dz partial;
-//   3. the forward's state and reduce kernels again, on (q, a): dS in the
-//      same two operand layouts;
+//      then dg, a, dden, S a on MFMA, and dq; each block also contracts its
+//      tokens' rq a^T into a dS partial and sums their dden fq into a dz
+//      partial;
+//   3. the reduce kernel on those partials: dS in the same two operand
+//      layouts, and dz in fp32;
 //   4. the key kernel here: dv and dS v on MFMA per token, dk.
 // Steps 2 and 4 use the output kernel's MFMA orientation (16x16x32, tokens
 // as the A operand, lane l holding token l % 16 and features
@@ -46,17 +48,25 @@ struct BwdCfg {
   static constexpr int OB = 2 * MB;   // bytes a lane owns of one token row
   static constexpr int PU = D / 32;   // rotation pairs in those bytes
   static constexpr int PITCH = 2 * D;  // row tiles are unpadded and swizzled (row_tile_offset)
-  // query kernel LDS: S^T rows + z rows, S rows, fp32 z, per-wave a tiles
+  // query kernel LDS: S^T rows + z rows, S rows, fp32 z, then two
+  // token-major tiles of the block's 16 NW tokens per step, rq = R phi(q)
+  // and a, at a row pitch the transposing reads take without bank conflicts
+  static constexpr int TP = tile_pitch(2 * D);
   static constexpr int Q_SR = (D + 2) * PITCH;
   static constexpr int Q_ZF = Q_SR + D * PITCH;
   static constexpr int Q_AT = Q_ZF + 4 * D;
-  static constexpr int Q_BYTES = Q_AT + kQueryWaves * 16 * PITCH;
+  static constexpr int Q_RQ = Q_AT + 16 * kQueryWaves * TP;
+  static constexpr int Q_BYTES = Q_RQ + 16 * kQueryWaves * TP;
+  // dS tiles of 32 x 32: wave w owns tiles w, w + NW, ... (row block
+  // t / (D / 32) of rq features, column block t % (D / 32) of a features)
+  static constexpr int NTI = (D / 32) * (D / 32);
+  static constexpr int TPW = (NTI + kQueryWaves - 1) / kQueryWaves;
   // key kernel LDS: dS^T rows, dS rows, fp32 dz
   static constexpr int K_SR = D * PITCH;
   static constexpr int K_ZF = 2 * D * PITCH;
   static constexpr int K_BYTES = K_ZF + 4 * D;
-  static_assert(Q_AT % 16 == 0 && K_ZF % 16 == 0, "16-byte aligned sections");
-  static_assert(kQueryWaves * D * 4 <= kQueryWaves * 16 * PITCH, "dz scratch fits the a tiles");
+  static_assert(Q_AT % 16 == 0 && Q_RQ % 16 == 0 && K_ZF % 16 == 0, "16-byte aligned sections");
+  static_assert(kQueryWaves * D * 4 <= 16 * kQueryWaves * TP, "dz scratch fits the a tile");
 };
 
 // (cos, sin) of the PU rotation pairs PU col + u (u < PU) of token n: the
@@ -114,30 +124,41 @@ __device__ __forceinline__ void contract_rows(const unsigned char* op, const bf1
 // ---------------------------------------------------------------------------
 // Query kernel.  Block = 8 waves, one (token range, head); grid (B H, C2).
 // LDS holds the head's S^T operand and z rows (as in the output kernel), the
-// S rows operand, fp32 z, and one 16-token tile per wave that turns a from
-// the accumulator layout into the A-operand layout.  Per 16-token step:
+// S rows operand, fp32 z, and two token-major tiles of the block's 128
+// tokens per step: rq = R phi(q) and a.  Per block step, each wave takes 16
+// tokens:
 //   - phi(q) against the z rows gives den, R phi(q) against S^T gives num;
+//     R phi(q) goes to the rq tile;
 //   - per owned column: s = sigmoid(g), o = s num / den, a = dout s / den,
 //     dg = dout o (1 - s) (1 - s = e^-g s), and the row sums of dout o;
-//   - dg and a (bf16) are stored; a also goes to the wave's LDS tile;
+//   - dg is stored and a (bf16) goes to the a tile;
 //   - dden = -(dout . o) / den from a 16-lane DPP sum;
-//   - S a on MFMA from the tile and the S rows operand, rotated back by R^T,
-//     plus dden z, masked by q > 0: dq;
+//   - S a on MFMA from the a tile and the S rows operand, rotated back by
+//     R^T, plus dden z, masked by q > 0: dq;
 //   - dden phi(q) accumulates into the lane's dz partial.
+// After an LDS barrier every wave adds the block step's rq a^T to the 32 x 32
+// tiles of dS it owns (v_mfma_f32_32x32x16_bf16 over the 128 tokens, both
+// operands read with transposing LDS reads as in the state kernel), and a
+// second barrier frees the tiles for the next step.  At the end the block
+// writes its dS partial and its dz partial, which the reduce kernel sums.
 // The loads form a ring: each class (q in the A layout, g and dout, q in the
 // row layout) is refilled for the next step as soon as this step is done with
-// it, so every wait is for loads issued a step earlier.
+// it.  The barriers wait for LDS only, so those loads stay in flight.
+// Every wave runs every block step; tokens past the range load zeros and add
+// nothing (rq and a are zero there).
 template <int D, bool ROPE, bool TLDS>
 __global__ __launch_bounds__(64 * kQueryWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_query_kernel(KArgs a, BArgs bw) {
   using Cf = BwdCfg<D>;
-  constexpr int KS = Cf::KS, MB = Cf::MB, OB = Cf::OB, PU = Cf::PU, PITCH = Cf::PITCH;
+  constexpr int KS = Cf::KS, MB = Cf::MB, OB = Cf::OB, PU = Cf::PU, TP = Cf::TP;
   constexpr int NW = kQueryWaves, NT = 64 * NW;
   using OChunk = typename Chunk<OB>::T;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char* sS = smem;
   unsigned char* sR = smem + Cf::Q_SR;
   float* zf = reinterpret_cast<float*>(smem + Cf::Q_ZF);
+  unsigned char* atile = smem + Cf::Q_AT;
+  unsigned char* rqtile = smem + Cf::Q_RQ;
   float2* ltab = reinterpret_cast<float2*>(smem + Cf::Q_BYTES);
 
   const int tid = threadIdx.x;
@@ -145,7 +166,6 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int m = lane >> 4;
   const int col = lane & 15;
-  unsigned char* at = smem + Cf::Q_AT + wave * 16 * PITCH;
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
   const int c = blockIdx.y;
@@ -181,7 +201,6 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(bw.dout + boff, a.slab_bytes);
   const __amdgpu_buffer_rsrc_t rdq = make_rsrc(bw.dq + boff, a.slab_bytes);
   const __amdgpu_buffer_rsrc_t rdg = make_rsrc(bw.dg + boff, a.slab_bytes);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(bw.abuf + boff, a.slab_bytes);
   const uint32_t tokstride = (uint32_t)a.H * D * 2;
   const uint32_t qoff = (uint32_t)h * D * 2 + 16u * m;            // A operand chunk
   const uint32_t roff = (uint32_t)h * D * 2 + (uint32_t)OB * col;  // owned row bytes
@@ -218,13 +237,22 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
   float dzacc[MB];
 #pragma unroll
   for (int j = 0; j < MB; ++j) dzacc[j] = 0.f;
+  f32x16 dsacc[Cf::TPW];
+#pragma unroll
+  for (int t = 0; t < Cf::TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dsacc[t][r] = 0.f;
+
+  // this wave's rows of the two tiles
+  unsigned char* my_a = atile + 16 * wave * TP;
+  unsigned char* my_rq = rqtile + 16 * wave * TP;
 
   int base = n_begin + 16 * wave;
   issue_q(base);
   issue_gd(base);
   issue_qc(base);
   wait_vmem_all();
-  for (; base < n_end; base += 16 * NW) {
+  for (int bs = n_begin; bs < n_end; bs += 16 * NW, base += 16 * NW) {
     const int next = base + 16 * NW;
     __builtin_amdgcn_sched_barrier(0);
     RowOff rof{};
@@ -251,6 +279,10 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
       Aq[s2] = __builtin_bit_cast(bf16x8, ROPE ? rope_chunk<D, s2>(fq[s2], tv, rof, m) : fq[s2]);
     });
     issue_q(next);
+    // R phi(q) of token col, features 32 s + 8 m .. + 7, into the rq tile
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+      *reinterpret_cast<bf16x8*>(my_rq + col * TP + 16 * (4 * s2 + m)) = Aq[s2];
     __builtin_amdgcn_sched_barrier(0);
 
     f32x4 acc[MB];
@@ -284,10 +316,8 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
         wa[w] = pack_bf16(av[0], av[1]);
         wg[w] = pack_bf16(gvv[0], gvv[1]);
       }
-      const uint32_t o = r_offset(base, i);
-      store_chunk_nt<OB>(rdg, o, wg);
-      store_chunk_nt<OB>(ra, o, wa);
-      *reinterpret_cast<OChunk*>(at + row_tile_offset<D>(4 * m + i, OB * col)) = wa;
+      store_chunk_nt<OB>(rdg, r_offset(base, i), wg);
+      *reinterpret_cast<OChunk*>(my_a + (4 * m + i) * TP + OB * col) = wa;
     }
     issue_gd(next);
     __builtin_amdgcn_sched_barrier(0);
@@ -301,7 +331,7 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
     bf16x8 Aa[KS];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2)
-      Aa[s2] = *reinterpret_cast<const bf16x8*>(at + row_tile_offset<D>(col, 16 * (4 * s2 + m)));
+      Aa[s2] = *reinterpret_cast<const bf16x8*>(my_a + col * TP + 16 * (4 * s2 + m));
     f32x4 acc2[MB];
     contract_rows<D>(sR, Aa, col, m, acc2);
 
@@ -329,8 +359,41 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
       store_chunk_nt<OB>(rdq, r_offset(base, i), wq);
     }
     issue_qc(next);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // dS += rq a^T over the block step's 16 NW tokens
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < NW; ++ks) {
+      const unsigned char* rt = rqtile + 16 * ks * TP;
+      const unsigned char* at = atile + 16 * ks * TP;
+#pragma unroll
+      for (int t = 0; t < Cf::TPW; ++t) {
+        const int ti = wave + NW * t;
+        if (Cf::NTI % NW == 0 || ti < Cf::NTI) {
+          const bf16x8 A = frag_tr(rt, TP, ti / (D / 32), lane);
+          const bf16x8 B = frag_tr(at, TP, ti % (D / 32), lane);
+          dsacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, dsacc[t], 0, 0, 0);
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
+  // the block's dS partial: element (d, e) of tile ti at row 32 (ti / (D/32)) + d
+  float* dst = bw.dsp + ((size_t)bh * bw.C2 + c) * (size_t)(D * D + D);
+#pragma unroll
+  for (int t = 0; t < Cf::TPW; ++t) {
+    const int ti = wave + NW * t;
+    if (Cf::NTI % NW == 0 || ti < Cf::NTI) {
+      const int ib = ti / (D / 32), jb = ti % (D / 32);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * ib + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        dst[d * D + 32 * jb + (lane & 31)] = dsacc[t][r];
+      }
+    }
+  }
   // dz of the block: lanes of one column hold the same features; then the
   // waves in order
 #pragma unroll
@@ -338,8 +401,7 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
     dzacc[j] += __shfl_xor(dzacc[j], 16);
     dzacc[j] += __shfl_xor(dzacc[j], 32);
   }
-  __syncthreads();  // every wave is done with its a tile
-  float* zw = reinterpret_cast<float*>(smem + Cf::Q_AT);
+  float* zw = reinterpret_cast<float*>(atile);  // free after the last barrier
   if (m == 0) {
 #pragma unroll
     for (int j = 0; j < MB; ++j) zw[wave * D + MB * col + j] = dzacc[j];
@@ -349,28 +411,8 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
     float sum = zw[tid];
 #pragma unroll
     for (int w = 1; w < NW; ++w) sum += zw[w * D + tid];
-    bw.dzp[((size_t)bh * bw.C2 + c) * D + tid] = sum;
+    dst[D * D + tid] = sum;
   }
-}
-
-// ---------------------------------------------------------------------------
-// dz of each head: the query kernel's range partials summed in range order
-// (one thread per feature; loads eight ranges ahead of the sum).
-template <int D>
-__global__ __launch_bounds__(D) void dz_sum_kernel(BArgs bw) {
-  const int bh = blockIdx.x, d = threadIdx.x;
-  const float* p = bw.dzp + (size_t)bh * bw.C2 * D + d;
-  float sum = 0.f;
-  int c = 0;
-  for (; c + 8 <= bw.C2; c += 8) {
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = p[(size_t)(c + i) * D];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sum += x[i];
-  }
-  for (; c < bw.C2; ++c) sum += p[(size_t)c * D];
-  bw.dz[(size_t)bh * D + d] = sum;
 }
 
 // Key kernel.  Block = 8 waves (the two operands take about half the LDS,
@@ -532,7 +574,10 @@ hipError_t launch_rows_kernel(const Plan& p, const KArgs& a, const BArgs& b, int
 
 template <int D>
 hipError_t launch_bwd_query_d(const Plan& p, const KArgs& a, const BArgs& b, hipStream_t s) {
-  const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;
+  // the table goes to LDS when it fits beside the operands and the two tiles
+  // (160 KB per compute unit); otherwise the kernel reads it from memory
+  const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes &&
+                  BwdCfg<D>::Q_BYTES + table_lds_bytes(a) <= 160 * 1024;
   const size_t lds = BwdCfg<D>::Q_BYTES + (tl ? table_lds_bytes(a) : 0);
   constexpr int T = 64 * kQueryWaves;
   if (!a.cs) return launch_rows_kernel<bwd_query_kernel<D, false, false>>(p, a, b, T, lds, s);
@@ -542,9 +587,6 @@ hipError_t launch_bwd_query_d(const Plan& p, const KArgs& a, const BArgs& b, hip
 
 template <int D>
 hipError_t launch_bwd_key_d(const Plan& p, const KArgs& a, const BArgs& b, hipStream_t s) {
-  hipLaunchKernelGGL((dz_sum_kernel<D>), dim3(p.BH), dim3(D), 0, s, b);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;
   const size_t lds = BwdCfg<D>::K_BYTES + (tl ? table_lds_bytes(a) : 0);
   constexpr int T = 64 * kKeyWaves;

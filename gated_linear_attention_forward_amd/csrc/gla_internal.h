@@ -110,18 +110,17 @@ struct BArgs {
   uint16_t* dk;
   uint16_t* dv;
   uint16_t* dg;
-  uint16_t* abuf;        // [B, N, H, D] bf16: a = dout * sigmoid(g) / den
   const float* z;        // forward z [BH][D] fp32
-  float* dzp;            // [BH][C2][D] fp32 per-range partial sums of dz
-  float* dz;             // [BH][D] fp32 dz, the partials summed in range order
+  float* dsp;            // [BH][C2][D*D + D] fp32 per-range partials: dS = sum rq a^T
+                         // (row-major, rq features by a features), then dz
+  const float* dz;       // [BH][D] fp32 dz (the reduce of dsp's last D entries)
   int C2;                // query/key kernel ranges per head
 };
 // Query side: reads q, g, dout and the state operands a.sl (S^T rows + z
-// rows) and a.sl2 (S rows); writes dq, dg, abuf and dzp.
+// rows) and a.sl2 (S rows); writes dq, dg and the dS and dz partials dsp.
 hipError_t launch_bwd_query(const Plan& p, KArgs a, BArgs b, hipStream_t stream);
-// Key side: sums dzp into dz (one small kernel), then reads k, v, the
-// gradient-state operands a.sl (dS^T rows) and a.sl2 (dS rows) and dz;
-// writes dk, dv.
+// Key side: reads k, v, the gradient-state operands a.sl (dS^T rows) and
+// a.sl2 (dS rows) and dz; writes dk, dv.
 hipError_t launch_bwd_key(const Plan& p, KArgs a, BArgs b, hipStream_t stream);
 
 // Projection prologue (gla_project.hip): q, k, v, g = x W^T per map.

@@ -281,8 +281,9 @@ int gla_backward(const void* q, const void* k, const void* v, const void* g, con
                  int N, int H, int D, void* stream);
 
 /* Workspace bytes gla_backward_ws needs (the forward's partials and state
- * operands, the S rows operand, z, dz partials and the bf16 a_n tensor of
- * B*N*H*D elements), 0 for bad shapes or B*N*H == 0. */
+ * operands, the S rows operand, z, and one fp32 dS and dz partial of
+ * D*D + D floats per head and token range), 0 for bad shapes or
+ * B*N*H == 0. */
 size_t gla_backward_workspace_bytes(int B, int N, int H, int D);
 
 /* gla_backward with a caller-owned device workspace (>= the size above,
