@@ -106,6 +106,8 @@ def counter_traffic(workload_name, path=COUNTERS, field="output_kernel_traffic_b
                 fields[key.strip()] = val.strip()
     if fields.get("kernel_source_sha256") != kernel_source_digest(sources):
         return None, "kernel source changed since the counters were taken"
+    if field not in fields:
+        return None, f"no {field} in the counter summary"
     return float(fields[field]), os.path.relpath(path, ROOT)
 
 
@@ -358,7 +360,7 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "D": w.D,
                    "grid": [w.T, w.Hh, w.W], "parallelism": "single-gpu"},
-        "roofline": {"kernel": "whole backward (state, query, gradient state, key kernels)",
+        "roofline": {"kernel": "whole backward (state, reduce, query, reduce, key kernels)",
                      "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "traffic_source": traffic_src,
@@ -385,10 +387,14 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
     torch.cuda.synchronize()
     sv_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     sv_achieved = nbytes / (sv_ms * 1e-3) / 1e9
+    sv_traffic, _ = counter_traffic(w.name, BWD_COUNTERS, "saved_state_pass_traffic_bytes",
+                                    BWD_SOURCES)
     result["saved_state"] = {
         "entry": "gla_backward_saved_ws", "value": w.B * w.N / (sv_ms * 1e-3), "unit": "tokens/s",
         "avg_ms": sv_ms, "achieved": sv_achieved, "peak": PEAK_HBM_GBPS, "unit_roofline": "GB/s",
-        "frac": sv_achieved / PEAK_HBM_GBPS, "algorithmic_bytes": nbytes}
+        "frac": sv_achieved / PEAK_HBM_GBPS, "traffic": sv_traffic,
+        "traffic_over_algorithmic": sv_traffic / nbytes if sv_traffic else None,
+        "algorithmic_bytes": nbytes}
     if not args.no_cpu_baseline:
         log("bench: timing the oracle (cpu_baseline)")
         q, k, v, g = (t.cpu() for t in tensors)
