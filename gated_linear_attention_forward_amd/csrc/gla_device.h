@@ -29,14 +29,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            kRsrcWord3);
 }
 
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
 // Stores of the output stream carry the non-temporal hint (cache policy bit
 // nt): nothing reads them back, and without the hint their write-back lands
 // in the next pass's state kernel instead of this one.
 constexpr int kCpolNt = 2;
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+// The state kernels' k and v loads carry the hint too: each byte is read
+// once.  Measured on the layer shapes: 1-3% off the forward pass.  (On the
+// output kernel's q and g loads it cost 1-3% instead.)
+__device__ __forceinline__ u32x4 load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNt);
+}
 
 __device__ __forceinline__ void store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNt);

@@ -101,8 +101,8 @@ struct StateWave {
     const uint32_t off = (it < nit && n < n_end) ? (uint32_t)n * tokstride + headoff : kOob;
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-      kr[st][s2] = load16(rk, off + 64u * s2);
-      vr[st][s2] = load16(rv, off + 64u * s2);
+      kr[st][s2] = load16_nt(rk, off + 64u * s2);
+      vr[st][s2] = load16_nt(rv, off + 64u * s2);
     }
   }
 
@@ -375,8 +375,8 @@ struct HalfWave {
     for (int i = 0; i < NI; ++i) {
       const int n = token(it, i);
       const uint32_t off = (it < nit && n < n_end) ? (uint32_t)n * tokstride + hoff : kOob;
-      kr[st][i] = load16(rk, off);
-      vr[st][i] = load16(rv, off);
+      kr[st][i] = load16_nt(rk, off);
+      vr[st][i] = load16_nt(rv, off);
     }
   }
 
