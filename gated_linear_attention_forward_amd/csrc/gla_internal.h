@@ -82,8 +82,8 @@ constexpr int kStateMinTilesPerWave = 2;
 constexpr int kOutputBlocks = 2048;
 // The backward pass's query and key kernels (8 waves, one block per compute
 // unit) take their token ranges from a plan of at most this many blocks:
-// three rounds of long ranges, each block staging its head's operands once.
-constexpr int kBackwardBlocks = 768;
+// one round of long ranges, each block staging its head's operands once.
+constexpr int kBackwardBlocks = 256;
 // Largest RoPE table slice (bytes) a block stages in LDS; larger grids read
 // the table from global memory instead.
 constexpr int kMaxLdsTableBytes = 24 * 1024;
