@@ -418,9 +418,9 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
 // Key kernel.  Block = 8 waves (the two operands take about half the LDS,
 // so one block per compute unit: 8 waves make two per SIMD), one (token
 // range, head); grid (B H, C2).
-// LDS holds the head's dS^T and dS row operands and fp32 dz.  Per 16-token step: R phi(k) against dS^T gives
-// dv; v (as loaded) against dS rows gives dS v, rotated back by R^T, plus dz,
-// masked by k > 0: dk.
+// LDS holds the head's dS^T and dS row operands and fp32 dz.  Per 16-token
+// step: R phi(k) against dS^T gives dv; v (as loaded) against dS rows gives
+// dS v, rotated back by R^T, plus dz, masked by k > 0: dk.
 template <int D, bool ROPE, bool TLDS>
 __global__ __launch_bounds__(64 * kKeyWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_key_kernel(KArgs a, BArgs bw) {
