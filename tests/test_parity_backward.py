@@ -90,6 +90,22 @@ def test_backward_small_shapes(B, H, D, grid, rope):
             assert_close(a, b, name)
 
 
+@pytest.mark.parametrize("D", [32, 64])
+def test_backward_long_ranges(D):
+    """D = 32 and 64 over 100,000 tokens: every block's range spans several
+    128-token steps of the query kernel's dS contraction (the layer shapes
+    cover D = 128), with RoPE and a ragged tail, against the full oracle."""
+    B, H, grid = 1, 2, (25, 40, 101)
+    N = grid[0] * grid[1] * grid[2]
+    say(f"case backward long ranges B={B} H={H} D={D} grid={grid} N={N}")
+    q, k, v, g = random_inputs(B, N, H, D, seed=1300 + D)
+    dout = random_grad(B, N, H, D, seed=1400 + D)
+    got = gpu_backward(q, k, v, g, dout, grid)
+    ref = oracle.backward(q, k, v, g, dout, oracle.Grid(*grid))
+    for name, a, b in zip(NAMES, got, ref):
+        assert_close(a, b, name)
+
+
 def rounding_envelope(q, k, v, g, dout, grid):
     """Norms of the dot-product error envelopes of dq and dk: with operands
     rounded to bf16, a dot product sum_e x_e y_e is off by at most about
