@@ -8,6 +8,7 @@ csrc/); this package is its thin ctypes binding.
 """
 from .gla import (  # noqa: F401
     EXPORTS,
+    GatedLinearAttention,
     GlaError,
     RopeTables,
     alloc_workspace,
@@ -46,5 +47,6 @@ from .gla import (  # noqa: F401
     gla_strerror,
     gla_workspace_bytes,
     gla_workspace_bytes_blocks,
+    gated_linear_attention,
     load_library,
 )

@@ -615,3 +615,35 @@ def gla_forward_proj_ws(x, w, H: int, D: int, rope, ws: torch.Tensor, out=None, 
                                                _stream_handle(stream, x.device)),
             "gla_forward_proj_ws")
     return out
+
+
+# ---------------------------------------------------------------------------
+# autograd: the forward keeps its fp32 state for the backward pass
+
+
+class GatedLinearAttention(torch.autograd.Function):
+    """o = mixer(q, k, v, g) with gradients through the library: the forward
+    runs gla_forward_blocks over one attention block (the bidirectional mixer)
+    and keeps S and z (fp32, B*H*(D*D + D) floats); the backward runs
+    gla_backward_saved on them.  rope: RopeTables or None, not differentiated."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, rope=None):
+        B, N, H, D = q.shape
+        S = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        z = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+        out = gla_forward_blocks(q, k, v, g, rope, max(N, 1), None, None, S, z)
+        ctx.save_for_backward(q, k, v, g, S, z)
+        ctx.rope = rope
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, g, S, z = ctx.saved_tensors
+        grads = gla_backward_saved(q, k, v, g, dout.contiguous(), S, z, ctx.rope)
+        return (*grads, None)
+
+
+def gated_linear_attention(q, k, v, g, rope=None) -> torch.Tensor:
+    """The mixer as a differentiable torch op (see GatedLinearAttention)."""
+    return GatedLinearAttention.apply(q, k, v, g, rope)

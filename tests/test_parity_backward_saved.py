@@ -137,3 +137,24 @@ def test_saved_state_empty_and_errors():
         gla.gla_backward_saved(q, q, q, q, q, S[:, :1], z)
     with pytest.raises(ValueError):
         gla.gla_backward_saved(q, q, q, q, q, None, z)
+
+
+@pytest.mark.parametrize("rope", [True, False])
+def test_autograd_function_matches_the_entry_points(rope):
+    """gated_linear_attention under torch.autograd: the forward equals
+    gla_forward and the gradients equal gla_backward's, bit for bit."""
+    B, H, D, grid = 2, 3, 64, (3, 5, 7)
+    N = grid[0] * grid[1] * grid[2]
+    say(f"case autograd function B={B} H={H} D={D} grid={grid} rope={rope}")
+    q, k, v, g = (t.to(DEV) for t in random_inputs(B, N, H, D, seed=1500 + N))
+    dout = random_grad(B, N, H, D, seed=1550 + N).to(DEV)
+    tables = gla.gla_rope_create(*grid, D) if rope else None
+    leaves = [t.clone().requires_grad_(True) for t in (q, k, v, g)]
+    out = gla.gated_linear_attention(*leaves, tables)
+    out.backward(dout)
+    assert torch.equal(out.detach(), gla.gla_forward(q, k, v, g, tables))
+    ref = gla.gla_backward(q, k, v, g, dout, tables)
+    for name, leaf, r in zip(NAMES, leaves, ref):
+        assert torch.equal(leaf.grad, r), f"{name} differs from gla_backward"
+    if tables is not None:
+        tables.close()
