@@ -300,6 +300,23 @@ def test_backward_saved_validation():
     assert scheck_bwd(N=0, S=0, z=0) == 0
 
 
+def test_backward_saved_state_must_not_overlap_the_workspace():
+    """The _ws entry point refuses a saved state inside its workspace before
+    any HIP call (fake addresses: validation never dereferences them)."""
+    lib = gla.load_library()
+    B, N, H, D = 1, 64, 2, 128
+    need = gla.gla_backward_workspace_bytes(B, N, H, D)
+    ws = 64 * A                                   # 256-byte aligned
+    args = [A, 2 * A, 3 * A, 4 * A, 5 * A, None]  # q, k, v, g, dout, rope
+    outs = [6 * A, 7 * A, 8 * A, 9 * A]
+
+    def call(S, z):
+        return lib.gla_backward_saved_ws(*args, S, z, *outs, B, N, H, D, ws, need, None)
+
+    assert call(ws + 256, 12 * A) == glamod.GLA_ERR_ALIAS          # S inside
+    assert call(11 * A, ws + need - 16) == glamod.GLA_ERR_ALIAS    # z at the end
+
+
 def test_backward_workspace_size():
     for (B, N, H, D) in ((1, 256, 2, 32), (2, 22000, 20, 128)):
         ws = gla.gla_backward_workspace_bytes(B, N, H, D)
