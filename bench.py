@@ -13,6 +13,10 @@ from HIP events recorded around it, on the stream it runs on, in K further
 passes right after; `traffic` is its HBM bytes per
 launch from the committed rocprofv3 byte counters (profiles/), or null when
 the kernel source differs from the one those counters were taken on.
+`cold_cache_median_ms` gives the median times of K more passes, each after a
+512 MiB read that evicts the last-level cache: the same as the rest on the
+5B 720p shapes, whose tensors exceed that cache, and the honest figure on
+the small shapes, whose tensors would otherwise be read from it.
 `cpu_baseline` times the fp64 oracle on a sample of the workload's heads
 (about ten seconds of CPU work) and scales to the whole workload.
 
@@ -27,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -188,6 +193,7 @@ def block_bench(args, w, gla, dev, tensors, out, rope, stream):
 
 
 PEAK_BF16_TFLOPS = 2500.0
+EVICT_BYTES = 512 << 20   # twice the MI355X's 256 MB last-level cache (MALL)
 
 
 def softmax_cpu_baseline(w, q, k, v, g, min_seconds=10.0):
@@ -605,6 +611,28 @@ def main():
     state_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     out_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     ev_step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
+
+    # K more passes from a cold cache: before each, outside its events, a
+    # 512 MiB read on the same stream evicts the 256 MB last-level cache
+    # (MALL), so a workload whose tensors fit in it is still read from HBM.
+    # A read, not a write: lines a write leaves dirty would be written back
+    # inside the next pass (about 50 us at 5B 720p), which no steady state of
+    # the mixer itself causes.
+    cold_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                for _ in range(args.steps)]
+    scratch = torch.zeros(EVICT_BYTES // 4, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):   # settle the zero fill's write-backs
+        scratch.sum()
+        step()
+    log(f"bench: {args.steps} instrumented steps after cache eviction")
+    for i in range(args.steps):
+        scratch.sum()
+        step(cold_evs[i])
+    torch.cuda.synchronize()
+    del scratch
+    cold_state = statistics.median(e[0].elapsed_time(e[1]) for e in cold_evs)
+    cold_out = statistics.median(e[1].elapsed_time(e[2]) for e in cold_evs)
+    cold_step = statistics.median(e[0].elapsed_time(e[2]) for e in cold_evs)
     units = w.B * w.N * w.H
     out_bytes = 6 * w.D * units        # q, g read + out written, bf16
     state_bytes = 4 * w.D * units      # k, v read, bf16
@@ -629,6 +657,9 @@ def main():
                    "grid": [w.T, w.Hh, w.W], "parallelism": "single-gpu"},
         "hbm_gbps_effective": all_bytes / (ms_step * 1e-3) / 1e9,
         "phases_ms": {"state": state_ms, "output": out_ms, "step_events": ev_step_ms},
+        "cold_cache_median_ms": {"state": cold_state, "output": cold_out, "step_events": cold_step,
+                                 "evict_bytes": EVICT_BYTES,
+                                 "output_frac": out_bytes / (cold_out * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "roofline": {
             "kernel": "output_kernel",
             "bound": "hbm",
