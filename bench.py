@@ -3,7 +3,10 @@
 One step = one whole pass of the hot path over one batch: the state half
 (state kernel + cross-chunk reduction, reading k and v) and the output half
 (output kernel, reading q and g, writing out), launched through the C ABI on
-torch's current stream with inputs already resident in HBM.
+torch's current stream with inputs already resident in HBM.  Passes cycle
+through three copies of the inputs, so no pass finds its inputs left in the
+256 MB last-level cache by the pass before (the forward, block-causal and
+backward benches).
 
 Prints ONE JSON line.  `value` is tokens/s per layer (B*N tokens per step).
 `value` and `ms_per_step` come from K uninstrumented passes (wall clock,
@@ -142,25 +145,28 @@ def block_bench(args, w, gla, dev, tensors, out, rope, stream):
     z = torch.zeros((w.B, w.H, w.D), dtype=torch.float32, device=dev)
     ws = gla.alloc_workspace_blocks(w.B, w.N, w.H, w.D, L, dev)
 
-    def step():
-        gla.gla_forward_blocks_ws(qd, kd, vd, gd, rope, L, ws, S, z, S, z, out, stream)
+    sets = input_sets((qd, kd, vd, gd))
+
+    def step(i=0):
+        qs, ks, vs, gs = sets[i % len(sets)]
+        gla.gla_forward_blocks_ws(qs, ks, vs, gs, rope, L, ws, S, z, S, z, out, stream)
 
     log(f"bench: block-causal, {args.block_frames} frames ({L} tokens) per block; "
         f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     log(f"bench: {args.steps} instrumented steps")
-    for e in evs:
+    for i, e in enumerate(evs):
         e[0].record(stream)
-        step()
+        step(i)
         e[1].record(stream)
     torch.cuda.synchronize()
     ev_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
@@ -194,6 +200,14 @@ def block_bench(args, w, gla, dev, tensors, out, rope, stream):
 
 PEAK_BF16_TFLOPS = 2500.0
 EVICT_BYTES = 512 << 20   # twice the MI355X's 256 MB last-level cache (MALL)
+ROTATE = 3                # input sets the HBM-bound benches cycle through
+
+
+def input_sets(tensors, n=ROTATE):
+    """n copies of the device inputs (the first is the given tensors): pass i
+    reads set i % n, so no pass finds its inputs left in the last-level cache
+    by the pass before, as it would when one set is read over and over."""
+    return [tuple(tensors)] + [tuple(t.clone() for t in tensors) for _ in range(n - 1)]
 
 
 def softmax_cpu_baseline(w, q, k, v, g, min_seconds=10.0):
@@ -334,24 +348,27 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
     grads = [torch.empty_like(qd) for _ in range(4)]
     ws = gla.alloc_workspace_backward(w.B, w.N, w.H, w.D, dev)
 
-    def step():
-        gla.gla_backward_ws(qd, kd, vd, gd, dout, rope, ws, *grads, stream=stream)
+    sets = input_sets((qd, kd, vd, gd, dout))
+
+    def step(i=0):
+        qs, ks, vs, gs, ds = sets[i % len(sets)]
+        gla.gla_backward_ws(qs, ks, vs, gs, ds, rope, ws, *grads, stream=stream)
 
     log(f"bench: backward; warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     log(f"bench: {args.steps} instrumented steps")
-    for e in evs:
+    for i, e in enumerate(evs):
         e[0].record(stream)
-        step()
+        step(i)
         e[1].record(stream)
     torch.cuda.synchronize()
     ev_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
@@ -388,16 +405,17 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
     z = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev)
     gla.gla_forward_blocks(qd, kd, vd, gd, rope, w.N, None, None, S, z, stream=stream)
 
-    def step_saved():
-        gla.gla_backward_saved_ws(qd, kd, vd, gd, dout, S, z, rope, ws, *grads, stream=stream)
+    def step_saved(i=0):
+        qs, ks, vs, gs, ds = sets[i % len(sets)]
+        gla.gla_backward_saved_ws(qs, ks, vs, gs, ds, S, z, rope, ws, *grads, stream=stream)
 
     log(f"bench: backward with the saved state; {args.warmup} + {args.steps} steps")
-    for _ in range(args.warmup):
-        step_saved()
+    for i in range(args.warmup):
+        step_saved(i)
     torch.cuda.synchronize()
-    for e in evs:
+    for i, e in enumerate(evs):
         e[0].record(stream)
-        step_saved()
+        step_saved(i)
         e[1].record(stream)
     torch.cuda.synchronize()
     sv_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
@@ -574,27 +592,30 @@ def main():
         block_bench(args, w, gla, dev, (qd, kd, vd, gd), out, rope, stream)
         return
 
-    def step(ev=None):
+    sets = input_sets((qd, kd, vd, gd))
+
+    def step(ev=None, i=0):
+        qs, ks, vs, gs = sets[i % len(sets)]
         if ev is not None:
             ev[0].record(stream)
-        gla.gla_state_ws(kd, vd, rope, ws, stream)
+        gla.gla_state_ws(ks, vs, rope, ws, stream)
         if ev is not None:
             ev[1].record(stream)
-        gla.gla_output_ws(qd, gd, rope, out, ws, stream)
+        gla.gla_output_ws(qs, gs, rope, out, ws, stream)
         if ev is not None:
             ev[2].record(stream)
 
     log(f"bench: warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i=i)
     torch.cuda.synchronize()
 
     # timed region: exactly K passes, no per-kernel instrumentation
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i=i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
@@ -606,7 +627,7 @@ def main():
     log(f"bench: {args.steps} instrumented steps for the per-kernel times")
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], i)
     torch.cuda.synchronize()
     state_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     out_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
@@ -621,13 +642,13 @@ def main():
     cold_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
                 for _ in range(args.steps)]
     scratch = torch.zeros(EVICT_BYTES // 4, dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):   # settle the zero fill's write-backs
+    for i in range(args.warmup):   # settle the zero fill's write-backs
         scratch.sum()
-        step()
+        step(i=i)
     log(f"bench: {args.steps} instrumented steps after cache eviction")
     for i in range(args.steps):
         scratch.sum()
-        step(cold_evs[i])
+        step(cold_evs[i], i)
     torch.cuda.synchronize()
     del scratch
     cold_state = statistics.median(e[0].elapsed_time(e[1]) for e in cold_evs)

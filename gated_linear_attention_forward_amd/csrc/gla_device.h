@@ -37,9 +37,11 @@ constexpr int kCpolNt = 2;
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
-// The state kernels' k and v loads carry the hint too: each byte is read
-// once.  Measured on the layer shapes: 1-3% off the forward pass.  (On the
-// output kernel's q and g loads it cost 1-3% instead.)
+// The state kernels' k and v loads and the output kernel's g loads carry the
+// hint too: each of those bytes is read once.  Measured A/B per forward pass:
+// the k, v hint took 1-3% off the layer shapes; the g hint another 9% at 5B
+// 720p and 14B 480p (0.5% at the 60 s shape, 2% slower on the small 5B 480p
+// one).  On q as well as g, or on q alone, it measured worse or mixed.
 __device__ __forceinline__ u32x4 load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNt);
 }
@@ -271,6 +273,18 @@ __device__ __forceinline__ typename Chunk<OB>::T load_chunk(__amdgpu_buffer_rsrc
     return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
   else
     return T{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)};
+}
+
+template <int OB>
+__device__ __forceinline__ typename Chunk<OB>::T load_chunk_nt(__amdgpu_buffer_rsrc_t r,
+                                                               uint32_t off) {
+  using T = typename Chunk<OB>::T;
+  if constexpr (OB == 16)
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNt);
+  else if constexpr (OB == 8)
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolNt);
+  else
+    return T{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCpolNt)};
 }
 
 template <int OB>

@@ -834,7 +834,7 @@ void output_kernel(KArgs a) {
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) qv[s2] = load16(rq, toff + 64u * s2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gv[i] = load_chunk<OB>(rg, g_offset(base, i));
+    for (int i = 0; i < 4; ++i) gv[i] = load_chunk_nt<OB>(rg, g_offset(base, i));
   };
 
   // one 16-token step of this wave: tokens base .. base + 15
