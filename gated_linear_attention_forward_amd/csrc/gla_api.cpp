@@ -195,17 +195,23 @@ struct WsBuf {
 std::mutex g_ws_mu;
 std::map<WsKey, WsBuf>* g_ws = nullptr;  // never destroyed: process-lifetime cache
 
-int get_workspace(size_t bytes, void* stream, void** out) {
+// Returns the (device, stream) workspace of at least `bytes`, with *lk
+// holding the cache's lock: the caller keeps it
+// until its kernels are enqueued, so no other host thread can replace (and
+// free) the buffer in between.  A buffer that grows is freed only after a
+// synchronisation of its stream, which covers all earlier work that read it.
+int get_workspace(size_t bytes, void* stream, void** out, std::unique_lock<std::mutex>* lk) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_ws_mu);
+  *lk = std::unique_lock<std::mutex>(g_ws_mu);
   if (!g_ws) g_ws = new (std::nothrow) std::map<WsKey, WsBuf>();
   if (!g_ws) return GLA_ERR_ALLOC;
   WsBuf& b = (*g_ws)[WsKey{dev, stream}];
   if (b.bytes < bytes) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
     if (b.ptr) {
       // earlier work on this stream may still read the old buffer
-      if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
+      if (hipStreamSynchronize(s) != hipSuccess) return GLA_ERR_HIP;
       (void)hipFree(b.ptr);
       b.ptr = nullptr;
       b.bytes = 0;
@@ -226,6 +232,17 @@ int check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
   if (!ws) return GLA_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return GLA_ERR_WORKSPACE;
   if (ws_bytes < p.ws_bytes) return GLA_ERR_WORKSPACE;
+  return GLA_OK;
+}
+
+// The used part of a caller workspace overlaps none of the call's tensors
+// (each `bytes` long) nor its states.
+int check_ws_disjoint(const void* ws, size_t ws_used, std::initializer_list<const void*> tensors,
+                      size_t bytes, std::initializer_list<std::pair<const void*, size_t>> extra = {}) {
+  for (const void* t : tensors)
+    if (t && bytes && overlap2(ws, ws_used, t, bytes)) return GLA_ERR_ALIAS;
+  for (const auto& e : extra)
+    if (e.first && e.second && overlap2(ws, ws_used, e.first, e.second)) return GLA_ERR_ALIAS;
   return GLA_OK;
 }
 
@@ -420,6 +437,7 @@ int gla_state_ws(const void* k, const void* v, const gla_rope_tables* rope, int 
   if (!aligned16(k) || !aligned16(v)) return GLA_ERR_ALIGN;
   Plan p = gla::make_plan(B, N, H, D);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  if ((rc = check_ws_disjoint(workspace, p.ws_bytes, {k, v}, bytes))) return rc;
   if ((rc = rope_device_ok(rope))) return rc;
   return run_state(p, k, v, rope, workspace, nullptr, nullptr, nullptr, nullptr, stream);
 }
@@ -434,6 +452,7 @@ int gla_output_ws(const void* q, const void* g, const gla_rope_tables* rope, voi
   if ((rc = check_tensors({q, g}, out, bytes))) return rc;
   Plan p = gla::make_plan(B, N, H, D);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  if ((rc = check_ws_disjoint(workspace, p.ws_bytes, {q, g, out}, bytes))) return rc;
   if ((rc = rope_device_ok(rope))) return rc;
   return run_output(p, q, g, rope, out, workspace, stream);
 }
@@ -446,6 +465,9 @@ int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
   if ((long long)B * N * H == 0) return GLA_OK;
   Plan p = gla::make_plan(B, N, H, D);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  if ((rc = check_ws_disjoint(workspace, p.ws_bytes, {q, k, v, g, out},
+                              (size_t)B * N * H * D * 2)))
+    return rc;
   if ((rc = rope_device_ok(rope))) return rc;
   rc = run_state(p, k, v, rope, workspace, nullptr, nullptr, nullptr, nullptr, stream);
   if (rc) return rc;
@@ -460,7 +482,8 @@ int gla_forward(const void* q, const void* k, const void* v, const void* g,
   if ((long long)B * N * H == 0) return GLA_OK;
   Plan p = gla::make_plan(B, N, H, D);
   void* ws = nullptr;
-  if ((rc = get_workspace(p.ws_bytes, stream, &ws))) return rc;
+  std::unique_lock<std::mutex> lk;
+  if ((rc = get_workspace(p.ws_bytes, stream, &ws, &lk))) return rc;
   return gla_forward_ws(q, k, v, g, rope, out, B, N, H, D, ws, p.ws_bytes, stream);
 }
 
@@ -492,7 +515,8 @@ int gla_state(const void* k, const void* v, const gla_rope_tables* rope, float* 
   }
   Plan p = gla::make_plan(B, N, H, D);
   void* ws = nullptr;
-  if ((rc = get_workspace(p.ws_bytes, stream, &ws))) return rc;
+  std::unique_lock<std::mutex> lk;
+  if ((rc = get_workspace(p.ws_bytes, stream, &ws, &lk))) return rc;
   if ((rc = rope_device_ok(rope))) return rc;
   return run_state(p, k, v, rope, ws, S, z, nullptr, nullptr, stream);
 }
@@ -541,6 +565,13 @@ int gla_forward_blocks_ws(const void* q, const void* k, const void* v, const voi
   }
   Plan p = gla::make_plan(B, N, H, D, block_tokens);
   if ((rc = check_ws(p, workspace, workspace_bytes))) return rc;
+  {
+    const size_t sb = (size_t)B * H * D * D * sizeof(float), zb = (size_t)B * H * D * sizeof(float);
+    if ((rc = check_ws_disjoint(workspace, p.ws_bytes, {q, k, v, g, out},
+                                (size_t)B * N * H * D * 2,
+                                {{S_in, sb}, {z_in, zb}, {S_out, sb}, {z_out, zb}})))
+      return rc;
+  }
   if ((rc = rope_device_ok(rope))) return rc;
   rc = run_state(p, k, v, rope, workspace, S_out, z_out, S_in, z_in, stream);
   if (rc) return rc;
@@ -557,10 +588,11 @@ int gla_forward_blocks(const void* q, const void* k, const void* v, const void* 
   if ((long long)B * H == 0) return GLA_OK;
   void* ws = nullptr;
   size_t wsb = 0;
+  std::unique_lock<std::mutex> lk;
   if (N > 0) {
     Plan p = gla::make_plan(B, N, H, D, block_tokens);
     wsb = p.ws_bytes;
-    if ((rc = get_workspace(wsb, stream, &ws))) return rc;
+    if ((rc = get_workspace(wsb, stream, &ws, &lk))) return rc;
   }
   return gla_forward_blocks_ws(q, k, v, g, rope, out, B, N, H, D, block_tokens, S_in, z_in, S_out,
                                z_out, ws, wsb, stream);
@@ -632,7 +664,8 @@ int gla_softmax_forward(const void* q, const void* k, const void* v, const void*
   const size_t need = gla_softmax_workspace_bytes(B, N, H, D);
   if (need == 0) return GLA_OK;
   void* ws = nullptr;
-  if ((rc = get_workspace(need, stream, &ws))) return rc;
+  std::unique_lock<std::mutex> lk;
+  if ((rc = get_workspace(need, stream, &ws, &lk))) return rc;
   return gla_softmax_forward_ws(q, k, v, g, rope, out, B, N, H, D, ws, need, stream);
 }
 
@@ -793,7 +826,8 @@ int gla_backward(const void* q, const void* k, const void* v, const void* g, con
   const size_t need = gla_backward_workspace_bytes(B, N, H, D);
   if (need == 0) return GLA_OK;
   void* ws = nullptr;
-  if ((rc = get_workspace(need, stream, &ws))) return rc;
+  std::unique_lock<std::mutex> lk;
+  if ((rc = get_workspace(need, stream, &ws, &lk))) return rc;
   return gla_backward_ws(q, k, v, g, dout, rope, dq, dk, dv, dg, B, N, H, D, ws, need, stream);
 }
 
@@ -833,7 +867,8 @@ int gla_backward_saved(const void* q, const void* k, const void* v, const void* 
   const size_t need = gla_backward_workspace_bytes(B, N, H, D);
   if (need == 0) return GLA_OK;
   void* ws = nullptr;
-  if ((rc = get_workspace(need, stream, &ws))) return rc;
+  std::unique_lock<std::mutex> lk;
+  if ((rc = get_workspace(need, stream, &ws, &lk))) return rc;
   return backward_run(q, k, v, g, dout, rope, S, z, dq, dk, dv, dg, B, N, H, D, ws, need, stream);
 }
 
@@ -943,7 +978,8 @@ int gla_forward_proj(const void* x, const void* w, const gla_rope_tables* rope, 
   const size_t need = gla_proj_workspace_bytes(B, N, C, H, D);
   if (need == 0) return GLA_OK;
   void* ws = nullptr;
-  if ((rc = get_workspace(need, stream, &ws))) return rc;
+  std::unique_lock<std::mutex> lk;
+  if ((rc = get_workspace(need, stream, &ws, &lk))) return rc;
   return gla_forward_proj_ws(x, w, rope, out, B, N, C, H, D, ws, need, stream);
 }
 

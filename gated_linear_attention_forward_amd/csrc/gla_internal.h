@@ -80,6 +80,13 @@ constexpr int kStateBlocks = 256;
 // Each wave of a state block should see at least this many 16-token tiles.
 constexpr int kStateMinTilesPerWave = 2;
 constexpr int kOutputBlocks = 2048;
+// The persistent output kernel (one attention block per head): blocks per
+// launch it aims for (one per compute unit), the LDS each block asks for (so
+// that no two blocks share a compute unit) and the largest RoPE table it
+// stages whole.
+constexpr int kPersistBlocks = 256;
+constexpr size_t kPersistLdsBytes = 90 * 1024;
+constexpr size_t kMaxPersistTableBytes = 56 * 1024;
 // The backward pass's query and key kernels (8 waves, one block per compute
 // unit) take their token ranges from a plan of at most this many blocks:
 // one round of long ranges, each block staging its head's operands once.

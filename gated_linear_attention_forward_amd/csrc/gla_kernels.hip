@@ -942,8 +942,370 @@ void output_kernel(KArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tile state kernel (D = 128).
+//
+// Block = 8 waves (512 threads), one (chunk, head), one block per compute
+// unit.  A step takes 64 tokens.  Thread t loads chunk t % 16 of token rows
+// t / 16 and t / 16 + 32 of k and of v (one load instruction covers four whole
+// 256-byte rows), PF steps ahead in a register ring.  The thread applies
+// ReLU, z and RoPE to its k chunks and writes R phi(k) and v token-major into
+// one of two LDS tile buffers.  Each wave owns two of the sixteen 32 x 32
+// blocks of S (row block w / 2, column blocks 2 (w % 2) and 2 (w % 2) + 1)
+// and contracts a step's 64 tokens into them with four
+// v_mfma_f32_32x32x16_bf16 k-steps, the operands read back transposed with
+// ds_read_b64_tr_b16.  The contraction of step t - 1 runs in step t, after
+// its operand reads and beside step t's ReLU and RoPE arithmetic, so the
+// matrix unit and the vector ALU work at the same time; one LDS barrier per
+// step both publishes step t's tiles and frees step t - 1's buffer.  No two
+// waves share an accumulator, so the block writes its fp32 partial straight
+// from the accumulators, with no cross-wave reduction.
+struct TileCfg {
+  static constexpr int D = 128;
+  static constexpr int NT = 512;               // threads
+  static constexpr int TT = 64;                // tokens per step
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int RPI = NT / CPR;         // rows one load instruction per thread covers
+  static constexpr int LPT = TT / RPI;         // loads per thread, tensor and step
+  static constexpr int P = tile_pitch(2 * D);  // LDS row pitch (bytes)
+  static constexpr int TILE = TT * P;
+  static constexpr int BUF = 2 * TILE;         // R phi(k) tile + v tile
+  static constexpr int LDS_BYTES = 2 * BUF;    // two buffers
+  static constexpr int RT = D / 32;
+  static constexpr int TPW = RT * RT / 8;      // accumulator blocks per wave
+  static constexpr int KSTEP = TT / 16;
+  static constexpr int PF = 2;                 // steps of loads in flight
+  static_assert(LPT == 2 && TPW == 2 && PF % 2 == 0, "tile state layout");
+};
+
+template <bool ROPE, bool TLDS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void state_tile_kernel(KArgs a) {
+  using Cf = TileCfg;
+  constexpr int D = Cf::D, LPT = Cf::LPT, TPW = Cf::TPW, P = Cf::P, PF = Cf::PF;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float2* ltab = reinterpret_cast<float2*>(smem + Cf::LDS_BYTES);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  int n_begin, n_end;
+  range_of(a, c, n_begin, n_end);
+
+  TabView tv{};
+  if (ROPE) tv = stage_table<D, 512>(a, ltab, TLDS, n_begin, n_end);
+  __syncthreads();
+
+  const size_t boff = (size_t)b * a.N * a.H * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + boff, a.slab_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + boff, a.slab_bytes);
+  const uint32_t tokstride = (uint32_t)a.H * D * 2;
+  const int cc = tid % Cf::CPR, r0 = tid / Cf::CPR;
+  const uint32_t hoff = (uint32_t)h * D * 2 + 16u * cc;
+  const int ntile = (n_end - n_begin + Cf::TT - 1) / Cf::TT;
+  const int nsteps = (ntile + PF - 1) / PF * PF;
+  // axis block of each of the thread's four rotation pairs 4 cc + u (the
+  // thread's chunk never changes)
+  using X = Axes<D>;
+  bool in_y[4], in_x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int p = 4 * cc + u;
+    in_y[u] = p >= X::Pt && p < X::Pt + X::Py;
+    in_x[u] = p >= X::Pt + X::Py;
+  }
+
+  u32x4 kr[PF][LPT], vr[PF][LPT];
+  f32x16 acc[TPW];
+  float zacc[8];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) zacc[j] = 0.f;
+
+  auto issue = [&](auto S, int t) {
+    constexpr int s = decltype(S)::value;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int n = n_begin + Cf::TT * t + r0 + Cf::RPI * j;
+      const uint32_t off = n < n_end ? (uint32_t)n * tokstride + hoff : kOob;
+      kr[s][j] = load16_nt(rk, off);
+      vr[s][j] = load16_nt(rv, off);
+    }
+  };
+  // ReLU, z and RoPE of the tile in ring slot s, into LDS buffer s % 2
+  auto transform = [&](auto S, int t) {
+    constexpr int s = decltype(S)::value;
+    unsigned char* kt = smem + (s % 2) * Cf::BUF;
+    unsigned char* vt = kt + Cf::TILE;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int row = r0 + Cf::RPI * j;
+      u32x4 fq;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        fq[u] = relu2(kr[s][j][u]);
+        zacc[2 * u] += bf_lo(fq[u]);
+        zacc[2 * u + 1] += bf_hi(fq[u]);
+      }
+      u32x4 w = fq;
+      if (ROPE) {
+        const int n = min(n_begin + Cf::TT * t + row, n_end - 1);
+        int tt, yy, xx;
+        grid_pos(a, (uint32_t)n, tt, yy, xx);
+        const RowOff ro = row_offsets<D>(a, tv, tt, yy, xx);
+        float2 cs[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int base = in_x[u] ? ro.ox : (in_y[u] ? ro.oy : ro.ot);
+          cs[u] = tv.tab[base + 4 * cc + u];
+        }
+        w = rotate_chunk(fq, cs);
+      }
+      *reinterpret_cast<u32x4*>(kt + row * P + 16 * cc) = w;
+      *reinterpret_cast<u32x4*>(vt + row * P + 16 * cc) = vr[s][j];
+    }
+  };
+  // operands of the tile in LDS buffer B, then its MFMAs
+  const int ti = wave >> 1, tj = 2 * (wave & 1);
+  auto read_ops = [&](int B, bf16x8 (&A)[Cf::KSTEP], bf16x8 (&Bv)[Cf::KSTEP][TPW]) {
+    const unsigned char* kt = smem + B * Cf::BUF;
+    const unsigned char* vt = kt + Cf::TILE;
+#pragma unroll
+    for (int ks = 0; ks < Cf::KSTEP; ++ks) {
+      A[ks] = frag_tr(kt + 16 * ks * P, P, ti, lane);
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) Bv[ks][u] = frag_tr(vt + 16 * ks * P, P, tj + u, lane);
+    }
+  };
+  auto contract = [&](const bf16x8 (&A)[Cf::KSTEP], const bf16x8 (&Bv)[Cf::KSTEP][TPW]) {
+#pragma unroll
+    for (int ks = 0; ks < Cf::KSTEP; ++ks)
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ks], Bv[ks][u], acc[u], 0, 0, 0);
+  };
+
+  // Loads return in issue order and a step waits for its own slot while the
+  // later slots are in flight; the entry issues the slots in the loop's order.
+  static_for<PF>([&](auto S) {
+    issue(S, decltype(S)::value);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  for (int it = 0; it < nsteps; it += PF) {
+    static_for<PF>([&](auto S) {
+      constexpr int s = decltype(S)::value;
+      const int t = it + s;
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 A[Cf::KSTEP], Bv[Cf::KSTEP][TPW];
+      const bool prev = t > 0;  // uniform
+      if (prev) read_ops(1 - s % 2, A, Bv);
+      transform(S, t);
+      if (prev) contract(A, Bv);
+      issue(S, t + PF);
+      // every wave's tile writes of this step are done, and every wave is
+      // done reading the other buffer (no wait on the loads in flight)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    });
+  }
+  if (nsteps > 0) {
+    bf16x8 A[Cf::KSTEP], Bv[Cf::KSTEP][TPW];
+    read_ops(1, A, Bv);  // nsteps is even: the last tile sits in buffer 1
+    contract(A, Bv);
+  }
+
+  // z: lanes l, l + 16, l + 32, l + 48 hold the same features; then the
+  // eight waves in wave order through LDS (buffer 0, which no wave reads now)
+#pragma unroll
+  for (int msk = Cf::CPR; msk < 64; msk *= 2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zacc[j] += __shfl_xor(zacc[j], msk);
+  float* zw = reinterpret_cast<float*>(smem);
+  if (lane < Cf::CPR) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zw[wave * D + 8 * cc + j] = zacc[j];
+  }
+  __syncthreads();
+  float* dst = a.part + ((size_t)bh * a.C + c) * (size_t)(D * D + D);
+  if (tid < D) {
+    float z = zw[tid];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) z += zw[w * D + tid];
+    dst[D * D + tid] = z;
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = 32 * ti + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int e = 32 * (tj + u) + (lane & 31);
+      dst[d * D + e] = acc[u][r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent output kernel (one attention block per head: the bidirectional
+// mixer).  Block = 4 waves (256 threads), one per compute unit: the launch
+// asks for enough LDS that two blocks never share a compute unit.  Each block
+// keeps one head's S operand (and the whole RoPE table when it fits) in LDS
+// for its whole life and walks the head's 64-token ranges s, s + NS, s + 2NS,
+// ... (NS blocks per head), wave w taking tokens 16 w .. 16 w + 15 of each.
+// The blocks of all heads then read and write a compact window of whole token
+// rows at any time, which measured faster than both the per-range blocks of
+// output_kernel (that restage S for every range) and long contiguous ranges
+// per block.  A step is output_kernel's step (same arithmetic, same result).
+template <int D, bool ROPE, bool TLDS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void output_persist_kernel(KArgs a, int nsub) {
+  constexpr int KS = D / 32;
+  constexpr int MB = D / 16;
+  constexpr int OB = 2 * MB;
+  constexpr int OW = OB / 4;
+  constexpr int ROWS = D + 2;
+  using OChunk = typename Chunk<OB>::T;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* sS = smem;
+  float2* ltab = reinterpret_cast<float2*>(smem + ROWS * 2 * D);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane >> 4;
+  const int col = lane & 15;
+  const int bh = blockIdx.x;  // heads vary fastest over the grid
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int s = blockIdx.y;
+  const int N = a.N;
+  TabView tv{};
+
+  const size_t boff = (size_t)b * a.N * a.H * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + boff, a.slab_bytes);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + boff, a.slab_bytes);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out + boff, a.slab_bytes);
+  const uint32_t tokstride = (uint32_t)a.H * D * 2;
+  const uint32_t qoff = (uint32_t)h * D * 2 + 16u * m;
+  const uint32_t goff = (uint32_t)h * D * 2 + (uint32_t)OB * col;
+
+  auto g_offset = [&](int base, int i) -> uint32_t {
+    const int n = base + 4 * m + i;
+    return (n < N) ? (uint32_t)n * tokstride + goff : kOob;
+  };
+  auto load_qg = [&](int base, u32x4 (&qv)[KS], OChunk (&gv)[4]) {
+    const int n = base + col;
+    const uint32_t toff = (n < N) ? (uint32_t)n * tokstride + qoff : kOob;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) qv[s2] = load16(rq, toff + 64u * s2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gv[i] = load_chunk_nt<OB>(rg, g_offset(base, i));
+  };
+
+  auto step = [&](int base, const u32x4 (&qv)[KS], const OChunk (&gv)[4]) {
+    asm volatile("" ::: "memory");
+    RowOff rof{};
+    if (ROPE) {
+      int t, y, x;
+      grid_pos(a, (uint32_t)min(base + col, N - 1), t, y, x);
+      rof = row_offsets<D>(a, tv, t, y, x);
+    }
+    u32x4 fq[KS];
+    f32x4 accd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fq[s2][u] = relu2(qv[s2][u]);
+      const bf16x8 Bz = *reinterpret_cast<const bf16x8*>(
+          sS + row_tile_offset<D>(D + (col & 1), 16 * (4 * s2 + m)));
+      accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fq[s2]), Bz, accd,
+                                                    0, 0, 0);
+    }
+    bf16x8 Aq[KS];
+    static_for<KS>([&](auto S2) {
+      constexpr int s2 = decltype(S2)::value;
+      Aq[s2] = __builtin_bit_cast(bf16x8, ROPE ? rope_chunk<D, s2>(fq[s2], tv, rof, m) : fq[s2]);
+    });
+    f32x4 acc[MB];
+    bf16x8 Bf[2][KS];
+    auto read_b = [&](int j, bf16x8 (&dst)[KS]) {
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        dst[s2] = *reinterpret_cast<const bf16x8*>(sS + row_tile_offset<D>(16 * j + col, 16 * (4 * s2 + m)));
+    };
+    read_b(0, Bf[0]);
+    static_for<MB>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j + 1 < MB) read_b(j + 1, Bf[(j + 1) & 1]);
+      asm volatile("" ::: "memory");
+      acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[s2], Bf[j & 1][s2], acc[j], 0, 0, 0);
+    });
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float other = __int_as_float(
+          __builtin_amdgcn_mov_dpp(__float_as_int(accd[i]), 0xB1, 0xF, 0xF, false));
+      const float den = (accd[i] + other) + kEps;
+      OChunk ow;
+#pragma unroll
+      for (int w = 0; w < OW; ++w) {
+        float o2[2];
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          const int j = 2 * w + hlf;
+          const float gval = hlf ? bf_hi(gv[i][w]) : bf_lo(gv[i][w]);
+          const float e = __expf(-gval);
+          o2[hlf] = acc[j][i] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, e, den));
+        }
+        ow[w] = pack_bf16(o2[0], o2[1]);
+      }
+      store_chunk_nt<OB>(ro, g_offset(base, i), ow);
+    }
+  };
+
+  // the wave's steps: tokens 64 r + 16 wave .. for ranges r = s + k nsub
+  const int stride = 64 * nsub;
+  int base = 64 * s + 16 * wave;
+  u32x4 qa[KS], qb[KS];
+  OChunk ga[4], gb[4];
+  if (base < N) load_qg(base, qa, ga);
+  {
+    RowStage<D, D, 256> st_s;
+    RowStage<D, 2, 256, D> st_z;
+    const uint16_t* sl = a.sl + (size_t)bh * ROWS * D;
+    st_s.load(sl);
+    st_z.load(sl);
+    if (ROPE) {
+      if (TLDS) {
+        copy_to_lds<256>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        tv.tab = ltab;
+      } else {
+        tv.tab = a.cs;
+      }
+      tv.tbase = 0;
+      tv.ntr = a.T;
+      tv.t_last = a.T - 1;
+    }
+    st_s.store(sS);
+    st_z.store(sS);
+  }
+  __syncthreads();
+
+  for (; base < N; base += 2 * stride) {
+    load_qg(base + stride, qb, gb);
+    step(base, qa, ga);
+    if (base + stride >= N) break;
+    load_qg(base + 2 * stride, qa, ga);
+    step(base + stride, qb, gb);
+  }
+}
+
 // D = 32 keeps the one-wave-per-tile kernel (its accumulator is small);
-// D = 64 and 128 use the half-state kernel.
+// D = 64 uses the half-state kernel and D = 128 the tile state kernel.
 template <int D>
 constexpr bool use_half() {
   return D >= 64;
@@ -983,7 +1345,12 @@ hipError_t launch_reduce_d(const Plan& p, const KArgs& a, hipStream_t stream) {
 template <int D, bool ROPE, bool TLDS>
 hipError_t launch_state_k(const Plan& p, const KArgs& a, size_t lds, hipStream_t stream) {
   const dim3 g1(p.C, p.BH);
-  if constexpr (use_half<D>()) {
+  if constexpr (D == 128) {
+    const size_t lds_t = lds - state_lds_bytes<D>() + TileCfg::LDS_BYTES;
+    hipError_t e = allow_lds<state_tile_kernel<ROPE, TLDS>>(lds_t);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((state_tile_kernel<ROPE, TLDS>), g1, dim3(512), lds_t, stream, a);
+  } else if constexpr (use_half<D>()) {
     hipError_t e = allow_lds<state_half_kernel<D, ROPE, TLDS>>(lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((state_half_kernel<D, ROPE, TLDS>), g1, dim3(512), lds, stream, a);
@@ -1014,6 +1381,27 @@ hipError_t launch_state_d(const Plan& p, KArgs a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream) {
+  if (p.NB == 1) {
+    // persistent: NS blocks per head, one block per compute unit
+    const int nsub = kPersistBlocks / p.BH > 0 ? kPersistBlocks / p.BH : 1;
+    const size_t tb = 8 * ((size_t)a.T * a.Pt + (size_t)a.Hh * a.Py + (size_t)a.W * a.Px);
+    const bool tl = a.cs && tb <= kMaxPersistTableBytes;
+    size_t lds = output_lds_bytes<D>() + (tl ? tb : 0);
+    if (lds < kPersistLdsBytes) lds = kPersistLdsBytes;
+    const dim3 g(p.BH, nsub);
+    hipError_t e;
+    if (!a.cs) {
+      if ((e = allow_lds<output_persist_kernel<D, false, false>>(lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL((output_persist_kernel<D, false, false>), g, dim3(256), lds, stream, a, nsub);
+    } else if (tl) {
+      if ((e = allow_lds<output_persist_kernel<D, true, true>>(lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL((output_persist_kernel<D, true, true>), g, dim3(256), lds, stream, a, nsub);
+    } else {
+      if ((e = allow_lds<output_persist_kernel<D, true, false>>(lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL((output_persist_kernel<D, true, false>), g, dim3(256), lds, stream, a, nsub);
+    }
+    return hipGetLastError();
+  }
   const dim3 g3(p.BH, p.C2);
   const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;
   const size_t lds = output_lds_bytes<D>() + (tl ? table_lds_bytes(a) : 0);

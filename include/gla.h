@@ -121,8 +121,9 @@ int gla_forward(const void* q, const void* k, const void* v, const void* g,
                 void* stream);
 
 /* Same as gla_forward with a caller-owned device workspace (>= the size
- * gla_workspace_bytes returns, 256-byte aligned).  The workspace must not be
- * used by other work while this call's kernels run.  Never allocates. */
+ * gla_workspace_bytes returns, 256-byte aligned, overlapping none of the
+ * tensors: GLA_ERR_ALIAS otherwise).  The workspace must not be used by
+ * other work while this call's kernels run.  Never allocates. */
 int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
                    const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
                    void* workspace, size_t workspace_bytes, void* stream);
@@ -196,8 +197,8 @@ int gla_forward_blocks(const void* q, const void* k, const void* v, const void* 
 size_t gla_workspace_bytes_blocks(int B, int N, int H, int D, int block_tokens);
 
 /* gla_forward_blocks with a caller-owned workspace (>= the size
- * gla_workspace_bytes_blocks returns, 256-byte aligned; may be NULL when
- * N == 0).  Never allocates. */
+ * gla_workspace_bytes_blocks returns, 256-byte aligned, overlapping no
+ * tensor or state; may be NULL when N == 0).  Never allocates. */
 int gla_forward_blocks_ws(const void* q, const void* k, const void* v, const void* g,
                           const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
                           int block_tokens, const float* S_in, const float* z_in, float* S_out,
