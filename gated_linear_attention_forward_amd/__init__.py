@@ -28,6 +28,7 @@ from .gla import (  # noqa: F401
     gla_forward_blocks_check,
     gla_forward_blocks_ws,
     gla_forward_check,
+    gla_forward_noalloc,
     gla_forward_proj,
     gla_forward_proj_check,
     gla_forward_proj_ws,

@@ -320,6 +320,8 @@ const char* gla_strerror(int status) {
     case GLA_ERR_ALIAS: return "out overlaps an input";
     case GLA_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case GLA_ERR_HIP: return "HIP runtime call failed";
+    case GLA_ERR_SCRATCH:
+      return "the call needs more workspace than gla_forward_noalloc's fixed 32 MiB scratch";
     default: return "unknown status";
   }
 }
@@ -485,6 +487,20 @@ int gla_forward(const void* q, const void* k, const void* v, const void* g,
   std::unique_lock<std::mutex> lk;
   if ((rc = get_workspace(p.ws_bytes, stream, &ws, &lk))) return rc;
   return gla_forward_ws(q, k, v, g, rope, out, B, N, H, D, ws, p.ws_bytes, stream);
+}
+
+int gla_forward_noalloc(const void* q, const void* k, const void* v, const void* g,
+                        const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                        void* stream) {
+  int rc = gla_forward_check(q, k, v, g, rope, out, B, N, H, D);
+  if (rc) return rc;
+  if ((long long)B * N * H == 0) return GLA_OK;
+  Plan p = gla::make_plan(B, N, H, D);
+  if (p.ws_bytes > gla::kScratchBytes) return GLA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (gla::scratch_pointer(&ws) != hipSuccess) return GLA_ERR_HIP;
+  // the same checks and launches as gla_forward_ws, on the fixed scratch
+  return gla_forward_ws(q, k, v, g, rope, out, B, N, H, D, ws, gla::kScratchBytes, stream);
 }
 
 int gla_state(const void* k, const void* v, const gla_rope_tables* rope, float* S, float* z,

@@ -100,6 +100,12 @@ constexpr int kMaxLdsTableBytes = 24 * 1024;
 Plan make_plan(int B, int N, int H, int D, int block_tokens = 0,
                int output_blocks = kOutputBlocks);
 
+// The fixed per-device scratch of the no-allocation entry point (gla_kernels.hip):
+// its size, and its device address on the current device (looked up on the
+// first call per device).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+hipError_t scratch_pointer(void** out);
+
 // Kernel launchers (gla_kernels.hip).  Return the hipError_t of the launch.
 hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream);
 // The scan alone over zero blocks: S_out/z_out = S_in/z_in (or zero).

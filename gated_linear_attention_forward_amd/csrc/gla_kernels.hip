@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "gla_device.h"
@@ -1415,6 +1416,36 @@ hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Fixed scratch for the entry point that allocates nothing: the forward
+// workspace (chunk partials and the bf16 state operand) of any call that fits
+// in kScratchBytes.  Each GPU the library runs on holds its own copy until
+// the process ends.  In host code the array's name is only a stand-in for the
+// device address; that address is looked up once per device, with the device
+// current, and kept.
+namespace {
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t scratch_pointer(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream) {
   switch (p.D) {

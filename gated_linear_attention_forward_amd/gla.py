@@ -26,11 +26,12 @@ GLA_ERR_LAUNCH = -6
 GLA_ERR_ALIAS = -7
 GLA_ERR_WORKSPACE = -8
 GLA_ERR_HIP = -9
+GLA_ERR_SCRATCH = -10
 
 EXPORTS = (
     "gla_strerror", "gla_rope_table_floats", "gla_rope_fill_host", "gla_rope_create",
     "gla_rope_destroy", "gla_workspace_bytes", "gla_forward", "gla_forward_ws",
-    "gla_forward_check", "gla_state_ws", "gla_output_ws", "gla_state",
+    "gla_forward_check", "gla_forward_noalloc", "gla_state_ws", "gla_output_ws", "gla_state",
     "gla_forward_blocks", "gla_forward_blocks_ws", "gla_workspace_bytes_blocks",
     "gla_forward_blocks_check", "gla_softmax_forward", "gla_softmax_forward_ws",
     "gla_softmax_workspace_bytes", "gla_softmax_forward_check", "gla_backward",
@@ -84,6 +85,7 @@ def load_library():
         "gla_forward": ([vp] * 4 + [rp, vp] + [i32] * 4 + [vp], i32),
         "gla_forward_ws": ([vp] * 4 + [rp, vp] + [i32] * 4 + [vp, sz, vp], i32),
         "gla_forward_check": ([vp] * 4 + [rp, vp] + [i32] * 4, i32),
+        "gla_forward_noalloc": ([vp] * 4 + [rp, vp] + [i32] * 4 + [vp], i32),
         "gla_state_ws": ([vp, vp, rp] + [i32] * 4 + [vp, sz, vp], i32),
         "gla_output_ws": ([vp, vp, rp, vp] + [i32] * 4 + [vp, sz, vp], i32),
         "gla_state": ([vp, vp, rp, vp, vp] + [i32] * 4 + [vp], i32),
@@ -251,6 +253,27 @@ def gla_forward(q, k, v, g, rope=None, out=None, stream=None) -> torch.Tensor:
                                        _rope_ptr(rope), out.data_ptr(), B, N, H, D,
                                        _stream_handle(stream, q.device)),
             "gla_forward")
+    return out
+
+
+def gla_forward_noalloc(q, k, v, g, rope=None, out=None, stream=None) -> torch.Tensor:
+    """gla_forward on the library's fixed per-GPU scratch (no device allocation
+    by the library).  Calls on one GPU share that scratch: do not overlap them."""
+    _check_bf16("q", q)
+    for name, t in (("k", k), ("v", v), ("g", g)):
+        _check_bf16(name, t, q.shape)
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bf16("out", out, q.shape)
+    B, N, H, D = q.shape
+    with torch.cuda.device(q.device):
+        _ok(load_library().gla_forward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                               g.data_ptr(), _rope_ptr(rope), out.data_ptr(),
+                                               B, N, H, D, _stream_handle(stream, q.device)),
+            "gla_forward_noalloc")
     return out
 
 

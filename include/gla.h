@@ -56,7 +56,8 @@ enum gla_status {
   GLA_ERR_LAUNCH = -6,    /* a kernel launch failed */
   GLA_ERR_ALIAS = -7,     /* out overlaps an input */
   GLA_ERR_WORKSPACE = -8, /* caller workspace too small or not 256-byte aligned */
-  GLA_ERR_HIP = -9        /* another HIP runtime call failed */
+  GLA_ERR_HIP = -9,       /* another HIP runtime call failed */
+  GLA_ERR_SCRATCH = -10   /* gla_forward_noalloc: the call needs more than its fixed scratch */
 };
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -127,6 +128,23 @@ int gla_forward(const void* q, const void* k, const void* v, const void* g,
 int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
                    const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* gla_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * calls no hipMalloc, hipFree or allocating library routine.  Instead of a
+ * workspace it uses a fixed 32 MiB scratch array in device memory that the
+ * library holds on each GPU it runs on until the process ends; calls whose
+ * gla_workspace_bytes exceed 32 MiB (33554432 bytes) return GLA_ERR_SCRATCH
+ * before any HIP call (at D = 128 every shape with B*H <= 256 fits).  All
+ * calls on one GPU share that array, so calls that overlap in time on one
+ * GPU (other streams, other host threads) race and must be serialised by the
+ * caller.  Nothing in the scratch needs to start at zero: each call writes
+ * all of it that it reads.  Arguments, results and errors otherwise as for
+ * gla_forward; the first call on a device also looks up the array's device
+ * address (GLA_ERR_HIP if that fails). */
+int gla_forward_noalloc(const void* q, const void* k, const void* v, const void* g,
+                        const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
+                        void* stream);
 
 /* Argument validation of gla_forward alone: returns the status gla_forward
  * would return before touching the GPU (GLA_OK if the arguments are valid).

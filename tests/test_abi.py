@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_strerror_covers_codes():
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         s = gla.gla_strerror(code)
         assert s and s != "unknown status"
     assert gla.gla_strerror(17) == "unknown status"
@@ -367,3 +367,18 @@ def test_proj_workspace_size():
     assert ws % 256 == 0
     assert gla.gla_proj_workspace_bytes(1, 0, 256, 2, 128) == 0
     assert gla.gla_proj_workspace_bytes(1, 10, 100, 2, 128) == 0
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_before_any_hip_call():
+    """gla_forward_noalloc's fixed scratch is 32 MiB; a call whose workspace
+    would be larger is refused with GLA_ERR_SCRATCH during validation (the
+    fake pointers are never used, and no GPU is needed)."""
+    lib = gla.load_library()
+    B, N, H, D = 1, 64, 600, 128  # one chunk per head: 600 fp32 partials of 66 KB
+    assert gla.gla_workspace_bytes(B, N, H, D) > 32 << 20
+    G = 1 << 30  # fake addresses far enough apart for 9.8 MB tensors
+    rc = lib.gla_forward_noalloc(G, 2 * G, 3 * G, 4 * G, None, 5 * G, B, N, H, D, None)
+    assert rc == glamod.GLA_ERR_SCRATCH
+    # argument errors are still reported first
+    rc = lib.gla_forward_noalloc(G, 2 * G, 3 * G, 4 * G, None, 5 * G, B, N, H, 96, None)
+    assert rc == glamod.GLA_ERR_DIM
