@@ -20,6 +20,10 @@ ARCH = "gfx950"
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC"]
+# The forward kernels read their MFMA results with ordinary vector ALU
+# instructions (the epilogue, the partial-state stores): keeping those results
+# in VGPRs instead of AGPRs saves a v_accvgpr_read per result.
+FILE_FLAGS = {"gla_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd, verbose):
@@ -39,7 +43,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in ("gla_kernels.hip", "gla_softmax.hip", "gla_backward.hip", "gla_project.hip"):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        _run(["hipcc", *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+        _run(["hipcc", *HIP_FLAGS, *FILE_FLAGS.get(src, []), f"-I{INCLUDE}", f"-I{CSRC}", "-c",
               os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     aobj = os.path.join(BUILD, "gla_api.o")

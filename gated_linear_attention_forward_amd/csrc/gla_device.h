@@ -191,6 +191,31 @@ __device__ __forceinline__ void grid_pos(const KArgs& a, uint32_t n, int& t, int
   x = (int)(rem - (uint32_t)y * (uint32_t)a.W);
 }
 
+// Grid position of a token that advances by a fixed number of tokens per
+// step: the advance is split once into (dt, dy, dx) with dx < W and dy < Hh,
+// so each step needs one carry per axis instead of two divisions.  Positions
+// past the last frame keep counting (table lookups clamp t).
+struct GridWalk {
+  int t, y, x;
+  int dt, dy, dx;
+  __device__ __forceinline__ void init(const KArgs& a, uint32_t n, uint32_t adv) {
+    grid_pos(a, n, t, y, x);
+    dt = (int)fast_div(adv, a.div_hw);
+    const uint32_t r = adv - (uint32_t)dt * (uint32_t)(a.Hh * a.W);
+    dy = (int)fast_div(r, a.div_w);
+    dx = (int)(r - (uint32_t)dy * (uint32_t)a.W);
+  }
+  __device__ __forceinline__ void advance(const KArgs& a) {
+    x += dx;
+    const int cx = x >= a.W ? 1 : 0;
+    x -= cx * a.W;
+    y += dy + cx;
+    const int cy = y >= a.Hh ? 1 : 0;
+    y -= cy * a.Hh;
+    t += dt + cy;
+  }
+};
+
 // (cos, sin) of pair p, where p is known to lie in [PMIN, PMAX]: when that
 // range sits inside one axis block the table row is chosen at compile time,
 // otherwise by masks (no branches).

@@ -1018,6 +1018,14 @@ void state_tile_kernel(KArgs a) {
     in_x[u] = p >= X::Pt + X::Py;
   }
 
+  // grid positions of the thread's rows in the tile being transformed
+  GridWalk gw[LPT];
+  if (ROPE) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j)
+      gw[j].init(a, (uint32_t)min(n_begin + r0 + Cf::RPI * j, a.N - 1), (uint32_t)Cf::TT);
+  }
+
   u32x4 kr[PF][LPT], vr[PF][LPT];
   f32x16 acc[TPW];
   float zacc[8];
@@ -1055,10 +1063,8 @@ void state_tile_kernel(KArgs a) {
       }
       u32x4 w = fq;
       if (ROPE) {
-        const int n = min(n_begin + Cf::TT * t + row, n_end - 1);
-        int tt, yy, xx;
-        grid_pos(a, (uint32_t)n, tt, yy, xx);
-        const RowOff ro = row_offsets<D>(a, tv, tt, yy, xx);
+        const RowOff ro = row_offsets<D>(a, tv, gw[j].t, gw[j].y, gw[j].x);
+        gw[j].advance(a);
         float2 cs[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -1163,6 +1169,8 @@ void state_tile_kernel(KArgs a) {
 template <int D, bool ROPE, bool TLDS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void output_persist_kernel(KArgs a, int nsub) {
+  constexpr bool QROWS = D == 128;  // whole-row q loads (four rows of 16 chunks)
+  constexpr int QT = 16 * 2 * D;    // per-wave q tile in LDS
   constexpr int KS = D / 32;
   constexpr int MB = D / 16;
   constexpr int OB = 2 * MB;
@@ -1171,7 +1179,8 @@ void output_persist_kernel(KArgs a, int nsub) {
   using OChunk = typename Chunk<OB>::T;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char* sS = smem;
-  float2* ltab = reinterpret_cast<float2*>(smem + ROWS * 2 * D);
+  unsigned char* myq = smem + ROWS * 2 * D + (threadIdx.x >> 6) * QT;
+  float2* ltab = reinterpret_cast<float2*>(smem + ROWS * 2 * D + (QROWS ? 4 * QT : 0));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1196,29 +1205,53 @@ void output_persist_kernel(KArgs a, int nsub) {
     const int n = base + 4 * m + i;
     return (n < N) ? (uint32_t)n * tokstride + goff : kOob;
   };
+  // QROWS: qv[i] holds chunk col of token base + 4 i + m (four whole rows per
+  // load instruction); the step turns them into the operand layout through the
+  // wave's LDS tile.  Otherwise qv[s2] is chunk 4 s2 + m of token base + col.
   auto load_qg = [&](int base, u32x4 (&qv)[KS], OChunk (&gv)[4]) {
-    const int n = base + col;
-    const uint32_t toff = (n < N) ? (uint32_t)n * tokstride + qoff : kOob;
+    if constexpr (QROWS) {
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) qv[s2] = load16(rq, toff + 64u * s2);
+      for (int i = 0; i < KS; ++i) {
+        const int n = base + 4 * i + m;
+        qv[i] = load16(rq, n < N ? (uint32_t)n * tokstride + (uint32_t)h * D * 2 + 16u * col : kOob);
+      }
+    } else {
+      const int n = base + col;
+      const uint32_t toff = (n < N) ? (uint32_t)n * tokstride + qoff : kOob;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) qv[s2] = load16(rq, toff + 64u * s2);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) gv[i] = load_chunk_nt<OB>(rg, g_offset(base, i));
   };
 
+  GridWalk gw;  // grid position of the lane's token (base + col) in the next step
   auto step = [&](int base, const u32x4 (&qv)[KS], const OChunk (&gv)[4]) {
     asm volatile("" ::: "memory");
     RowOff rof{};
     if (ROPE) {
-      int t, y, x;
-      grid_pos(a, (uint32_t)min(base + col, N - 1), t, y, x);
-      rof = row_offsets<D>(a, tv, t, y, x);
+      rof = row_offsets<D>(a, tv, gw.t, gw.y, gw.x);
+      gw.advance(a);
     }
     u32x4 fq[KS];
+    if constexpr (QROWS) {
+      // the wave's own tile: its LDS instructions execute in order, so the
+      // reads see the writes and the next step's writes follow these reads
+#pragma unroll
+      for (int i = 0; i < KS; ++i)
+        *reinterpret_cast<u32x4*>(myq + row_tile_offset<D>(4 * i + m, 16 * col)) = qv[i];
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        fq[s2] = *reinterpret_cast<const u32x4*>(myq + row_tile_offset<D>(col, 16 * (4 * s2 + m)));
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) fq[s2] = qv[s2];
+    }
     f32x4 accd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) fq[s2][u] = relu2(qv[s2][u]);
+      for (int u = 0; u < 4; ++u) fq[s2][u] = relu2(fq[s2][u]);
       const bf16x8 Bz = *reinterpret_cast<const bf16x8*>(
           sS + row_tile_offset<D>(D + (col & 1), 16 * (4 * s2 + m)));
       accd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fq[s2]), Bz, accd,
@@ -1271,6 +1304,7 @@ void output_persist_kernel(KArgs a, int nsub) {
   // the wave's steps: tokens 64 r + 16 wave .. for ranges r = s + k nsub
   const int stride = 64 * nsub;
   int base = 64 * s + 16 * wave;
+  if (ROPE) gw.init(a, (uint32_t)min(base + col, N - 1), (uint32_t)stride);
   u32x4 qa[KS], qb[KS];
   OChunk ga[4], gb[4];
   if (base < N) load_qg(base, qa, ga);
@@ -1296,12 +1330,24 @@ void output_persist_kernel(KArgs a, int nsub) {
   }
   __syncthreads();
 
-  for (; base < N; base += 2 * stride) {
+  // three register sets: the loads of the next two steps are in flight
+  // during a step
+  u32x4 qc[KS];
+  OChunk gc[4];
+  if (base < N) {
     load_qg(base + stride, qb, gb);
-    step(base, qa, ga);
-    if (base + stride >= N) break;
-    load_qg(base + 2 * stride, qa, ga);
-    step(base + stride, qb, gb);
+    for (;;) {
+      load_qg(base + 2 * stride, qc, gc);
+      step(base, qa, ga);
+      if (base + stride >= N) break;
+      load_qg(base + 3 * stride, qa, ga);
+      step(base + stride, qb, gb);
+      if (base + 2 * stride >= N) break;
+      load_qg(base + 4 * stride, qb, gb);
+      step(base + 2 * stride, qc, gc);
+      if (base + 3 * stride >= N) break;
+      base += 3 * stride;
+    }
   }
 }
 
@@ -1387,7 +1433,7 @@ hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream) {
     const int nsub = kPersistBlocks / p.BH > 0 ? kPersistBlocks / p.BH : 1;
     const size_t tb = 8 * ((size_t)a.T * a.Pt + (size_t)a.Hh * a.Py + (size_t)a.W * a.Px);
     const bool tl = a.cs && tb <= kMaxPersistTableBytes;
-    size_t lds = output_lds_bytes<D>() + (tl ? tb : 0);
+    size_t lds = output_lds_bytes<D>() + (D == 128 ? 4 * 16 * 2 * D : 0) + (tl ? tb : 0);
     if (lds < kPersistLdsBytes) lds = kPersistLdsBytes;
     const dim3 g(p.BH, nsub);
     hipError_t e;
