@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "gla_internal.h"
@@ -410,16 +411,28 @@ inline int table_lds_bytes(const KArgs& a) {
   return 8 * (a.nt * a.Pt + a.Hh * a.Py + a.W * a.Px);
 }
 
-// A kernel that takes more than 64 KB of dynamic LDS raises its limit to the
-// largest size asked for so far (one record per kernel).
+// A kernel that takes more than 64 KB of dynamic LDS raises its limit on the
+// current device to the largest size asked for there so far (one record per
+// kernel and device).  Concurrent callers may both set the attribute, which
+// is harmless; the record only grows (compare-and-swap).
+constexpr int kMaxLdsDevices = 64;
 template <auto K>
 hipError_t allow_lds(size_t bytes) {
-  static size_t granted = 0;
-  if (bytes <= 65536 || bytes <= granted) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(K),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) granted = bytes;
-  return e;
+  static std::atomic<size_t> granted[kMaxLdsDevices];
+  if (bytes <= 65536) return hipSuccess;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxLdsDevices) return hipErrorInvalidDevice;
+  if (bytes <= granted[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(K),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  size_t cur = granted[dev].load(std::memory_order_relaxed);
+  while (cur < bytes && !granted[dev].compare_exchange_weak(cur, bytes, std::memory_order_release,
+                                                           std::memory_order_relaxed)) {
+  }
+  return hipSuccess;
 }
 
 }  // namespace

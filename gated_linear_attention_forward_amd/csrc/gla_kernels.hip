@@ -995,10 +995,7 @@ void state_tile_kernel(KArgs a) {
   int n_begin, n_end;
   range_of(a, c, n_begin, n_end);
 
-  TabView tv{};
-  if (ROPE) tv = stage_table<D, 512>(a, ltab, TLDS, n_begin, n_end);
-  __syncthreads();
-
+  TabView tv{};  // the RoPE table view, set once staged (after the first loads)
   const size_t boff = (size_t)b * a.N * a.H * D;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + boff, a.slab_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + boff, a.slab_bytes);
@@ -1098,11 +1095,14 @@ void state_tile_kernel(KArgs a) {
   };
 
   // Loads return in issue order and a step waits for its own slot while the
-  // later slots are in flight; the entry issues the slots in the loop's order.
+  // later slots are in flight; the entry issues the slots in the loop's order,
+  // before the table staging, so the two wait for memory together.
   static_for<PF>([&](auto S) {
     issue(S, decltype(S)::value);
     __builtin_amdgcn_sched_barrier(0);
   });
+  if (ROPE) tv = stage_table<D, 512>(a, ltab, TLDS, n_begin, n_end);
+  __syncthreads();
   for (int it = 0; it < nsteps; it += PF) {
     static_for<PF>([&](auto S) {
       constexpr int s = decltype(S)::value;

@@ -390,6 +390,30 @@ def projected_heads(x, w, H: int, D: int, heads, which="qkvg"):
     return out
 
 
+def project_maps(x, w, H: int, D: int, chunk: int = 8192):
+    """All four projections of every head, rounded to bf16: (q, k, v, g) bit
+    patterns, each [B, N, H, D].  The fp64 products x W^T come from numpy's
+    matrix product (a library primitive: the same sums as project, in
+    another order, exact to fp64 rounding), taken over chunks of tokens so
+    that a layer's fp64 products never sit in memory at once."""
+    xb, wb = as_bits(x), as_bits(w)
+    if wb.ndim == 3:
+        wb = wb.reshape(-1, wb.shape[-1])
+    B, N, C = xb.shape
+    if wb.shape != (4 * H * D, C):
+        raise ValueError("w must be [4, H*D, C] (or [4*H*D, C])")
+    wf = (wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # exact widening
+    outs = [np.empty((B, N, H, D), np.uint16) for _ in range(4)]
+    for b in range(B):
+        for n0 in range(0, N, chunk):
+            n1 = min(n0 + chunk, N)
+            xf = (xb[b, n0:n1].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            y = round_bf16(xf @ wf.T).reshape(n1 - n0, 4, H, D)
+            for i in range(4):
+                outs[i][b, n0:n1] = y[:, i]
+    return tuple(outs)
+
+
 def projected_forward(x, w, H: int, D: int, grid: Grid | None, eps: float = EPS) -> np.ndarray:
     """The projections rounded to bf16, then the mixer: [B, N, H, D] fp64."""
     t = projected_heads(x, w, H, D, range(H))

@@ -59,3 +59,17 @@ def test_selection_weights_reproduce_the_mixer():
     heads = oracle.projected_heads(x, w.reshape(4 * H * D, C), H, D, [1])
     assert np.array_equal(heads["k"][:, :, 0], oracle.as_bits(k)[:, :, 1])
     assert np.array_equal(heads["g"][:, :, 0], oracle.as_bits(g)[:, :, 1])
+
+
+def test_project_maps_matches_the_c_projection():
+    """project_maps (numpy's product, chunked over tokens) against the C
+    oracle's projected_heads for every map and head, bit for bit after the
+    bf16 rounding (the fp64 sums differ only in order, far below a bf16
+    rounding boundary except on exact ties, which random data does not hit)."""
+    B, N, C, H, D = 2, 37, 128, 3, 32
+    x, w = random_projection(B, N, C, H, D, seed=11)
+    maps = oracle.project_maps(x, w, H, D, chunk=16)
+    ref = oracle.projected_heads(x, w, H, D, range(H))
+    for name, got in zip("qkvg", maps):
+        assert got.shape == (B, N, H, D)
+        assert np.array_equal(got, ref[name]), name

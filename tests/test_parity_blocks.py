@@ -134,7 +134,9 @@ def test_two_calls_handing_over_the_state():
     assert r_out <= 2e-3 and r_S <= 1e-5 and r_z <= 1e-6
 
 
-def test_workload_720p_in_five_frame_blocks_sampled():
+def test_workload_720p_in_five_frame_blocks():
+    """The 5B 720p layer in 5-frame blocks: every output of every head and
+    every returned state against oracle.forward_blocks (a few heads at a time)."""
     w = BY_NAME["5b_720p_193f"]
     L = 5 * w.Hh * w.W
     say(f"case blocks {w.name} L={L}")
@@ -146,19 +148,31 @@ def test_workload_720p_in_five_frame_blocks_sampled():
     out = gla.gla_forward_blocks(qd, kd, vd, gd, rope, L, None, None, S_out, z_out).cpu()
     torch.cuda.synchronize()
     rope.close()
-    rng = np.random.default_rng(7)
+    del qd, kd, vd, gd
+    S_gpu, z_gpu = S_out.double().cpu().numpy(), z_out.double().cpu().numpy()
     grid = oracle.Grid(w.T, w.Hh, w.W)
-    got_all, ref_all = [], []
-    for (b, h) in [(0, 0), (1, 19), (0, 11)]:
-        sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous()
-        ref, S_ref, z_ref = oracle.forward_blocks(sl(q), sl(k), sl(v), sl(g), grid, L)
-        toks = np.unique(np.concatenate([rng.integers(0, w.N, 64), [0, L - 1, L, w.N - 1]]))
-        got_all.append(out[b, torch.from_numpy(toks), h].double().numpy())
-        ref_all.append(ref[0, toks, 0])
-        rs = rel(S_out[b, h].double().cpu().numpy(), S_ref[0, 0])
-        say(f"  head ({b},{h}) final S rel_l2={rs:.3e}")
-        assert rs <= 3e-3
-    assert_close(np.concatenate(got_all), np.concatenate(ref_all), "sampled rows")
+    d2 = r2 = 0.0
+    mx = 0.0
+    sd2 = sr2 = zd2 = zr2 = 0.0
+    group = max(4, oracle.num_threads())  # the oracle runs one head per thread
+    for b in range(w.B):
+        for h0 in range(0, w.H, group):
+            h1 = min(h0 + group, w.H)
+            sl = lambda t: t[b:b + 1, :, h0:h1].contiguous()
+            ref, S_ref, z_ref = oracle.forward_blocks(sl(q), sl(k), sl(v), sl(g), grid, L)
+            got = out[b:b + 1, :, h0:h1].double().numpy()
+            d2 += float(np.sum((got - ref) ** 2))
+            r2 += float(np.sum(ref ** 2))
+            mx = max(mx, float(np.max(np.abs(got - ref))))
+            sd2 += float(np.sum((S_gpu[b, h0:h1] - S_ref[0]) ** 2))
+            sr2 += float(np.sum(S_ref[0] ** 2))
+            zd2 += float(np.sum((z_gpu[b, h0:h1] - z_ref[0]) ** 2))
+            zr2 += float(np.sum(z_ref[0] ** 2))
+    r_out, r_S, r_z = (d2 / r2) ** 0.5, (sd2 / sr2) ** 0.5, (zd2 / zr2) ** 0.5
+    say(f"  all outputs: rel_l2={r_out:.3e} max_abs={mx:.3e}; final S rel_l2={r_S:.3e} "
+        f"z rel_l2={r_z:.3e}")
+    assert r_out <= REL_TOL and mx <= ABS_TOL
+    assert r_S <= 3e-3 and r_z <= 1e-6
 
 
 def test_empty_sequence_returns_the_carried_state():

@@ -5,9 +5,9 @@ x W^T in fp64, rounded to bf16, then the fp64 mixer.
 Bar: relative L2 error <= 5e-3 and max absolute error <= 3e-2 of the bf16
 output.  The GPU accumulates the projections in fp32 before rounding them to
 bf16 (a value next to a rounding boundary can land one bf16 step away from
-the oracle's), then rounds as the mixer does.  Small shapes are compared on
-every output; the layer shapes on sampled rows of sampled heads, whose
-projections the oracle forms for that head alone.
+the oracle's), then rounds as the mixer does.  Every shape is compared on
+every output; at the layer shapes the oracle's projections of all heads come
+from oracle.project_maps (numpy's fp64 product, chunked over tokens).
 """
 import numpy as np
 import pytest
@@ -64,7 +64,10 @@ def test_proj_small_shapes(B, H, D, grid, C, rope):
 
 
 @pytest.mark.parametrize("name", [w.name for w in PROJ_WORKLOADS])
-def test_proj_workload_sampled(name):
+def test_proj_workload(name):
+    """The layer shapes: every output of every head against the oracle's
+    projections (oracle.project_maps, rounded to bf16) followed by the mixer
+    oracle, a few heads at a time."""
     w = BY_NAME[name]
     say(f"case proj workload {w.name} B={w.B} N={w.N} C={w.C} H={w.H} D={w.D}")
     x, wt = make_projection(w)
@@ -72,26 +75,23 @@ def test_proj_workload_sampled(name):
     out = gla.gla_forward_proj(x.to(DEV), wt.to(DEV), w.H, w.D, rope)
     torch.cuda.synchronize()
     rope.close()
+    out = out.cpu()
     grid = oracle.Grid(w.T, w.Hh, w.W, w.theta)
-    rng = np.random.default_rng(w.seed + 3)
-    heads = sorted({(int(rng.integers(0, w.B)), int(rng.integers(0, w.H))) for _ in range(2)})
-    if w.N > 100_000:
-        heads = heads[:1]
-    got, ref = [], []
-    for b, h in heads:
-        toks = np.unique(np.concatenate([rng.integers(0, w.N, 48), [0, w.N - 1]]))
-        xb = x[b:b + 1].contiguous()
-        kv = oracle.projected_heads(xb, wt, w.H, w.D, [h], "kv")
-        qg = oracle.projected_heads(x[b:b + 1, toks].contiguous(), wt, w.H, w.D, [h], "qg")
-        S, z = oracle.state(kv["k"], kv["v"], grid)
-        # rows of the sampled tokens: q, g placed at their token positions
-        qfull = np.zeros((1, w.N, 1, w.D), np.uint16)
-        gfull = np.zeros((1, w.N, 1, w.D), np.uint16)
-        qfull[0, toks] = qg["q"][0]
-        gfull[0, toks] = qg["g"][0]
-        ref.append(oracle.rows(qfull, gfull, grid, 0, 0, S[0, 0], z[0, 0], toks))
-        got.append(out[b, toks, h].double().cpu().numpy())
-    assert_close(np.concatenate(got), np.concatenate(ref), f"{w.name} sampled rows")
+    q, k, v, g = oracle.project_maps(x, wt, w.H, w.D)
+    d2 = r2 = mx = 0.0
+    group = max(4, oracle.num_threads())  # the oracle runs one head per thread
+    for b in range(w.B):
+        for h0 in range(0, w.H, group):
+            h1 = min(h0 + group, w.H)
+            sl = lambda t: np.ascontiguousarray(t[b:b + 1, :, h0:h1])
+            ref = oracle.forward(sl(q), sl(k), sl(v), sl(g), grid)
+            got = out[b:b + 1, :, h0:h1].double().numpy()
+            d2 += float(np.sum((got - ref) ** 2))
+            r2 += float(np.sum(ref ** 2))
+            mx = max(mx, float(np.max(np.abs(got - ref))))
+    rel = (d2 / r2) ** 0.5
+    say(f"  {w.name} all outputs: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_TOL and mx <= ABS_TOL
 
 
 def test_proj_deterministic_and_workspace_entry_point():
