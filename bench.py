@@ -9,17 +9,23 @@ through three copies of the inputs, so no pass finds its inputs left in the
 backward benches).
 
 Prints ONE JSON line.  `value` is tokens/s per layer (B*N tokens per step).
-`value` and `ms_per_step` come from K uninstrumented passes (wall clock,
-synchronised on both sides).  `roofline` reports the output kernel (the
-largest byte stream: q, g read and out written, 6*D bytes per (token, head))
-from HIP events recorded around it, on the stream it runs on, in K further
-passes right after; `traffic` is its HBM bytes per
-launch from the committed rocprofv3 byte counters (profiles/), or null when
-the kernel source differs from the one those counters were taken on.
-`cold_cache_median_ms` gives the median times of K more passes, each after a
-512 MiB read that evicts the last-level cache: the same as the rest on the
-5B 720p shapes, whose tensors exceed that cache, and the honest figure on
-the small shapes, whose tensors would otherwise be read from it.
+`value` and `ms_per_step` come from K uninstrumented passes of
+gla_forward_ws (wall clock, synchronised on both sides).  `roofline`
+reports the output kernel (the largest byte stream: q, g read and out
+written, 6*D bytes per (token, head)) from HIP events recorded around
+gla_output_ws, on the stream it runs on, in max(50, K) further passes;
+`state_roofline` does the same for the state half (k, v read, 4*D bytes per
+(token, head)); `traffic` is the output kernel's HBM bytes per launch from
+the committed rocprofv3 byte counters (profiles/), or null when the kernel
+source differs from the one those counters were taken on.
+`all_configs` holds, for each of the five layer shapes, the median of
+max(50, K) event-timed passes, warm and after a 512 MiB read that evicts
+the last-level cache before each pass (the honest figure on the small
+shapes, whose tensors would otherwise be read from that cache).
+`streaming_ceiling` is what plain 16-byte non-temporal streaming reaches on
+the same GPU, in the state half's mix (two reads) and the output half's
+(two reads, one write), and each shape's `frac_of_streaming_ceiling` the
+pass time those rates imply over its measured median.
 `cpu_baseline` times the fp64 oracle on a sample of the workload's heads
 (about ten seconds of CPU work) and scales to the whole workload.
 
@@ -74,10 +80,12 @@ def cpu_baseline(w, q, k, v, g, min_seconds=10.0):
     return {
         "value": (w.B * w.N) / whole,
         "unit": "tokens/s",
-        "cores": hs,
+        "cores": threads,
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
-        "sample": f"{hs} of {w.B * w.H} heads (batch 0, all N={w.N} tokens), {reps} passes in "
-                  f"{dt:.1f} s; {per_head:.3f} s per head, scaled to {w.B * w.H} heads",
+        "sample": f"{hs} of {w.B * w.H} heads (batch 0, all N={w.N} tokens, one head per "
+                  f"OpenMP thread), {reps} passes in {dt:.1f} s; {per_head:.3f} s per head, "
+                  f"scaled to {w.B * w.H} heads",
     }
 
 
@@ -236,6 +244,7 @@ def softmax_cpu_baseline(w, q, k, v, g, min_seconds=10.0):
         "value": (w.B * w.N) / whole,
         "unit": "tokens/s",
         "cores": threads,
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"{rows_done} query rows of head (0, 0) against all N={w.N} keys in "
                   f"{dt:.1f} s; {per_row * 1e3:.2f} ms per row, scaled to "
@@ -326,7 +335,8 @@ def backward_cpu_baseline(w, q, k, v, g, dout, min_seconds=10.0):
     return {
         "value": (w.B * w.N) / (per_head * w.B * w.H),
         "unit": "tokens/s",
-        "cores": hs,
+        "cores": threads,
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"{hs} of {w.B * w.H} heads (batch 0, all N={w.N} tokens), {reps} passes in "
                   f"{dt:.1f} s; {per_head:.3f} s per head, scaled to {w.B * w.H} heads",
@@ -456,6 +466,7 @@ def proj_cpu_baseline(w, x, wt, min_seconds=10.0):
         "value": (w.B * w.N) / (per_head * w.B * w.H),
         "unit": "tokens/s",
         "cores": oracle.num_threads(),
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"{heads} heads of batch 0 (all N={w.N} tokens, C={w.C}) in {dt:.1f} s; "
                   f"{per_head:.2f} s per head, scaled to {w.B * w.H} heads",
@@ -530,6 +541,222 @@ def proj_bench(args, w, gla, dev):
     print(json.dumps(result), flush=True)
 
 
+STREAM_PROBE_BYTES = 768 << 20  # per buffer; three sets of three exceed the 256 MB MALL
+
+
+def stream_ceiling(gla, dev, stream, reps=20):
+    """The GPU's plain-streaming bandwidth on the mixer's load path
+    (gla_stream_probe): two read streams (the state half's mix) and two reads
+    plus one write (the output half's mix), over three rotating sets of
+    768 MiB buffers, median of `reps` timed launches each."""
+    import torch
+    sets = [tuple(torch.empty(STREAM_PROBE_BYTES, dtype=torch.uint8, device=dev) for _ in range(3))
+            for _ in range(ROTATE)]
+    for st in sets:
+        for t in st:
+            t.fill_(1)
+    res = {}
+    for mode, name, streams in ((0, "read_2_streams", 2), (1, "read_2_write_1", 3)):
+        for i in range(3):
+            gla.gla_stream_probe(*sets[i % ROTATE], mode, stream)
+        ts = []
+        for i in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            gla.gla_stream_probe(*sets[i % ROTATE], mode, stream)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = statistics.median(ts)
+        res[name] = {"GB/s": streams * STREAM_PROBE_BYTES / (ms * 1e-3) / 1e9, "ms": ms}
+    del sets
+    torch.cuda.synchronize()
+    res["buffers"] = f"3 rotating sets of 3 x {STREAM_PROBE_BYTES >> 20} MiB"
+    return res
+
+
+def device_inputs(w, dev):
+    """Inputs of a timing-only shape, drawn on the GPU (N(0, 1), q and k
+    scaled by the workload's qk_scale, rounded to bf16): the same
+    distribution as the seeded CPU inputs, without minutes of host work on
+    the long shapes."""
+    import torch
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    out = []
+    for i in range(4):
+        x = torch.randn((w.B, w.N, w.H, w.D), generator=gen, dtype=torch.float32, device=dev)
+        if i < 2 and w.qk_scale != 1.0:
+            x.mul_(w.qk_scale)
+        out.append(x.to(torch.bfloat16))
+        del x
+    return tuple(out)
+
+
+def time_forward(gla, w, sets, rope, ws, out, stream, n, evict=None):
+    """Median and mean of n passes of gla_forward_ws (HIP events on the launch
+    stream around each call), cycling through the input sets; with `evict`,
+    a 512 MiB read runs before each pass outside its events."""
+    import torch
+    ts = []
+    for i in range(n):
+        qs, ks, vs, gs = sets[i % len(sets)]
+        if evict is not None:
+            evict.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gla.gla_forward_ws(qs, ks, vs, gs, rope, out, ws, stream)
+        e1.record(stream)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ts]
+    return statistics.median(ms), sum(ms) / len(ms)
+
+
+def config_figures(w, ms):
+    units = w.B * w.N * w.H
+    nbytes = 10 * w.D * units
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": ms, "tokens_per_s": w.B * w.N / (ms * 1e-3), "GB/s": gbps,
+            "frac_of_8TBps": gbps / PEAK_HBM_GBPS, "algorithmic_bytes": nbytes}
+
+
+def forward_bench(args, w, gla, dev, stream, host_inputs, dev_inputs):
+    """The bidirectional mixer.  Headline: K wall-clock passes of
+    gla_forward_ws on the workload (one call per pass, inputs resident in
+    HBM, three rotating sets).  Then, on every one of the five layer shapes,
+    the median of >= 50 event-timed passes (warm and after a 512 MiB cache
+    eviction); per-kernel event times of the two halves on the headline
+    workload for the roofline; the streaming ceiling; the oracle baseline."""
+    import torch
+    from workloads import WORKLOADS
+
+    npass = max(50, args.steps)
+    configs = list(WORKLOADS) if any(x.name == w.name for x in WORKLOADS) else [w]
+    scratch = torch.zeros(EVICT_BYTES // 4, dtype=torch.float32, device=dev)
+    all_cfg = []
+    headline = None
+    for wl in configs:
+        if wl.name == w.name:
+            qd, kd, vd, gd = dev_inputs
+        else:
+            qd, kd, vd, gd = device_inputs(wl, dev)
+        sets = input_sets((qd, kd, vd, gd))
+        del qd, kd, vd, gd
+        rope = gla.gla_rope_create(wl.T, wl.Hh, wl.W, wl.D, wl.theta)
+        ws = gla.alloc_workspace(wl.B, wl.N, wl.H, wl.D, dev)
+        out = torch.empty_like(sets[0][0])
+        for i in range(args.warmup):
+            qs, ks, vs, gs = sets[i % len(sets)]
+            gla.gla_forward_ws(qs, ks, vs, gs, rope, out, ws, stream)
+        torch.cuda.synchronize()
+        if wl.name == w.name:
+            # timed region: exactly K passes, nothing else enqueued
+            log(f"bench: {wl.name}: timing {args.steps} steps")
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                qs, ks, vs, gs = sets[i % len(sets)]
+                gla.gla_forward_ws(qs, ks, vs, gs, rope, out, ws, stream)
+            torch.cuda.synchronize()
+            ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+            # per-kernel durations of the two halves: state (state + reduce
+            # kernels) and output (the output kernel alone), HIP events on the
+            # stream they run on
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(npass)]
+            for i, e in enumerate(evs):
+                qs, ks, vs, gs = sets[i % len(sets)]
+                e[0].record(stream)
+                gla.gla_state_ws(ks, vs, rope, ws, stream)
+                e[1].record(stream)
+                gla.gla_output_ws(qs, gs, rope, out, ws, stream)
+                e[2].record(stream)
+            torch.cuda.synchronize()
+            state_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / npass
+            out_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / npass
+            headline = (ms_step, state_ms, out_ms)
+        log(f"bench: {wl.name}: {npass} event-timed passes, warm and after cache eviction")
+        warm_med, warm_mean = time_forward(gla, wl, sets, rope, ws, out, stream, npass)
+        cold_med, _ = time_forward(gla, wl, sets, rope, ws, out, stream, npass, evict=scratch)
+        fig = config_figures(wl, warm_med)
+        fig.update({"workload": wl.name, "B": wl.B, "N": wl.N, "H": wl.H, "D": wl.D,
+                    "passes": npass, "mean_ms": warm_mean, "cold_cache_median_ms": cold_med,
+                    "cold_cache_frac_of_8TBps": config_figures(wl, cold_med)["frac_of_8TBps"]})
+        all_cfg.append(fig)
+        rope.close()
+        del sets, ws, out
+        torch.cuda.synchronize()
+    del scratch
+    log("bench: streaming ceiling")
+    ceiling = stream_ceiling(gla, dev, stream)
+    rd, rw = ceiling["read_2_streams"]["GB/s"], ceiling["read_2_write_1"]["GB/s"]
+    for fig, wl in zip(all_cfg, configs):
+        units = wl.B * wl.N * wl.H
+        t_ceil = 4 * wl.D * units / (rd * 1e9) + 6 * wl.D * units / (rw * 1e9)
+        fig["frac_of_streaming_ceiling"] = t_ceil * 1e3 / fig["ms"]
+
+    ms_step, state_ms, out_ms = headline
+    units = w.B * w.N * w.H
+    out_bytes = 6 * w.D * units
+    state_bytes = 4 * w.D * units
+    achieved = out_bytes / (out_ms * 1e-3) / 1e9
+    traffic, traffic_src = counter_traffic(w.name)
+    head_fig = next(f for f in all_cfg if f["workload"] == w.name)
+    result = {
+        "metric": METRIC,
+        "value": w.B * w.N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "D": w.D,
+                   "grid": [w.T, w.Hh, w.W], "parallelism": "single-gpu"},
+        "hbm_gbps_effective": 10 * w.D * units / (ms_step * 1e-3) / 1e9,
+        "frac_of_8TBps": 10 * w.D * units / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "pass_median_ms": head_fig["ms"],
+        "pass_median_frac_of_8TBps": head_fig["frac_of_8TBps"],
+        "phases_ms": {"state": state_ms, "output": out_ms},
+        "roofline": {
+            "kernel": "output_persist_kernel",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "traffic_source": traffic_src,
+            "traffic_over_algorithmic": traffic / out_bytes if traffic else None,
+            "algorithmic_bytes": out_bytes,
+            "avg_ms": out_ms,
+        },
+        "state_roofline": {
+            "kernels": "state_tile_kernel + reduce_kernel",
+            "bound": "hbm",
+            "achieved": state_bytes / (state_ms * 1e-3) / 1e9,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": state_bytes / (state_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "algorithmic_bytes": state_bytes,
+            "avg_ms": state_ms,
+        },
+        "streaming_ceiling": ceiling,
+        "all_configs": all_cfg,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle (cpu_baseline)")
+        q, k, v, g = host_inputs
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, g)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -586,130 +813,12 @@ def main():
     if args.backward:
         backward_bench(args, w, gla, dev, (qd, kd, vd, gd), rope, stream)
         return
-    out = torch.empty_like(qd)
-    ws = gla.alloc_workspace(w.B, w.N, w.H, w.D, dev)
     if args.block_frames > 0:
+        out = torch.empty_like(qd)
         block_bench(args, w, gla, dev, (qd, kd, vd, gd), out, rope, stream)
         return
-
-    sets = input_sets((qd, kd, vd, gd))
-
-    def step(ev=None, i=0):
-        qs, ks, vs, gs = sets[i % len(sets)]
-        if ev is not None:
-            ev[0].record(stream)
-        gla.gla_state_ws(ks, vs, rope, ws, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        gla.gla_output_ws(qs, gs, rope, out, ws, stream)
-        if ev is not None:
-            ev[2].record(stream)
-
-    log(f"bench: warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i=i)
-    torch.cuda.synchronize()
-
-    # timed region: exactly K passes, no per-kernel instrumentation
-    log(f"bench: timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i=i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-
-    # per-kernel durations: K more passes with HIP events recorded on the
-    # launch stream around each half (the records themselves add a few
-    # microseconds between kernels, so they stay out of the region above)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"bench: {args.steps} instrumented steps for the per-kernel times")
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evs[i], i)
-    torch.cuda.synchronize()
-    state_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    out_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    ev_step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
-
-    # K more passes from a cold cache: before each, outside its events, a
-    # 512 MiB read on the same stream evicts the 256 MB last-level cache
-    # (MALL), so a workload whose tensors fit in it is still read from HBM.
-    # A read, not a write: lines a write leaves dirty would be written back
-    # inside the next pass (about 50 us at 5B 720p), which no steady state of
-    # the mixer itself causes.
-    cold_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                for _ in range(args.steps)]
-    scratch = torch.zeros(EVICT_BYTES // 4, dtype=torch.float32, device=dev)
-    for i in range(args.warmup):   # settle the zero fill's write-backs
-        scratch.sum()
-        step(i=i)
-    log(f"bench: {args.steps} instrumented steps after cache eviction")
-    for i in range(args.steps):
-        scratch.sum()
-        step(cold_evs[i], i)
-    torch.cuda.synchronize()
-    del scratch
-    cold_state = statistics.median(e[0].elapsed_time(e[1]) for e in cold_evs)
-    cold_out = statistics.median(e[1].elapsed_time(e[2]) for e in cold_evs)
-    cold_step = statistics.median(e[0].elapsed_time(e[2]) for e in cold_evs)
-    units = w.B * w.N * w.H
-    out_bytes = 6 * w.D * units        # q, g read + out written, bf16
-    state_bytes = 4 * w.D * units      # k, v read, bf16
-    all_bytes = out_bytes + state_bytes
-    achieved = out_bytes / (out_ms * 1e-3) / 1e9
-    tokens = w.B * w.N
-    traffic, traffic_src = counter_traffic(w.name)
-    result = {
-        "metric": METRIC,
-        "value": tokens / (ms_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "D": w.D,
-                   "grid": [w.T, w.Hh, w.W], "parallelism": "single-gpu"},
-        "hbm_gbps_effective": all_bytes / (ms_step * 1e-3) / 1e9,
-        "phases_ms": {"state": state_ms, "output": out_ms, "step_events": ev_step_ms},
-        "cold_cache_median_ms": {"state": cold_state, "output": cold_out, "step_events": cold_step,
-                                 "evict_bytes": EVICT_BYTES,
-                                 "output_frac": out_bytes / (cold_out * 1e-3) / 1e9 / PEAK_HBM_GBPS},
-        "roofline": {
-            "kernel": "output_kernel",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBPS,
-            "traffic": traffic,
-            "traffic_source": traffic_src,
-            "traffic_over_algorithmic": traffic / out_bytes if traffic else None,
-            "algorithmic_bytes": out_bytes,
-            "avg_ms": out_ms,
-        },
-        "state_roofline": {
-            "kernels": "state + reduce",
-            "bound": "hbm",
-            "achieved": state_bytes / (state_ms * 1e-3) / 1e9,
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": state_bytes / (state_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-            "algorithmic_bytes": state_bytes,
-            "avg_ms": state_ms,
-        },
-    }
     rope.close()
-    if not args.no_cpu_baseline:
-        log("bench: timing the oracle (cpu_baseline)")
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, g)
-    print(json.dumps(result), flush=True)
+    forward_bench(args, w, gla, dev, stream, (q, k, v, g), (qd, kd, vd, gd))
 
 
 if __name__ == "__main__":

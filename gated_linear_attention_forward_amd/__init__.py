@@ -45,6 +45,7 @@ from .gla import (  # noqa: F401
     gla_softmax_workspace_bytes,
     gla_state,
     gla_state_ws,
+    gla_stream_probe,
     gla_strerror,
     gla_workspace_bytes,
     gla_workspace_bytes_blocks,

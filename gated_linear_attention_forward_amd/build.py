@@ -41,7 +41,8 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    for src in ("gla_kernels.hip", "gla_softmax.hip", "gla_backward.hip", "gla_project.hip"):
+    for src in ("gla_kernels.hip", "gla_softmax.hip", "gla_backward.hip", "gla_project.hip",
+                "gla_probe.hip"):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         _run(["hipcc", *HIP_FLAGS, *FILE_FLAGS.get(src, []), f"-I{INCLUDE}", f"-I{CSRC}", "-c",
               os.path.join(CSRC, src), "-o", obj], verbose)

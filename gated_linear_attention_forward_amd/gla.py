@@ -38,7 +38,7 @@ EXPORTS = (
     "gla_backward_ws", "gla_backward_workspace_bytes", "gla_backward_check",
     "gla_backward_saved", "gla_backward_saved_ws", "gla_backward_saved_check",
     "gla_forward_proj", "gla_forward_proj_ws", "gla_proj_workspace_bytes",
-    "gla_forward_proj_check",
+    "gla_forward_proj_check", "gla_stream_probe",
 )
 
 
@@ -108,6 +108,7 @@ def load_library():
         "gla_forward_proj_ws": ([vp, vp, rp, vp] + [i32] * 5 + [vp, sz, vp], i32),
         "gla_proj_workspace_bytes": ([i32] * 5, sz),
         "gla_forward_proj_check": ([vp, vp, rp, vp] + [i32] * 5, i32),
+        "gla_stream_probe": ([vp, vp, vp, sz, i32, vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -670,3 +671,17 @@ class GatedLinearAttention(torch.autograd.Function):
 def gated_linear_attention(q, k, v, g, rope=None) -> torch.Tensor:
     """The mixer as a differentiable torch op (see GatedLinearAttention)."""
     return GatedLinearAttention.apply(q, k, v, g, rope)
+
+
+def gla_stream_probe(src0: torch.Tensor, src1: torch.Tensor, dst: torch.Tensor, mode: int,
+                     stream=None):
+    """Streams src0 and src1 (and writes dst in mode 1) through the library's
+    bandwidth probe kernel; all three same-sized contiguous device tensors."""
+    nbytes = src0.numel() * src0.element_size()
+    for t in (src0, src1, dst):
+        if t.numel() * t.element_size() != nbytes or not t.is_contiguous():
+            raise ValueError("probe buffers must be contiguous and of one size")
+    with torch.cuda.device(src0.device):
+        _ok(load_library().gla_stream_probe(src0.data_ptr(), src1.data_ptr(), dst.data_ptr(),
+                                            nbytes, int(mode), _stream_handle(stream, src0.device)),
+            "gla_stream_probe")

@@ -386,6 +386,21 @@ int gla_forward_proj_ws(const void* x, const void* w, const gla_rope_tables* rop
 int gla_forward_proj_check(const void* x, const void* w, const gla_rope_tables* rope,
                            const void* out, int B, int N, int C, int H, int D);
 
+/* ---------------------------------------------------------------------
+ * Bandwidth probe (a measurement aid, not part of the mixer).
+ *
+ * Streams `bytes` (a multiple of 16, below 2 GiB) of each of two device
+ * buffers through the load path the mixer's kernels use (16-byte buffer
+ * loads with the non-temporal hint, 64 KB contiguous per block):
+ *   mode 0: reads src0 and src1 (the state half's two read streams);
+ *   mode 1: also writes dst = src0 ^ src1 with non-temporal stores (the
+ *           output half's two reads and one write).
+ * dst must hold `bytes` (mode 0 may write at most 4 KB of it).  Pointers
+ * 16-byte aligned; GLA_ERR_NULL / GLA_ERR_ALIGN / GLA_ERR_DIM before any HIP
+ * call.  Enqueued on `stream`; the caller times it. */
+int gla_stream_probe(const void* src0, const void* src1, void* dst, size_t bytes, int mode,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

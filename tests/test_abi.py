@@ -382,3 +382,60 @@ def test_noalloc_rejects_calls_beyond_its_scratch_before_any_hip_call():
     # argument errors are still reported first
     rc = lib.gla_forward_noalloc(G, 2 * G, 3 * G, 4 * G, None, 5 * G, B, N, H, 96, None)
     assert rc == glamod.GLA_ERR_DIM
+
+
+# ---------------------------------------------------------------------------
+# caller workspaces: the used part may overlap no tensor of the call (checked
+# before any HIP call, so these need no GPU)
+
+def test_forward_workspaces_must_not_overlap_the_tensors():
+    lib = gla.load_library()
+    B, N, H, D = 1, 64, 2, 128
+    nbytes = B * N * H * D * 2
+    need = gla.gla_workspace_bytes(B, N, H, D)
+    W = 64 * A  # a workspace far from every tensor
+
+    def fwd(ws):
+        return lib.gla_forward_ws(A, 2 * A, 3 * A, 4 * A, None, 5 * A, B, N, H, D, ws, need, None)
+
+    def state(ws):
+        return lib.gla_state_ws(2 * A, 3 * A, None, B, N, H, D, ws, need, None)
+
+    def output(ws):
+        return lib.gla_output_ws(A, 4 * A, None, 5 * A, B, N, H, D, ws, need, None)
+
+    for call, tensors in ((fwd, (A, 2 * A, 3 * A, 4 * A, 5 * A)), (state, (2 * A, 3 * A)),
+                          (output, (A, 4 * A, 5 * A))):
+        for t in tensors:
+            assert call(t) == glamod.GLA_ERR_ALIAS                    # starts on a tensor
+            assert call(t + nbytes - 256) == glamod.GLA_ERR_ALIAS     # starts in its tail
+            assert call(t - need + 256) == glamod.GLA_ERR_ALIAS       # ends inside it
+    # too small a workspace is reported as such
+    assert need % 256 == 0
+    assert lib.gla_forward_ws(A, 2 * A, 3 * A, 4 * A, None, 5 * A, B, N, H, D, W,
+                              need - 256, None) == glamod.GLA_ERR_WORKSPACE
+
+
+def test_block_workspace_must_not_overlap_tensors_or_states():
+    lib = gla.load_library()
+    B, N, H, D, L = 1, 64, 2, 128, 16
+    need = gla.gla_workspace_bytes_blocks(B, N, H, D, L)
+
+    def call(ws, S_in=8 * A, z_in=9 * A, S_out=10 * A, z_out=11 * A):
+        return lib.gla_forward_blocks_ws(A, 2 * A, 3 * A, 4 * A, None, 5 * A, B, N, H, D, L,
+                                         S_in, z_in, S_out, z_out, ws, need, None)
+
+    assert call(3 * A + 512) == glamod.GLA_ERR_ALIAS        # inside v
+    assert call(8 * A) == glamod.GLA_ERR_ALIAS              # on the carried state
+    assert call(11 * A - need + 256) == glamod.GLA_ERR_ALIAS  # ends on the returned z
+
+
+def test_stream_probe_validates_before_launching():
+    lib = gla.load_library()
+    assert lib.gla_stream_probe(0, 2 * A, 3 * A, 1 << 20, 0, None) == glamod.GLA_ERR_NULL
+    assert lib.gla_stream_probe(A, 2 * A, 0, 1 << 20, 1, None) == glamod.GLA_ERR_NULL
+    assert lib.gla_stream_probe(A + 8, 2 * A, 3 * A, 1 << 20, 0, None) == glamod.GLA_ERR_ALIGN
+    assert lib.gla_stream_probe(A, 2 * A, 3 * A, 0, 0, None) == glamod.GLA_ERR_DIM
+    assert lib.gla_stream_probe(A, 2 * A, 3 * A, 1000, 0, None) == glamod.GLA_ERR_DIM
+    assert lib.gla_stream_probe(A, 2 * A, 3 * A, 1 << 31, 0, None) == glamod.GLA_ERR_DIM
+    assert lib.gla_stream_probe(A, 2 * A, 3 * A, 1 << 20, 2, None) == glamod.GLA_ERR_DIM
