@@ -624,20 +624,30 @@ def config_figures(w, ms):
 
 
 def forward_bench(args, w, gla, dev, stream, host_inputs, dev_inputs):
-    """The bidirectional mixer.  Headline: K wall-clock passes of
-    gla_forward_ws on the workload (one call per pass, inputs resident in
-    HBM, three rotating sets).  Then, on every one of the five layer shapes,
-    the median of >= 50 event-timed passes (warm and after a 512 MiB cache
-    eviction); per-kernel event times of the two halves on the headline
-    workload for the roofline; the streaming ceiling; the oracle baseline."""
+    """The bidirectional mixer.  First, on every one of the five layer
+    shapes, the median of >= 50 event-timed passes of gla_forward_ws (warm,
+    and after a 512 MiB cache eviction).  Then the headline on the workload:
+    W warmup passes and K wall-clock passes (one call per pass, inputs
+    resident in HBM, three rotating sets), and per-kernel event times of the
+    two halves for the roofline.  Last, the streaming ceiling and the oracle
+    baseline."""
     import torch
     from workloads import WORKLOADS
 
     npass = max(50, args.steps)
     configs = list(WORKLOADS) if any(x.name == w.name for x in WORKLOADS) else [w]
+    if args.no_sweep:
+        configs = [w]
     scratch = torch.zeros(EVICT_BYTES // 4, dtype=torch.float32, device=dev)
+    # about half a second of streaming first, untimed: an idle GPU runs its
+    # first milliseconds of work at lower clocks
+    spin_end = time.perf_counter() + 0.5
+    while time.perf_counter() < spin_end:
+        for _ in range(100):
+            scratch.sum()
+        torch.cuda.synchronize()
     all_cfg = []
-    headline = None
+    head = None
     for wl in configs:
         if wl.name == w.name:
             qd, kd, vd, gd = dev_inputs
@@ -648,35 +658,10 @@ def forward_bench(args, w, gla, dev, stream, host_inputs, dev_inputs):
         rope = gla.gla_rope_create(wl.T, wl.Hh, wl.W, wl.D, wl.theta)
         ws = gla.alloc_workspace(wl.B, wl.N, wl.H, wl.D, dev)
         out = torch.empty_like(sets[0][0])
-        for i in range(args.warmup):
+        for i in range(3):
             qs, ks, vs, gs = sets[i % len(sets)]
             gla.gla_forward_ws(qs, ks, vs, gs, rope, out, ws, stream)
         torch.cuda.synchronize()
-        if wl.name == w.name:
-            # timed region: exactly K passes, nothing else enqueued
-            log(f"bench: {wl.name}: timing {args.steps} steps")
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for i in range(args.steps):
-                qs, ks, vs, gs = sets[i % len(sets)]
-                gla.gla_forward_ws(qs, ks, vs, gs, rope, out, ws, stream)
-            torch.cuda.synchronize()
-            ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-            # per-kernel durations of the two halves: state (state + reduce
-            # kernels) and output (the output kernel alone), HIP events on the
-            # stream they run on
-            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(npass)]
-            for i, e in enumerate(evs):
-                qs, ks, vs, gs = sets[i % len(sets)]
-                e[0].record(stream)
-                gla.gla_state_ws(ks, vs, rope, ws, stream)
-                e[1].record(stream)
-                gla.gla_output_ws(qs, gs, rope, out, ws, stream)
-                e[2].record(stream)
-            torch.cuda.synchronize()
-            state_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / npass
-            out_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / npass
-            headline = (ms_step, state_ms, out_ms)
         log(f"bench: {wl.name}: {npass} event-timed passes, warm and after cache eviction")
         warm_med, warm_mean = time_forward(gla, wl, sets, rope, ws, out, stream, npass)
         cold_med, _ = time_forward(gla, wl, sets, rope, ws, out, stream, npass, evict=scratch)
@@ -685,19 +670,54 @@ def forward_bench(args, w, gla, dev, stream, host_inputs, dev_inputs):
                     "passes": npass, "mean_ms": warm_mean, "cold_cache_median_ms": cold_med,
                     "cold_cache_frac_of_8TBps": config_figures(wl, cold_med)["frac_of_8TBps"]})
         all_cfg.append(fig)
-        rope.close()
+        if wl.name == w.name:
+            head = (sets, rope, ws, out)  # timed below, after the sweep
+        else:
+            rope.close()
         del sets, ws, out
         torch.cuda.synchronize()
     del scratch
-    log("bench: streaming ceiling")
-    ceiling = stream_ceiling(gla, dev, stream)
-    rd, rw = ceiling["read_2_streams"]["GB/s"], ceiling["read_2_write_1"]["GB/s"]
-    for fig, wl in zip(all_cfg, configs):
-        units = wl.B * wl.N * wl.H
-        t_ceil = 4 * wl.D * units / (rd * 1e9) + 6 * wl.D * units / (rw * 1e9)
-        fig["frac_of_streaming_ceiling"] = t_ceil * 1e3 / fig["ms"]
 
-    ms_step, state_ms, out_ms = headline
+    # the headline: W warmup passes, then exactly K passes, nothing else
+    # enqueued, on the GPU the sweep above has brought up to speed
+    sets, rope, ws, out = head
+    log(f"bench: {w.name}: {args.warmup} warmup steps, then timing {args.steps} steps")
+    for i in range(args.warmup):
+        qs, ks, vs, gs = sets[i % len(sets)]
+        gla.gla_forward_ws(qs, ks, vs, gs, rope, out, ws, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        qs, ks, vs, gs = sets[i % len(sets)]
+        gla.gla_forward_ws(qs, ks, vs, gs, rope, out, ws, stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # per-kernel durations of the two halves: state (state + reduce kernels)
+    # and output (the output kernel alone), HIP events on the stream they run on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(npass)]
+    for i, e in enumerate(evs):
+        qs, ks, vs, gs = sets[i % len(sets)]
+        e[0].record(stream)
+        gla.gla_state_ws(ks, vs, rope, ws, stream)
+        e[1].record(stream)
+        gla.gla_output_ws(qs, gs, rope, out, ws, stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    state_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / npass
+    out_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / npass
+    rope.close()
+    del head, sets, ws, out
+    torch.cuda.synchronize()
+    ceiling = None
+    if not args.no_sweep:
+        log("bench: streaming ceiling")
+        ceiling = stream_ceiling(gla, dev, stream)
+        rd, rw = ceiling["read_2_streams"]["GB/s"], ceiling["read_2_write_1"]["GB/s"]
+        for fig, wl in zip(all_cfg, configs):
+            units = wl.B * wl.N * wl.H
+            t_ceil = 4 * wl.D * units / (rd * 1e9) + 6 * wl.D * units / (rw * 1e9)
+            fig["frac_of_streaming_ceiling"] = t_ceil * 1e3 / fig["ms"]
+
     units = w.B * w.N * w.H
     out_bytes = 6 * w.D * units
     state_bytes = 4 * w.D * units
@@ -764,6 +784,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="time only the workload (no five-shape sweep, no streaming ceiling): "
+                         "for profiler runs whose kernel statistics must cover it alone")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (for hardware byte counters)")
     ap.add_argument("--block-frames", type=int, default=0,
