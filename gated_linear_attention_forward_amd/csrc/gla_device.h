@@ -108,6 +108,7 @@ struct TabView {
   int tbase;   // first t-row present
   int ntr;     // t-rows present
   int t_last;  // last t of the block's tokens (positions past the range clamp to it)
+  const uint32_t* tab16;  // the same pairs as packed fp16 (cos, sin), when so staged
 };
 
 // Copies n float2 from global memory to LDS with a block of NT threads,
@@ -130,6 +131,29 @@ __device__ __forceinline__ void copy_to_lds(float2* dst, const float2* src, int 
   }
 }
 
+// copy_to_lds, rounding each (cos, sin) pair to fp16 (round to nearest even)
+// and packing it into one dword: half the LDS of the fp32 pairs.
+template <int NT>
+__device__ __forceinline__ void copy_to_lds_f16(uint32_t* dst, const float2* src, int n) {
+  for (int b0 = threadIdx.x; b0 < n; b0 += 4 * NT) {
+    float2 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = b0 + k * NT;
+      if (i < n) v[k] = src[i];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = b0 + k * NT;
+      if (i < n) {
+        const _Float16 c = (_Float16)v[k].x, sn = (_Float16)v[k].y;
+        dst[i] = (uint32_t)__builtin_bit_cast(uint16_t, c) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, sn) << 16);
+      }
+    }
+  }
+}
+
 // Copies the table rows a block of NT threads needs into LDS.  Caller
 // synchronises.
 template <int D, int NT = 256>
@@ -137,6 +161,7 @@ __device__ __forceinline__ TabView stage_table(const KArgs& a, float2* ltab, boo
                                                int n_begin, int n_end) {
   using X = Axes<D>;
   TabView tv;
+  tv.tab16 = nullptr;
   const int t_first = (int)fast_div((uint32_t)n_begin, a.div_hw);
   tv.t_last = (int)fast_div((uint32_t)(n_end - 1), a.div_hw);
   if (in_lds) {
@@ -220,7 +245,7 @@ struct GridWalk {
 // (cos, sin) of pair p, where p is known to lie in [PMIN, PMAX]: when that
 // range sits inside one axis block the table row is chosen at compile time,
 // otherwise by masks (no branches).
-template <int D, int PMIN, int PMAX>
+template <int D, int PMIN, int PMAX, bool H16 = false>
 __device__ __forceinline__ float2 rope_factor(const TabView& tv, const RowOff& r, int p) {
   using X = Axes<D>;
   int base;
@@ -235,17 +260,23 @@ __device__ __forceinline__ float2 rope_factor(const TabView& tv, const RowOff& r
     const int mx = -(int)(p >= X::Pt + X::Py);
     base = r.ot + ((r.oy - r.ot) & my) + ((r.ox - r.ot) & mx);
   }
-  return tv.tab[base + p];
+  if constexpr (H16) {
+    const uint32_t w = tv.tab16[base + p];
+    return float2{(float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)),
+                  (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16))};
+  } else {
+    return tv.tab[base + p];
+  }
 }
 
 // RoPE factors of the 4 pairs of one 16-byte chunk: chunk index c = 4 S + m
 // with S compile-time and m in [0, 3].
-template <int D, int S>
+template <int D, int S, bool H16 = false>
 __device__ __forceinline__ void rope_factors(const TabView& tv, const RowOff& ro, int m,
                                              float2 (&cs)[4]) {
   static_for<4>([&](auto U) {
     constexpr int u = decltype(U)::value;
-    cs[u] = rope_factor<D, 16 * S + u, 16 * S + 12 + u>(tv, ro, 4 * (4 * S + m) + u);
+    cs[u] = rope_factor<D, 16 * S + u, 16 * S + 12 + u, H16>(tv, ro, 4 * (4 * S + m) + u);
   });
 }
 
@@ -262,11 +293,11 @@ __device__ __forceinline__ u32x4 rotate_chunk(const u32x4 fq, const float2 (&cs)
   return pk;
 }
 
-template <int D, int S>
+template <int D, int S, bool H16 = false>
 __device__ __forceinline__ u32x4 rope_chunk(const u32x4 fq, const TabView& tv, const RowOff& ro,
                                             int m) {
   float2 cs[4];
-  rope_factors<D, S>(tv, ro, m, cs);
+  rope_factors<D, S, H16>(tv, ro, m, cs);
   return rotate_chunk(fq, cs);
 }
 

@@ -87,6 +87,8 @@ constexpr int kOutputBlocks = 2048;
 constexpr int kPersistBlocks = 256;
 constexpr size_t kPersistLdsBytes = 90 * 1024;
 constexpr size_t kMaxPersistTableBytes = 56 * 1024;
+// LDS a block may ask for on gfx950 (160 KB per compute unit).
+constexpr size_t kMaxLdsPerBlock = 160 * 1024;
 // The backward pass's query and key kernels (8 waves, one block per compute
 // unit) take their token ranges from a plan of at most this many blocks:
 // one round of long ranges, each block staging its head's operands once.

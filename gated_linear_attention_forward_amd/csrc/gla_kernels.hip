@@ -1166,29 +1166,38 @@ void state_tile_kernel(KArgs a) {
 // rows at any time, which measured faster than both the per-range blocks of
 // output_kernel (that restage S for every range) and long contiguous ranges
 // per block.  A step is output_kernel's step (same arithmetic, same result).
-template <int D, bool ROPE, bool TLDS>
+template <int D, bool ROPE, bool TLDS, int G, bool T16, bool QROWS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void output_persist_kernel(KArgs a, int nsub) {
-  constexpr bool QROWS = D == 128;  // whole-row q loads (four rows of 16 chunks)
+  // QROWS: whole-row q loads (four rows of 16 chunks) through a per-wave LDS
+  // tile (D = 128)
+  static_assert(!QROWS || D == 128, "whole-row q tiles");
   constexpr int QT = 16 * 2 * D;    // per-wave q tile in LDS
   constexpr int KS = D / 32;
   constexpr int MB = D / 16;
   constexpr int OB = 2 * MB;
   constexpr int OW = OB / 4;
   constexpr int ROWS = D + 2;
+  constexpr int OPB = ROWS * 2 * D;  // one head's S operand and z rows
+  constexpr int RANGE = 64 / G;      // tokens of a head per block and step
+  static_assert(G == 1 || ((G == 2 || G == 4) && D == 128), "heads per block");
+  static_assert(!T16 || (TLDS && G > 1), "fp16 pairs only in a grouped block's LDS table");
   using OChunk = typename Chunk<OB>::T;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* sS = smem;
-  unsigned char* myq = smem + ROWS * 2 * D + (threadIdx.x >> 6) * QT;
-  float2* ltab = reinterpret_cast<float2*>(smem + ROWS * 2 * D + (QROWS ? 4 * QT : 0));
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane >> 4;
   const int col = lane & 15;
-  const int bh = blockIdx.x;  // heads vary fastest over the grid
-  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  unsigned char* sS = smem + (wave % G) * OPB;
+  unsigned char* myq = smem + G * OPB + wave * QT;
+  float2* ltab = reinterpret_cast<float2*>(smem + G * OPB + (QROWS ? 4 * QT : 0));
+  // head groups vary fastest over the grid; wave w takes head G g + w % G of
+  // the group's batch element, and tokens 16 (w / G) .. of each range
+  const int hgs = a.H / G;
+  const int b = (int)blockIdx.x / hgs;
+  const int h = ((int)blockIdx.x - b * hgs) * G + wave % G;
+  const int bh = b * a.H + h;
   const int s = blockIdx.y;
   const int N = a.N;
   TabView tv{};
@@ -1260,7 +1269,7 @@ void output_persist_kernel(KArgs a, int nsub) {
     bf16x8 Aq[KS];
     static_for<KS>([&](auto S2) {
       constexpr int s2 = decltype(S2)::value;
-      Aq[s2] = __builtin_bit_cast(bf16x8, ROPE ? rope_chunk<D, s2>(fq[s2], tv, rof, m) : fq[s2]);
+      Aq[s2] = __builtin_bit_cast(bf16x8, ROPE ? rope_chunk<D, s2, T16>(fq[s2], tv, rof, m) : fq[s2]);
     });
     f32x4 acc[MB];
     bf16x8 Bf[2][KS];
@@ -1301,14 +1310,53 @@ void output_persist_kernel(KArgs a, int nsub) {
     }
   };
 
-  // the wave's steps: tokens 64 r + 16 wave .. for ranges r = s + k nsub
-  const int stride = 64 * nsub;
-  int base = 64 * s + 16 * wave;
+  // the wave's steps: tokens RANGE r + 16 (wave / G) .. for ranges
+  // r = s + k nsub
+  const int stride = RANGE * nsub;
+  int base = RANGE * s + 16 * (wave / G);
   if (ROPE) gw.init(a, (uint32_t)min(base + col, N - 1), (uint32_t)stride);
   u32x4 qa[KS], qb[KS];
   OChunk ga[4], gb[4];
   if (base < N) load_qg(base, qa, ga);
-  {
+  if constexpr (G > 1) {
+    // the waves of head slot w % G (4 / G of them) stage that head's operand
+    // together, eight 16-byte chunks per lane in flight at a time
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.sl + (size_t)bh * ROWS * D);
+    constexpr int CH = ROWS * D / 8;
+    constexpr int WPH = 4 / G;  // waves per head
+    const int li = (wave / G) * 64 + lane;
+#pragma unroll
+    for (int k0 = 0; k0 < CH; k0 += 8 * 64 * WPH) {
+      u32x4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = k0 + 64 * WPH * k + li;
+        if (i < CH) v[k] = src[i];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = k0 + 64 * WPH * k + li;
+        if (i < CH)
+          *reinterpret_cast<u32x4*>(sS + row_tile_offset<D>(i / (D / 8), 16 * (i % (D / 8)))) = v[k];
+      }
+    }
+    if (ROPE) {
+      if (T16) {
+        uint32_t* lt16 = reinterpret_cast<uint32_t*>(ltab);
+        copy_to_lds_f16<256>(lt16, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        tv.tab16 = lt16;
+        tv.tab = nullptr;
+      } else if (TLDS) {
+        copy_to_lds<256>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        tv.tab = ltab;
+      } else {
+        tv.tab = a.cs;
+      }
+      tv.tbase = 0;
+      tv.ntr = a.T;
+      tv.t_last = a.T - 1;
+    }
+  } else {
     RowStage<D, D, 256> st_s;
     RowStage<D, 2, 256, D> st_z;
     const uint16_t* sl = a.sl + (size_t)bh * ROWS * D;
@@ -1426,28 +1474,71 @@ hipError_t launch_state_d(const Plan& p, KArgs a, hipStream_t stream) {
   return launch_reduce_d<D>(p, a, stream);
 }
 
+// A kernel as a type, so one generic launch helper can take any of them.
+template <auto K>
+struct KernelTag {
+  static constexpr auto value = K;
+};
+
+size_t persist_table_pairs(const KArgs& a) {
+  return (size_t)a.T * a.Pt + (size_t)a.Hh * a.Py + (size_t)a.W * a.Px;
+}
+// LDS of a persistent output block besides the table: G heads' S operands
+// and, with whole-row q loads, the four waves' q tiles.
+template <int D, int G, bool QR>
+constexpr size_t persist_fixed_lds() {
+  return G * output_lds_bytes<D>() + (QR ? 4 * 16 * 2 * D : 0);
+}
+
+// Persistent output launch with G heads per block: about kPersistBlocks
+// blocks, one per compute unit (the LDS request keeps a second block off).
+// The RoPE table goes into LDS as fp32 pairs when it fits, else (grouped
+// blocks only) as fp16 pairs, else it is read from global memory.
+template <int D, int G, bool QR>
+hipError_t launch_output_persist(const Plan& p, KArgs a, hipStream_t stream) {
+  const int groups = p.BH / G;
+  const int nsub = kPersistBlocks / groups > 0 ? kPersistBlocks / groups : 1;
+  const size_t pairs = persist_table_pairs(a);
+  const size_t fixed = persist_fixed_lds<D, G, QR>();
+  const bool t32 = a.cs && 8 * pairs <= kMaxPersistTableBytes && fixed + 8 * pairs <= kMaxLdsPerBlock;
+  const bool t16 = G > 1 && a.cs && !t32 && fixed + 4 * pairs <= kMaxLdsPerBlock;
+  size_t lds = fixed + (t32 ? 8 * pairs : (t16 ? 4 * pairs : 0));
+  if (lds < kPersistLdsBytes) lds = kPersistLdsBytes;
+  const dim3 g(groups, nsub);
+  auto go = [&](auto kern) -> hipError_t {
+    hipError_t e = allow_lds<decltype(kern)::value>(lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decltype(kern)::value, g, dim3(256), lds, stream, a, nsub);
+    return hipGetLastError();
+  };
+  if (!a.cs) return go(KernelTag<output_persist_kernel<D, false, false, G, false, QR>>{});
+  if (t32) return go(KernelTag<output_persist_kernel<D, true, true, G, false, QR>>{});
+  if constexpr (G > 1) {
+    if (t16) return go(KernelTag<output_persist_kernel<D, true, true, G, true, QR>>{});
+  }
+  return go(KernelTag<output_persist_kernel<D, true, false, G, false, QR>>{});
+}
+
 template <int D>
 hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream) {
   if (p.NB == 1) {
-    // persistent: NS blocks per head, one block per compute unit
-    const int nsub = kPersistBlocks / p.BH > 0 ? kPersistBlocks / p.BH : 1;
-    const size_t tb = 8 * ((size_t)a.T * a.Pt + (size_t)a.Hh * a.Py + (size_t)a.W * a.Px);
-    const bool tl = a.cs && tb <= kMaxPersistTableBytes;
-    size_t lds = output_lds_bytes<D>() + (D == 128 ? 4 * 16 * 2 * D : 0) + (tl ? tb : 0);
-    if (lds < kPersistLdsBytes) lds = kPersistLdsBytes;
-    const dim3 g(p.BH, nsub);
-    hipError_t e;
-    if (!a.cs) {
-      if ((e = allow_lds<output_persist_kernel<D, false, false>>(lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((output_persist_kernel<D, false, false>), g, dim3(256), lds, stream, a, nsub);
-    } else if (tl) {
-      if ((e = allow_lds<output_persist_kernel<D, true, true>>(lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((output_persist_kernel<D, true, true>), g, dim3(256), lds, stream, a, nsub);
-    } else {
-      if ((e = allow_lds<output_persist_kernel<D, true, false>>(lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((output_persist_kernel<D, true, false>), g, dim3(256), lds, stream, a, nsub);
+    if constexpr (D == 128) {
+      // as many heads per block (4, then 2) as divide H with the table in LDS
+      // (fp16 pairs at least; whole-row q tiles if they fit beside it): the
+      // blocks of a group read whole contiguous runs of the group's heads,
+      // which streams faster than one head's rows
+      const size_t tb16 = a.cs ? 4 * persist_table_pairs(a) : 0;
+      if (p.H % 4 == 0) {
+        if (persist_fixed_lds<D, 4, true>() + tb16 <= kMaxLdsPerBlock)
+          return launch_output_persist<D, 4, true>(p, a, stream);
+        if (persist_fixed_lds<D, 4, false>() + tb16 <= kMaxLdsPerBlock)
+          return launch_output_persist<D, 4, false>(p, a, stream);
+      }
+      if (p.H % 2 == 0 && persist_fixed_lds<D, 2, true>() + tb16 <= kMaxLdsPerBlock)
+        return launch_output_persist<D, 2, true>(p, a, stream);
+      return launch_output_persist<D, 1, true>(p, a, stream);
     }
-    return hipGetLastError();
+    return launch_output_persist<D, 1, false>(p, a, stream);
   }
   const dim3 g3(p.BH, p.C2);
   const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;
