@@ -87,6 +87,9 @@ constexpr int kOutputBlocks = 2048;
 constexpr int kPersistBlocks = 256;
 constexpr size_t kPersistLdsBytes = 90 * 1024;
 constexpr size_t kMaxPersistTableBytes = 56 * 1024;
+// Steps per wave below which the persistent output kernel keeps one head
+// per block (staging several heads' operands would not pay).
+constexpr int kGroupMinSteps = 16;
 // LDS a block may ask for on gfx950 (160 KB per compute unit).
 constexpr size_t kMaxLdsPerBlock = 160 * 1024;
 // The backward pass's query and key kernels (8 waves, one block per compute

@@ -1526,15 +1526,24 @@ hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream) {
       // as many heads per block (4, then 2) as divide H with the table in LDS
       // (fp16 pairs at least; whole-row q tiles if they fit beside it): the
       // blocks of a group read whole contiguous runs of the group's heads,
-      // which streams faster than one head's rows
+      // which streams faster than one head's rows.  A block stages G heads'
+      // operands, so this pays only where each wave then runs at least
+      // kGroupMinSteps steps (5B 480p/81f, with about 5, measured 19.5 us
+      // per output pass with one head per block and 22.7 with four).
       const size_t tb16 = a.cs ? 4 * persist_table_pairs(a) : 0;
-      if (p.H % 4 == 0) {
+      auto steps = [&](int G) {
+        const int groups = p.BH / G;
+        const int nsub = kPersistBlocks / groups > 0 ? kPersistBlocks / groups : 1;
+        return (p.N + 64 / G * nsub - 1) / (64 / G * nsub);
+      };
+      if (p.H % 4 == 0 && steps(4) >= kGroupMinSteps) {
         if (persist_fixed_lds<D, 4, true>() + tb16 <= kMaxLdsPerBlock)
           return launch_output_persist<D, 4, true>(p, a, stream);
         if (persist_fixed_lds<D, 4, false>() + tb16 <= kMaxLdsPerBlock)
           return launch_output_persist<D, 4, false>(p, a, stream);
       }
-      if (p.H % 2 == 0 && persist_fixed_lds<D, 2, true>() + tb16 <= kMaxLdsPerBlock)
+      if (p.H % 2 == 0 && steps(2) >= kGroupMinSteps &&
+          persist_fixed_lds<D, 2, true>() + tb16 <= kMaxLdsPerBlock)
         return launch_output_persist<D, 2, true>(p, a, stream);
       return launch_output_persist<D, 1, true>(p, a, stream);
     }

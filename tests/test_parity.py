@@ -73,11 +73,12 @@ SMALL = [
     (2, 2, 128, (7, 11, 13)),   # 1001 tokens, B = 2
     (1, 1, 128, (1, 1, 65)),    # one past a tile
     (3, 1, 32, (5, 7, 11)),     # 385 tokens, D = 32, B = 3
-    (1, 4, 128, (2, 3, 43)),    # four heads to a block of the output kernel, ragged
-    (2, 8, 128, (3, 7, 11)),    # two head groups per batch element, B = 2
+    (1, 4, 128, (2, 3, 43)),    # four heads, too short to group them (one per block)
     (1, 4, 128, (1, 1, 1)),     # four heads, a single token
-    (1, 4, 128, (200, 1, 1)),   # four heads, a RoPE table too long for LDS beside the q tiles
-    (1, 6, 128, (3, 5, 9)),     # six heads: two to a block
+    (1, 4, 128, (64, 32, 33)),  # 67,584 tokens: four heads to an output block, ragged
+    (2, 8, 128, (16, 40, 103)), # 65,920 tokens, B = 2: two head groups per batch element
+    (1, 4, 128, (200, 3, 110)), # four heads, a RoPE table too long for LDS beside the q tiles
+    (1, 6, 128, (45, 31, 32)),  # six heads: two to an output block
 ]
 
 
