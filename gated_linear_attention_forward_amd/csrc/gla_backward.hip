@@ -65,6 +65,9 @@ struct BwdCfg {
   static constexpr int K_SR = D * PITCH;
   static constexpr int K_ZF = 2 * D * PITCH;
   static constexpr int K_BYTES = K_ZF + 4 * D;
+  // key kernel whole-row k and v (D = 128): a 16-token tile of each per wave
+  static constexpr int K_TILE = 16 * 2 * D;
+  static constexpr int K_TILES = kKeyWaves * 2 * K_TILE;
   static_assert(Q_AT % 16 == 0 && Q_RQ % 16 == 0 && K_ZF % 16 == 0, "16-byte aligned sections");
   static_assert(kQueryWaves * D * 4 <= 16 * kQueryWaves * TP, "dz scratch fits the a tile");
 };
@@ -169,8 +172,9 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
   const int c = blockIdx.y;
-  int n_begin, n_end;
-  range_of(a, c, n_begin, n_end);
+  // strided walk: ranges of 16 NW tokens c, c + nsub, ...
+  const int nsub = gridDim.y;
+  const int n_begin = 16 * NW * c, n_end = a.N, wstride = 16 * NW * nsub;
 
   TabView tv{};
   {
@@ -182,7 +186,17 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
     st_z.load(sl);
     st_r.load(a.sl2 + (size_t)bh * D * D);
     const float zv = tid < D ? bw.z[(size_t)bh * D + tid] : 0.f;
-    if (ROPE) tv = stage_table<D, NT>(a, ltab, TLDS, n_begin, n_end);
+    if (ROPE) {
+      if (TLDS) {
+        copy_to_lds<NT>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        tv.tab = ltab;
+      } else {
+        tv.tab = a.cs;
+      }
+      tv.tbase = 0;
+      tv.ntr = a.T;
+      tv.t_last = a.T - 1;
+    }
     st_s.store(sS);
     st_z.store(sS);
     st_r.store(sR);
@@ -252,8 +266,8 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
   issue_gd(base);
   issue_qc(base);
   wait_vmem_all();
-  for (int bs = n_begin; bs < n_end; bs += 16 * NW, base += 16 * NW) {
-    const int next = base + 16 * NW;
+  for (int bs = n_begin; bs < n_end; bs += wstride, base += wstride) {
+    const int next = base + wstride;
     __builtin_amdgcn_sched_barrier(0);
     RowOff rof{};
     if (ROPE) {
@@ -429,20 +443,26 @@ void bwd_key_kernel(KArgs a, BArgs bw) {
   constexpr int NW = kKeyWaves, NT = 64 * NW;
   using OChunk = typename Chunk<OB>::T;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // KROWS: k and v are loaded as whole token rows only (four rows per load
+  // instruction) and turned into the A-operand layout through a per-wave LDS
+  // tile, so k is read once and no load covers partial rows
+  constexpr bool KROWS = D == 128;
   unsigned char* sD = smem;
   unsigned char* sR = smem + Cf::K_SR;
   float* zf = reinterpret_cast<float*>(smem + Cf::K_ZF);
-  float2* ltab = reinterpret_cast<float2*>(smem + Cf::K_BYTES);
+  float2* ltab = reinterpret_cast<float2*>(smem + Cf::K_BYTES + (KROWS ? Cf::K_TILES : 0));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int m = lane >> 4;
   const int col = lane & 15;
+  unsigned char* myk = smem + Cf::K_BYTES + wave * 2 * Cf::K_TILE;  // KROWS: the wave's tiles
+  unsigned char* myv = myk + Cf::K_TILE;
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  int n_begin, n_end;
-  range_of(a, blockIdx.y, n_begin, n_end);
+  const int nsub = gridDim.y;
+  const int n_begin = 16 * NW * blockIdx.y, n_end = a.N, wstride = 16 * NW * nsub;
 
   TabView tv{};
   {
@@ -451,7 +471,17 @@ void bwd_key_kernel(KArgs a, BArgs bw) {
     st_d.load(a.sl + (size_t)bh * (D + 2) * D);
     st_r.load(a.sl2 + (size_t)bh * D * D);
     const float zv = tid < D ? bw.dz[(size_t)bh * D + tid] : 0.f;
-    if (ROPE) tv = stage_table<D, NT>(a, ltab, TLDS, n_begin, n_end);
+    if (ROPE) {
+      if (TLDS) {
+        copy_to_lds<NT>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        tv.tab = ltab;
+      } else {
+        tv.tab = a.cs;
+      }
+      tv.tbase = 0;
+      tv.ntr = a.T;
+      tv.t_last = a.T - 1;
+    }
     st_d.store(sD);
     st_r.store(sR);
     if (tid < D) zf[tid] = zv;
@@ -480,6 +510,91 @@ void bwd_key_kernel(KArgs a, BArgs bw) {
     return (n < n_end) ? (uint32_t)n * tokstride + roff : kOob;
   };
 
+  if constexpr (KROWS) {
+    OChunk kc[4], vc[4];
+    auto issue_rows = [&](int base) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t o = r_offset(base, i);
+        kc[i] = load_chunk<OB>(rk, o);
+        vc[i] = load_chunk<OB>(rv, o);
+      }
+    };
+    int base = n_begin + 16 * wave;
+    issue_rows(base);
+    wait_vmem_all();
+    for (; base < n_end; base += wstride) {
+      const int next = base + wstride;
+      __builtin_amdgcn_sched_barrier(0);
+      // rows 4 m + i into the wave's tiles, then token col's operand chunks
+      // back (the wave's LDS accesses execute in order)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<OChunk*>(myk + row_tile_offset<D>(4 * m + i, OB * col)) = kc[i];
+        *reinterpret_cast<OChunk*>(myv + row_tile_offset<D>(4 * m + i, OB * col)) = vc[i];
+      }
+      u32x4 kv[KS], vv[KS];
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+        kv[s2] = *reinterpret_cast<const u32x4*>(myk + row_tile_offset<D>(col, 16 * (4 * s2 + m)));
+        vv[s2] = *reinterpret_cast<const u32x4*>(myv + row_tile_offset<D>(col, 16 * (4 * s2 + m)));
+      }
+      issue_rows(next);
+      __builtin_amdgcn_sched_barrier(0);
+      RowOff rof{};
+      if (ROPE) {
+        int t, y, x;
+        grid_pos(a, (uint32_t)min(base + col, n_end - 1), t, y, x);
+        rof = row_offsets<D>(a, tv, t, y, x);
+      }
+      bf16x8 Ak[KS];
+      static_for<KS>([&](auto S2) {
+        constexpr int s2 = decltype(S2)::value;
+        u32x4 fk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) fk[u] = relu2(kv[s2][u]);
+        Ak[s2] = __builtin_bit_cast(bf16x8, ROPE ? rope_chunk<D, s2>(fk, tv, rof, m) : fk);
+      });
+      f32x4 acc[MB];
+      contract_rows<D>(sD, Ak, col, m, acc);
+      bf16x8 Av[KS];
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) Av[s2] = __builtin_bit_cast(bf16x8, vv[s2]);
+      f32x4 acc2[MB];
+      contract_rows<D>(sR, Av, col, m, acc2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        OChunk wv;
+#pragma unroll
+        for (int w = 0; w < OB / 4; ++w) wv[w] = pack_bf16(acc[2 * w][i], acc[2 * w + 1][i]);
+        store_chunk_nt<OB>(rdv, r_offset(base, i), wv);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // the row chunk of k again, from the tile, for the k > 0 mask
+        const OChunk kr = *reinterpret_cast<const OChunk*>(myk + row_tile_offset<D>(4 * m + i, OB * col));
+        float2 cs[PU];
+        if (ROPE) acc_factors<D>(a, tv, min(base + 4 * m + i, n_end - 1), col, cs);
+        OChunk wk;
+#pragma unroll
+        for (int u = 0; u < PU; ++u) {
+          const float x = acc2[2 * u][i], y = acc2[2 * u + 1][i];
+          float xr = x, yr = y;
+          if (ROPE) {
+            xr = x * cs[u].x + y * cs[u].y;
+            yr = y * cs[u].x - x * cs[u].y;
+          }
+          const float k0 = bf_lo(kr[u]), k1 = bf_hi(kr[u]);
+          const float g0 = k0 > 0.f ? xr + zl[2 * u] : 0.f;
+          const float g1 = k1 > 0.f ? yr + zl[2 * u + 1] : 0.f;
+          wk[u] = pack_bf16(g0, g1);
+        }
+        store_chunk_nt<OB>(rdk, r_offset(base, i), wk);
+      }
+    }
+    return;
+  } else {
   u32x4 kv[KS], vv[KS];
   OChunk kc[4];
   auto issue_k = [&](int base) {
@@ -502,8 +617,8 @@ void bwd_key_kernel(KArgs a, BArgs bw) {
   issue_v(base);
   issue_kc(base);
   wait_vmem_all();
-  for (; base < n_end; base += 16 * NW) {
-    const int next = base + 16 * NW;
+  for (; base < n_end; base += wstride) {
+    const int next = base + wstride;
     __builtin_amdgcn_sched_barrier(0);
     RowOff rof{};
     if (ROPE) {
@@ -561,6 +676,7 @@ void bwd_key_kernel(KArgs a, BArgs bw) {
     }
     issue_kc(next);
   }
+  }
 }
 
 template <auto K>
@@ -576,9 +692,9 @@ template <int D>
 hipError_t launch_bwd_query_d(const Plan& p, const KArgs& a, const BArgs& b, hipStream_t s) {
   // the table goes to LDS when it fits beside the operands and the two tiles
   // (160 KB per compute unit); otherwise the kernel reads it from memory
-  const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes &&
-                  BwdCfg<D>::Q_BYTES + table_lds_bytes(a) <= 160 * 1024;
-  const size_t lds = BwdCfg<D>::Q_BYTES + (tl ? table_lds_bytes(a) : 0);
+  const size_t tbw = 8 * ((size_t)a.T * a.Pt + (size_t)a.Hh * a.Py + (size_t)a.W * a.Px);
+  const bool tl = a.cs && BwdCfg<D>::Q_BYTES + tbw <= 160 * 1024;
+  const size_t lds = BwdCfg<D>::Q_BYTES + (tl ? tbw : 0);
   constexpr int T = 64 * kQueryWaves;
   if (!a.cs) return launch_rows_kernel<bwd_query_kernel<D, false, false>>(p, a, b, T, lds, s);
   if (tl) return launch_rows_kernel<bwd_query_kernel<D, true, true>>(p, a, b, T, lds, s);
@@ -587,8 +703,10 @@ hipError_t launch_bwd_query_d(const Plan& p, const KArgs& a, const BArgs& b, hip
 
 template <int D>
 hipError_t launch_bwd_key_d(const Plan& p, const KArgs& a, const BArgs& b, hipStream_t s) {
-  const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;
-  const size_t lds = BwdCfg<D>::K_BYTES + (tl ? table_lds_bytes(a) : 0);
+  const size_t tbw = 8 * ((size_t)a.T * a.Pt + (size_t)a.Hh * a.Py + (size_t)a.W * a.Px);
+  const size_t fixed = BwdCfg<D>::K_BYTES + (D == 128 ? BwdCfg<D>::K_TILES : 0);
+  const bool tl = a.cs && fixed + tbw <= 160 * 1024;
+  const size_t lds = fixed + (tl ? tbw : 0);
   constexpr int T = 64 * kKeyWaves;
   if (!a.cs) return launch_rows_kernel<bwd_key_kernel<D, false, false>>(p, a, b, T, lds, s);
   if (tl) return launch_rows_kernel<bwd_key_kernel<D, true, true>>(p, a, b, T, lds, s);
