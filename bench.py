@@ -161,9 +161,7 @@ def block_bench(args, w, gla, dev, tensors, out, rope, stream):
 
     log(f"bench: block-causal, {args.block_frames} frames ({L} tokens) per block; "
         f"warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     log(f"bench: timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -209,6 +207,21 @@ def block_bench(args, w, gla, dev, tensors, out, rope, stream):
 PEAK_BF16_TFLOPS = 2500.0
 EVICT_BYTES = 512 << 20   # twice the MI355X's 256 MB last-level cache (MALL)
 ROTATE = 3                # input sets the HBM-bound benches cycle through
+
+
+def warm_up(step, warmup, min_seconds=0.3):
+    """`warmup` untimed steps, then more until about `min_seconds` have
+    passed: the first passes over freshly allocated inputs, and an idle
+    GPU's first milliseconds, run slower than the steady state."""
+    import torch
+    i = 0
+    t_end = time.perf_counter() + min_seconds
+    while i < warmup or time.perf_counter() < t_end:
+        step(i)
+        i += 1
+        if i % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def input_sets(tensors, n=ROTATE):
@@ -267,9 +280,7 @@ def softmax_bench(args, w, gla, dev, tensors, rope, stream):
         gla.gla_softmax_forward_ws(qd, kd, vd, gd, rope, ws, out, stream)
 
     log(f"bench: softmax anchor attention; warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(lambda i: step(), args.warmup)
     log(f"bench: timing {args.steps} steps")
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -365,9 +376,7 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
         gla.gla_backward_ws(qs, ks, vs, gs, ds, rope, ws, *grads, stream=stream)
 
     log(f"bench: backward; warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     log(f"bench: timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -420,9 +429,7 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
         gla.gla_backward_saved_ws(qs, ks, vs, gs, ds, S, z, rope, ws, *grads, stream=stream)
 
     log(f"bench: backward with the saved state; {args.warmup} + {args.steps} steps")
-    for i in range(args.warmup):
-        step_saved(i)
-    torch.cuda.synchronize()
+    warm_up(step_saved, args.warmup)
     for i, e in enumerate(evs):
         e[0].record(stream)
         step_saved(i)
@@ -493,9 +500,7 @@ def proj_bench(args, w, gla, dev):
         gla.gla_forward_proj_ws(xd, wd, w.H, w.D, rope, ws, out, stream)
 
     log(f"bench: warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(lambda i: step(), args.warmup)
     log(f"bench: timing {args.steps} steps")
     t0 = time.perf_counter()
     for _ in range(args.steps):
