@@ -1497,7 +1497,10 @@ constexpr size_t persist_fixed_lds() {
 template <int D, int G, bool QR>
 hipError_t launch_output_persist(const Plan& p, KArgs a, hipStream_t stream) {
   const int groups = p.BH / G;
-  const int nsub = kPersistBlocks / groups > 0 ? kPersistBlocks / groups : 1;
+  // about kPersistBlocks blocks, but no more per group than it has ranges
+  const int ranges = (p.N + 64 / G - 1) / (64 / G);
+  int nsub = kPersistBlocks / groups > 0 ? kPersistBlocks / groups : 1;
+  if (nsub > ranges) nsub = ranges;
   const size_t pairs = persist_table_pairs(a);
   const size_t fixed = persist_fixed_lds<D, G, QR>();
   const bool t32 = a.cs && 8 * pairs <= kMaxPersistTableBytes && fixed + 8 * pairs <= kMaxLdsPerBlock;
