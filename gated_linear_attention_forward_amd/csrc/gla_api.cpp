@@ -471,6 +471,19 @@ int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
                               (size_t)B * N * H * D * 2)))
     return rc;
   if ((rc = rope_device_ok(rope))) return rc;
+  if (gla::output_sums_partials(p)) {
+    // small partials: the output kernel sums them (two launches, not three)
+    gla::KArgs as = kernel_args(p, rope, p.L, p.CB, workspace);
+    as.k = static_cast<const uint16_t*>(k);
+    as.v = static_cast<const uint16_t*>(v);
+    if ((rc = status_of(gla::launch_state(p, as, static_cast<hipStream_t>(stream), false))))
+      return rc;
+    gla::KArgs ao = kernel_args(p, rope, p.L2, p.SUB, workspace);
+    ao.q = static_cast<const uint16_t*>(q);
+    ao.g = static_cast<const uint16_t*>(g);
+    ao.out = static_cast<uint16_t*>(out);
+    return status_of(gla::launch_output(p, ao, static_cast<hipStream_t>(stream), true));
+  }
   rc = run_state(p, k, v, rope, workspace, nullptr, nullptr, nullptr, nullptr, stream);
   if (rc) return rc;
   return run_output(p, q, g, rope, out, workspace, stream);

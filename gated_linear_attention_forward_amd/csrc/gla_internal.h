@@ -90,6 +90,11 @@ constexpr size_t kMaxPersistTableBytes = 56 * 1024;
 // Steps per wave below which the persistent output kernel keeps one head
 // per block (staging several heads' operands would not pay).
 constexpr int kGroupMinSteps = 16;
+// Limits for folding the reduction into the output kernel: partial bytes
+// one block reads, and all blocks together.
+constexpr size_t kFoldBlockBytes = 64 * 1024;
+constexpr size_t kFoldTotalBytes = 4 << 20;
+constexpr int kFoldMaxChunks = 16;
 // LDS a block may ask for on gfx950 (160 KB per compute unit).
 constexpr size_t kMaxLdsPerBlock = 160 * 1024;
 // The backward pass's query and key kernels (8 waves, one block per compute
@@ -112,10 +117,18 @@ constexpr size_t kScratchBytes = (size_t)32 << 20;
 hipError_t scratch_pointer(void** out);
 
 // Kernel launchers (gla_kernels.hip).  Return the hipError_t of the launch.
-hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream);
+// State kernel, then (unless `reduce` is false) the cross-chunk reduction.
+hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream, bool reduce = true);
 // The scan alone over zero blocks: S_out/z_out = S_in/z_in (or zero).
 hipError_t launch_carry(const Plan& p, KArgs a, hipStream_t stream);
-hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream);
+// Output kernel.  With `sum_partials` its blocks sum the chunk partials
+// (a.part) themselves, in place of reading the reduced operand (a.sl).
+hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream, bool sum_partials = false);
+// True when a bidirectional pass of this plan runs with the reduction folded
+// into the output kernel's prologue: the chunk partials are small (D <= 64,
+// a few KB per head and block), so re-reading them in every output block
+// costs less than a launch of the reduce kernel.
+bool output_sums_partials(const Plan& p);
 // Gated softmax anchor attention (gla_softmax.hip): prep (rotated, scaled q
 // into qr, rotated k into kr, [B, N, H, D] bf16 each) then the flash kernel.
 // Reads a.q, a.k, a.v, a.g, a.cs (nullptr: RoPE off), writes a.out.

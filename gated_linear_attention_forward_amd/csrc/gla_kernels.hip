@@ -1166,7 +1166,7 @@ void state_tile_kernel(KArgs a) {
 // rows at any time, which measured faster than both the per-range blocks of
 // output_kernel (that restage S for every range) and long contiguous ranges
 // per block.  A step is output_kernel's step (same arithmetic, same result).
-template <int D, bool ROPE, bool TLDS, int G, bool T16, bool QROWS>
+template <int D, bool ROPE, bool TLDS, int G, bool T16, bool QROWS, bool SUMP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void output_persist_kernel(KArgs a, int nsub) {
   // QROWS: whole-row q loads (four rows of 16 chunks) through a per-wave LDS
@@ -1182,6 +1182,7 @@ void output_persist_kernel(KArgs a, int nsub) {
   constexpr int RANGE = 64 / G;      // tokens of a head per block and step
   static_assert(G == 1 || ((G == 2 || G == 4) && D == 128), "heads per block");
   static_assert(!T16 || (TLDS && G > 1), "fp16 pairs only in a grouped block's LDS table");
+  static_assert(!SUMP || (G == 1 && !QROWS), "partials are summed by one-head blocks (D <= 64)");
   using OChunk = typename Chunk<OB>::T;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x;
@@ -1356,6 +1357,49 @@ void output_persist_kernel(KArgs a, int nsub) {
       tv.ntr = a.T;
       tv.t_last = a.T - 1;
     }
+  } else if constexpr (SUMP) {
+    // the reduction folded in: S and z are the sums of the head's C <= 16
+    // chunk partials in the reduce kernel's pairwise tree (so the same
+    // values), written straight into the operand layout (row out_row_of(e)
+    // holds column e of S; rows D and D + 1 the hi and lo halves of z)
+    const float* pp = a.part + (size_t)bh * a.C * (D * D + D);
+    constexpr int GR = (D * D + D) / 4;  // groups of four floats
+    for (int gi = tid; gi < GR; gi += 256) {
+      f32x4 x[kFoldMaxChunks];
+#pragma unroll
+      for (int c = 0; c < kFoldMaxChunks; ++c)
+        x[c] = c < a.C ? *reinterpret_cast<const f32x4*>(pp + (size_t)c * (D * D + D) + 4 * gi)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 acc = sum_chunks<kFoldMaxChunks>(x);
+      if (gi < D * D / 4) {
+        const int d = gi / (D / 4), e0 = 4 * (gi % (D / 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint16_t*>(sS + row_tile_offset<D>(out_row_of<D>(e0 + j), 2 * d)) =
+              (uint16_t)(pack_bf16(acc[j], 0.f) & 0xffffu);
+      } else {
+        const int z0 = 4 * (gi - D * D / 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t hl = pack_bf16(acc[j], 0.f) & 0xffffu;
+          const float hi = __uint_as_float(hl << 16);
+          *reinterpret_cast<uint16_t*>(sS + row_tile_offset<D>(D, 2 * (z0 + j))) = (uint16_t)hl;
+          *reinterpret_cast<uint16_t*>(sS + row_tile_offset<D>(D + 1, 2 * (z0 + j))) =
+              (uint16_t)(pack_bf16(acc[j] - hi, 0.f) & 0xffffu);
+        }
+      }
+    }
+    if (ROPE) {
+      if (TLDS) {
+        copy_to_lds<256>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        tv.tab = ltab;
+      } else {
+        tv.tab = a.cs;
+      }
+      tv.tbase = 0;
+      tv.ntr = a.T;
+      tv.t_last = a.T - 1;
+    }
   } else {
     RowStage<D, D, 256> st_s;
     RowStage<D, 2, 256, D> st_z;
@@ -1458,7 +1502,7 @@ hipError_t launch_state_k(const Plan& p, const KArgs& a, size_t lds, hipStream_t
 }
 
 template <int D>
-hipError_t launch_state_d(const Plan& p, KArgs a, hipStream_t stream) {
+hipError_t launch_state_d(const Plan& p, KArgs a, hipStream_t stream, bool reduce) {
   const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;
   const size_t lds = state_lds_bytes<D>() + (tl ? table_lds_bytes(a) : 0);
   hipError_t e0;
@@ -1470,7 +1514,7 @@ hipError_t launch_state_d(const Plan& p, KArgs a, hipStream_t stream) {
     e0 = launch_state_k<D, true, false>(p, a, lds, stream);
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !reduce) return e;
   return launch_reduce_d<D>(p, a, stream);
 }
 
@@ -1494,13 +1538,19 @@ constexpr size_t persist_fixed_lds() {
 // blocks, one per compute unit (the LDS request keeps a second block off).
 // The RoPE table goes into LDS as fp32 pairs when it fits, else (grouped
 // blocks only) as fp16 pairs, else it is read from global memory.
-template <int D, int G, bool QR>
+// Blocks per head group of the persistent output launch: about
+// kPersistBlocks in all, but no more per group than it has ranges.
+int persist_nsub(const Plan& p, int G) {
+  const int groups = p.BH / G;
+  const int ranges = (p.N + 64 / G - 1) / (64 / G);
+  const int nsub = kPersistBlocks / groups > 0 ? kPersistBlocks / groups : 1;
+  return nsub < ranges ? nsub : ranges;
+}
+
+template <int D, int G, bool QR, bool SUMP = false>
 hipError_t launch_output_persist(const Plan& p, KArgs a, hipStream_t stream) {
   const int groups = p.BH / G;
-  // about kPersistBlocks blocks, but no more per group than it has ranges
-  const int ranges = (p.N + 64 / G - 1) / (64 / G);
-  int nsub = kPersistBlocks / groups > 0 ? kPersistBlocks / groups : 1;
-  if (nsub > ranges) nsub = ranges;
+  const int nsub = persist_nsub(p, G);
   const size_t pairs = persist_table_pairs(a);
   const size_t fixed = persist_fixed_lds<D, G, QR>();
   const bool t32 = a.cs && 8 * pairs <= kMaxPersistTableBytes && fixed + 8 * pairs <= kMaxLdsPerBlock;
@@ -1514,16 +1564,19 @@ hipError_t launch_output_persist(const Plan& p, KArgs a, hipStream_t stream) {
     hipLaunchKernelGGL(decltype(kern)::value, g, dim3(256), lds, stream, a, nsub);
     return hipGetLastError();
   };
-  if (!a.cs) return go(KernelTag<output_persist_kernel<D, false, false, G, false, QR>>{});
-  if (t32) return go(KernelTag<output_persist_kernel<D, true, true, G, false, QR>>{});
+  if (!a.cs) return go(KernelTag<output_persist_kernel<D, false, false, G, false, QR, SUMP>>{});
+  if (t32) return go(KernelTag<output_persist_kernel<D, true, true, G, false, QR, SUMP>>{});
   if constexpr (G > 1) {
     if (t16) return go(KernelTag<output_persist_kernel<D, true, true, G, true, QR>>{});
   }
-  return go(KernelTag<output_persist_kernel<D, true, false, G, false, QR>>{});
+  return go(KernelTag<output_persist_kernel<D, true, false, G, false, QR, SUMP>>{});
 }
 
 template <int D>
-hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream) {
+hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream, bool sum_partials) {
+  if constexpr (D <= 64) {
+    if (sum_partials) return launch_output_persist<D, 1, false, true>(p, a, stream);
+  }
   if (p.NB == 1) {
     if constexpr (D == 128) {
       // as many heads per block (4, then 2) as divide H with the table in LDS
@@ -1596,13 +1649,21 @@ hipError_t scratch_pointer(void** out) {
   return hipSuccess;
 }
 
-hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream) {
+hipError_t launch_state(const Plan& p, KArgs a, hipStream_t stream, bool reduce) {
   switch (p.D) {
-    case 32: return launch_state_d<32>(p, a, stream);
-    case 64: return launch_state_d<64>(p, a, stream);
-    case 128: return launch_state_d<128>(p, a, stream);
+    case 32: return launch_state_d<32>(p, a, stream, reduce);
+    case 64: return launch_state_d<64>(p, a, stream, reduce);
+    case 128: return launch_state_d<128>(p, a, stream, reduce);
     default: return hipErrorInvalidValue;
   }
+}
+
+bool output_sums_partials(const Plan& p) {
+  if (p.NB != 1 || p.D > 64 || p.BH == 0 || p.N == 0) return false;
+  const size_t per_block = (size_t)p.C * (size_t)(p.D * p.D + p.D) * sizeof(float);
+  const size_t blocks = (size_t)p.BH * (size_t)persist_nsub(p, 1);
+  return p.C <= kFoldMaxChunks && per_block <= kFoldBlockBytes &&
+         per_block * blocks <= kFoldTotalBytes;
 }
 
 hipError_t launch_reduce_state(const Plan& p, KArgs a, hipStream_t stream) {
@@ -1625,11 +1686,11 @@ hipError_t launch_carry(const Plan& p, KArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream) {
+hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream, bool sum_partials) {
   switch (p.D) {
-    case 32: return launch_output_d<32>(p, a, stream);
-    case 64: return launch_output_d<64>(p, a, stream);
-    case 128: return launch_output_d<128>(p, a, stream);
+    case 32: return launch_output_d<32>(p, a, stream, sum_partials);
+    case 64: return launch_output_d<64>(p, a, stream, sum_partials);
+    case 128: return launch_output_d<128>(p, a, stream, sum_partials);
     default: return hipErrorInvalidValue;
   }
 }

@@ -295,6 +295,31 @@ def test_bitwise_deterministic_and_entry_points_agree():
     assert torch.equal(o1.view(torch.int16), o4.view(torch.int16))
 
 
+@pytest.mark.parametrize("B,H,D,grid", [(1, 2, 32, (4, 8, 8)), (3, 1, 32, (5, 7, 11)),
+                                        (2, 3, 64, (3, 5, 7)), (1, 2, 32, (10, 12, 16))])
+@pytest.mark.parametrize("rope", [True, False])
+def test_folded_reduction_matches_the_reduce_kernel(B, H, D, grid, rope):
+    """Small shapes run the whole pass as two launches, the output kernel
+    summing the chunk partials itself; the two halves called separately run
+    the reduce kernel in between.  Both sum in the same pairwise order, so
+    the outputs are bitwise equal (the 10x12x16 grid takes 15 chunks)."""
+    T, Hh, W = grid
+    N = T * Hh * W
+    say(f"case folded reduction B={B} H={H} D={D} grid={grid} rope={rope}")
+    q, k, v, g = to_dev(*random_inputs(B, N, H, D, seed=91))
+    r = gla.gla_rope_create(T, Hh, W, D) if rope else None
+    ws = gla.alloc_workspace(B, N, H, D, DEV)
+    o1 = torch.empty_like(q)
+    gla.gla_forward_ws(q, k, v, g, r, o1, ws)
+    o2 = torch.empty_like(q)
+    gla.gla_state_ws(k, v, r, ws)
+    gla.gla_output_ws(q, g, r, o2, ws)
+    torch.cuda.synchronize()
+    if r is not None:
+        r.close()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 def test_relative_position_shift():
     """Tables built with shifted grid indices give the same output (RoPE is relative)."""
     B, H, D, grid = 1, 2, 128, (3, 6, 9)
