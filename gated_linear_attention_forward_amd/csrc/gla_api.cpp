@@ -471,6 +471,16 @@ int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
                               (size_t)B * N * H * D * 2)))
     return rc;
   if ((rc = rope_device_ok(rope))) return rc;
+  if (gla::pass_in_block(p)) {
+    // short sequence: one launch, one block per head (state, then outputs)
+    gla::KArgs a1 = kernel_args(p, rope, p.N, 1, workspace);
+    a1.q = static_cast<const uint16_t*>(q);
+    a1.k = static_cast<const uint16_t*>(k);
+    a1.v = static_cast<const uint16_t*>(v);
+    a1.g = static_cast<const uint16_t*>(g);
+    a1.out = static_cast<uint16_t*>(out);
+    return status_of(gla::launch_pass_in_block(p, a1, static_cast<hipStream_t>(stream)));
+  }
   if (gla::output_sums_partials(p)) {
     // small partials: the output kernel sums them (two launches, not three)
     gla::KArgs as = kernel_args(p, rope, p.L, p.CB, workspace);

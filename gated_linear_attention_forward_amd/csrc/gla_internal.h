@@ -95,6 +95,8 @@ constexpr int kGroupMinSteps = 16;
 constexpr size_t kFoldBlockBytes = 64 * 1024;
 constexpr size_t kFoldTotalBytes = 4 << 20;
 constexpr int kFoldMaxChunks = 16;
+// Largest N * D a one-launch pass takes (one block streams a head's tokens).
+constexpr long long kInBlockMaxND = 32768;
 // LDS a block may ask for on gfx950 (160 KB per compute unit).
 constexpr size_t kMaxLdsPerBlock = 160 * 1024;
 // The backward pass's query and key kernels (8 waves, one block per compute
@@ -129,6 +131,12 @@ hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream, bool sum_pa
 // a few KB per head and block), so re-reading them in every output block
 // costs less than a launch of the reduce kernel.
 bool output_sums_partials(const Plan& p);
+// True when a bidirectional pass of this plan runs as one launch: one block
+// per head forms the head's state from all N tokens and then its outputs
+// (short sequences at D <= 64, where launches, not bytes, set the time).
+bool pass_in_block(const Plan& p);
+// That launch: reads a.q, a.k, a.v, a.g and a.cs, writes a.out (no workspace).
+hipError_t launch_pass_in_block(const Plan& p, KArgs a, hipStream_t stream);
 // Gated softmax anchor attention (gla_softmax.hip): prep (rotated, scaled q
 // into qr, rotated k into kr, [B, N, H, D] bf16 each) then the flash kernel.
 // Reads a.q, a.k, a.v, a.g, a.cs (nullptr: RoPE off), writes a.out.

@@ -1166,7 +1166,12 @@ void state_tile_kernel(KArgs a) {
 // rows at any time, which measured faster than both the per-range blocks of
 // output_kernel (that restage S for every range) and long contiguous ranges
 // per block.  A step is output_kernel's step (same arithmetic, same result).
-template <int D, bool ROPE, bool TLDS, int G, bool T16, bool QROWS, bool SUMP = false>
+// Where a block's state operand comes from (the SRC template argument).
+constexpr int kSrcReduced = 0;   // the reduce kernel's operand rows (a.sl)
+constexpr int kSrcPartials = 1;  // the head's chunk partials, summed here
+constexpr int kSrcInBlock = 2;   // the head's state, formed here from all N tokens
+
+template <int D, bool ROPE, bool TLDS, int G, bool T16, bool QROWS, int SRC = kSrcReduced>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void output_persist_kernel(KArgs a, int nsub) {
   // QROWS: whole-row q loads (four rows of 16 chunks) through a per-wave LDS
@@ -1182,7 +1187,8 @@ void output_persist_kernel(KArgs a, int nsub) {
   constexpr int RANGE = 64 / G;      // tokens of a head per block and step
   static_assert(G == 1 || ((G == 2 || G == 4) && D == 128), "heads per block");
   static_assert(!T16 || (TLDS && G > 1), "fp16 pairs only in a grouped block's LDS table");
-  static_assert(!SUMP || (G == 1 && !QROWS), "partials are summed by one-head blocks (D <= 64)");
+  static_assert(SRC == kSrcReduced || (G == 1 && !QROWS && D <= 64),
+                "partials or the state are summed by one-head blocks (D <= 64)");
   using OChunk = typename Chunk<OB>::T;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x;
@@ -1192,7 +1198,10 @@ void output_persist_kernel(KArgs a, int nsub) {
   const int col = lane & 15;
   unsigned char* sS = smem + (wave % G) * OPB;
   unsigned char* myq = smem + G * OPB + wave * QT;
-  float2* ltab = reinterpret_cast<float2*>(smem + G * OPB + (QROWS ? 4 * QT : 0));
+  // kSrcInBlock: the state kernel's tiles and reduction scratch follow the
+  // operand
+  constexpr int SCR = SRC == kSrcInBlock ? StateCfg<D>::LDS_BYTES : 0;
+  float2* ltab = reinterpret_cast<float2*>(smem + G * OPB + (QROWS ? 4 * QT : 0) + SCR);
   // head groups vary fastest over the grid; wave w takes head G g + w % G of
   // the group's batch element, and tokens 16 (w / G) .. of each range
   const int hgs = a.H / G;
@@ -1357,7 +1366,93 @@ void output_persist_kernel(KArgs a, int nsub) {
       tv.ntr = a.T;
       tv.t_last = a.T - 1;
     }
-  } else if constexpr (SUMP) {
+  } else if constexpr (SRC == kSrcInBlock) {
+    // the whole pass in one block per head: the table, then the state over
+    // all N tokens (the state kernel's waves, one 16-token tile each in turn),
+    // the four waves' sums added in wave order through LDS and written into
+    // the operand layout
+    using Cf = StateCfg<D>;
+    constexpr int KS2 = Cf::KS;
+    unsigned char* scr = smem + OPB;
+    if (ROPE) {
+      if (TLDS) {
+        copy_to_lds<256>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        tv.tab = ltab;
+      } else {
+        tv.tab = a.cs;
+      }
+      tv.tbase = 0;
+      tv.ntr = a.T;
+      tv.t_last = a.T - 1;
+    }
+    __syncthreads();
+    const int ntile = (N + Cf::TW - 1) / Cf::TW;
+    StateWave<D, ROPE> sw{a,
+                          tv,
+                          make_rsrc(a.k + boff, a.slab_bytes),
+                          make_rsrc(a.v + boff, a.slab_bytes),
+                          tokstride,
+                          (uint32_t)h * D * 2 + 16u * m,
+                          0,
+                          N,
+                          wave,
+                          (ntile - wave + 3) / 4,
+                          lane,
+                          m,
+                          col,
+                          scr + wave * Cf::WAVE_BYTES};
+    sw.run();
+#pragma unroll
+    for (int msk = 1; msk < 16; msk *= 2)
+#pragma unroll
+      for (int s2 = 0; s2 < KS2; ++s2)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sw.zacc[s2][j] += __shfl_xor(sw.zacc[s2][j], msk);
+    __syncthreads();  // every wave is done with its tiles; they become scratch
+    float* red = reinterpret_cast<float*>(scr);
+    float* zw = reinterpret_cast<float*>(scr + Cf::ZW_OFF);
+    if (col == 0) {
+#pragma unroll
+      for (int s2 = 0; s2 < KS2; ++s2)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) zw[wave * D + 8 * (4 * s2 + m) + j] = sw.zacc[s2][j];
+    }
+    __syncthreads();
+    if (tid < D) {
+      const float zs = ((zw[tid] + zw[D + tid]) + zw[2 * D + tid]) + zw[3 * D + tid];
+      const uint32_t hl = pack_bf16(zs, 0.f) & 0xffffu;
+      *reinterpret_cast<uint16_t*>(sS + row_tile_offset<D>(D, 2 * tid)) = (uint16_t)hl;
+      *reinterpret_cast<uint16_t*>(sS + row_tile_offset<D>(D + 1, 2 * tid)) =
+          (uint16_t)(pack_bf16(zs - __uint_as_float(hl << 16), 0.f) & 0xffffu);
+    }
+    constexpr int NTI = Cf::RT * Cf::RT;
+    constexpr int WSTRIDE = Cf::RED_TILES * 1024;
+#pragma unroll
+    for (int t0 = 0; t0 < NTI; t0 += Cf::RED_TILES) {
+      __syncthreads();  // the previous round's reads (and the z reads) are done
+#pragma unroll
+      for (int qq = 0; qq < Cf::RED_TILES; ++qq) {
+        if (t0 + qq < NTI) {
+          const int ti = (t0 + qq) / Cf::RT, tj = (t0 + qq) % Cf::RT;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[wave * WSTRIDE + (qq * 16 + r) * 64 + lane] = sw.acc[ti][tj][r];
+        }
+      }
+      __syncthreads();
+      for (int idx = tid; idx < WSTRIDE; idx += 256) {
+        const int qq = idx / 1024, r = (idx / 64) % 16, l = idx % 64;
+        if (t0 + qq < NTI) {
+          const int ti = (t0 + qq) / Cf::RT, tj = (t0 + qq) % Cf::RT;
+          const float sum = ((red[idx] + red[WSTRIDE + idx]) + red[2 * WSTRIDE + idx]) +
+                            red[3 * WSTRIDE + idx];
+          const int d = 32 * ti + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+          const int e = 32 * tj + (l & 31);
+          *reinterpret_cast<uint16_t*>(sS + row_tile_offset<D>(out_row_of<D>(e), 2 * d)) =
+              (uint16_t)(pack_bf16(sum, 0.f) & 0xffffu);
+        }
+      }
+    }
+  } else if constexpr (SRC == kSrcPartials) {
     // the reduction folded in: S and z are the sums of the head's C <= 16
     // chunk partials in the reduce kernel's pairwise tree (so the same
     // values), written straight into the operand layout (row out_row_of(e)
@@ -1547,12 +1642,14 @@ int persist_nsub(const Plan& p, int G) {
   return nsub < ranges ? nsub : ranges;
 }
 
-template <int D, int G, bool QR, bool SUMP = false>
+template <int D, int G, bool QR, int SRC = kSrcReduced>
 hipError_t launch_output_persist(const Plan& p, KArgs a, hipStream_t stream) {
   const int groups = p.BH / G;
-  const int nsub = persist_nsub(p, G);
+  // kSrcInBlock: one block per head, which forms the state itself
+  const int nsub = SRC == kSrcInBlock ? 1 : persist_nsub(p, G);
   const size_t pairs = persist_table_pairs(a);
-  const size_t fixed = persist_fixed_lds<D, G, QR>();
+  const size_t fixed =
+      persist_fixed_lds<D, G, QR>() + (SRC == kSrcInBlock ? StateCfg<D>::LDS_BYTES : 0);
   const bool t32 = a.cs && 8 * pairs <= kMaxPersistTableBytes && fixed + 8 * pairs <= kMaxLdsPerBlock;
   const bool t16 = G > 1 && a.cs && !t32 && fixed + 4 * pairs <= kMaxLdsPerBlock;
   size_t lds = fixed + (t32 ? 8 * pairs : (t16 ? 4 * pairs : 0));
@@ -1564,18 +1661,19 @@ hipError_t launch_output_persist(const Plan& p, KArgs a, hipStream_t stream) {
     hipLaunchKernelGGL(decltype(kern)::value, g, dim3(256), lds, stream, a, nsub);
     return hipGetLastError();
   };
-  if (!a.cs) return go(KernelTag<output_persist_kernel<D, false, false, G, false, QR, SUMP>>{});
-  if (t32) return go(KernelTag<output_persist_kernel<D, true, true, G, false, QR, SUMP>>{});
+  if (!a.cs) return go(KernelTag<output_persist_kernel<D, false, false, G, false, QR, SRC>>{});
+  if (t32) return go(KernelTag<output_persist_kernel<D, true, true, G, false, QR, SRC>>{});
   if constexpr (G > 1) {
     if (t16) return go(KernelTag<output_persist_kernel<D, true, true, G, true, QR>>{});
   }
-  return go(KernelTag<output_persist_kernel<D, true, false, G, false, QR, SUMP>>{});
+  return go(KernelTag<output_persist_kernel<D, true, false, G, false, QR, SRC>>{});
 }
 
 template <int D>
-hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream, bool sum_partials) {
+hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream, int src) {
   if constexpr (D <= 64) {
-    if (sum_partials) return launch_output_persist<D, 1, false, true>(p, a, stream);
+    if (src == kSrcPartials) return launch_output_persist<D, 1, false, kSrcPartials>(p, a, stream);
+    if (src == kSrcInBlock) return launch_output_persist<D, 1, false, kSrcInBlock>(p, a, stream);
   }
   if (p.NB == 1) {
     if constexpr (D == 128) {
@@ -1687,12 +1785,25 @@ hipError_t launch_carry(const Plan& p, KArgs a, hipStream_t stream) {
 }
 
 hipError_t launch_output(const Plan& p, KArgs a, hipStream_t stream, bool sum_partials) {
+  const int src = sum_partials ? kSrcPartials : kSrcReduced;
   switch (p.D) {
-    case 32: return launch_output_d<32>(p, a, stream, sum_partials);
-    case 64: return launch_output_d<64>(p, a, stream, sum_partials);
-    case 128: return launch_output_d<128>(p, a, stream, sum_partials);
+    case 32: return launch_output_d<32>(p, a, stream, src);
+    case 64: return launch_output_d<64>(p, a, stream, src);
+    case 128: return launch_output_d<128>(p, a, stream, src);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_pass_in_block(const Plan& p, KArgs a, hipStream_t stream) {
+  switch (p.D) {
+    case 32: return launch_output_d<32>(p, a, stream, kSrcInBlock);
+    case 64: return launch_output_d<64>(p, a, stream, kSrcInBlock);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool pass_in_block(const Plan& p) {
+  return p.NB == 1 && p.D <= 64 && p.BH > 0 && (long long)p.N * p.D <= kInBlockMaxND;
 }
 
 }  // namespace gla

@@ -295,14 +295,14 @@ def test_bitwise_deterministic_and_entry_points_agree():
     assert torch.equal(o1.view(torch.int16), o4.view(torch.int16))
 
 
-@pytest.mark.parametrize("B,H,D,grid", [(1, 2, 32, (4, 8, 8)), (3, 1, 32, (5, 7, 11)),
-                                        (2, 3, 64, (3, 5, 7)), (1, 2, 32, (10, 12, 16))])
+@pytest.mark.parametrize("B,H,D,grid", [(1, 2, 32, (10, 12, 16)), (3, 1, 32, (9, 11, 12)),
+                                        (1, 1, 32, (1, 1, 1100))])
 @pytest.mark.parametrize("rope", [True, False])
 def test_folded_reduction_matches_the_reduce_kernel(B, H, D, grid, rope):
-    """Small shapes run the whole pass as two launches, the output kernel
-    summing the chunk partials itself; the two halves called separately run
-    the reduce kernel in between.  Both sum in the same pairwise order, so
-    the outputs are bitwise equal (the 10x12x16 grid takes 15 chunks)."""
+    """D = 32 sequences of 1,100 to 1,920 tokens run the whole pass as two
+    launches, the output kernel summing the 9 to 15 chunk partials itself;
+    the two halves called separately run the reduce kernel in between.  Both
+    sum in the same pairwise order, so the outputs are bitwise equal."""
     T, Hh, W = grid
     N = T * Hh * W
     say(f"case folded reduction B={B} H={H} D={D} grid={grid} rope={rope}")
@@ -318,6 +318,39 @@ def test_folded_reduction_matches_the_reduce_kernel(B, H, D, grid, rope):
     if r is not None:
         r.close()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,H,D,grid", [(1, 2, 32, (4, 8, 8)), (3, 1, 32, (5, 7, 11)),
+                                        (2, 3, 64, (3, 5, 7)), (1, 4, 64, (2, 16, 16)),
+                                        (2, 2, 32, (4, 16, 16))])
+@pytest.mark.parametrize("rope", [True, False])
+def test_one_launch_pass_against_the_oracle_and_the_split_halves(B, H, D, grid, rope):
+    """Short D <= 64 sequences (N D <= 32,768) run the whole pass in one
+    launch, one block per head forming the state from all N tokens; its
+    output meets the oracle's bar, and agrees with the separately called
+    halves (state, reduce and output kernels) to bf16 rounding."""
+    T, Hh, W = grid
+    N = T * Hh * W
+    say(f"case one-launch pass B={B} H={H} D={D} grid={grid} rope={rope}")
+    q, k, v, g = random_inputs(B, N, H, D, seed=93)
+    qd, kd, vd, gd = to_dev(q, k, v, g)
+    r = gla.gla_rope_create(T, Hh, W, D) if rope else None
+    ws = gla.alloc_workspace(B, N, H, D, DEV)
+    o1 = torch.empty_like(qd)
+    gla.gla_forward_ws(qd, kd, vd, gd, r, o1, ws)
+    o2 = torch.empty_like(qd)
+    gla.gla_state_ws(kd, vd, r, ws)
+    gla.gla_output_ws(qd, gd, r, o2, ws)
+    torch.cuda.synchronize()
+    if r is not None:
+        r.close()
+    ref = oracle.forward(q, k, v, g, oracle.Grid(T, Hh, W) if rope else None)
+    rel, mx = errs(o1.double().cpu().numpy(), ref)
+    say(f"  vs oracle rel={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_TOL and mx <= ABS_TOL
+    rel2, mx2 = errs(o1.double().cpu().numpy(), o2.double().cpu().numpy())
+    say(f"  vs split halves rel={rel2:.3e} max_abs={mx2:.3e}")
+    assert rel2 <= REL_TOL and mx2 <= ABS_TOL
 
 
 def test_relative_position_shift():
