@@ -1158,14 +1158,21 @@ void state_tile_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 // Persistent output kernel (one attention block per head: the bidirectional
 // mixer).  Block = 4 waves (256 threads), one per compute unit: the launch
-// asks for enough LDS that two blocks never share a compute unit.  Each block
-// keeps one head's S operand (and the whole RoPE table when it fits) in LDS
-// for its whole life and walks the head's 64-token ranges s, s + NS, s + 2NS,
-// ... (NS blocks per head), wave w taking tokens 16 w .. 16 w + 15 of each.
-// The blocks of all heads then read and write a compact window of whole token
-// rows at any time, which measured faster than both the per-range blocks of
-// output_kernel (that restage S for every range) and long contiguous ranges
-// per block.  A step is output_kernel's step (same arithmetic, same result).
+// asks for enough LDS that two blocks never share a compute unit.  A block
+// serves G consecutive heads of one batch element (G = 1, 2 or 4): it keeps
+// their S operands (and the whole RoPE table when it fits: fp32 pairs, or
+// fp16 pairs beside several operands) in LDS for its whole life and walks
+// the group's (64 / G)-token ranges s, s + NS, s + 2 NS, ... (NS blocks per
+// group); wave w takes head G g + w % G and tokens 16 (w / G) .. + 15 of each
+// range.  The blocks of all groups then read and write a compact window of
+// the sequence at any time, in runs of G heads' whole rows per token, which
+// measured faster than the per-range blocks of output_kernel (that restage
+// S for every range), than long contiguous ranges per block, and (G = 4)
+// than one head's rows.  A step is output_kernel's step (same arithmetic,
+// same result).  At D <= 64 the block can instead take its head's operand
+// from the chunk partials, or form the head's whole state itself first
+// (the SRC template argument), so that short passes need fewer launches.
+//
 // Where a block's state operand comes from (the SRC template argument).
 constexpr int kSrcReduced = 0;   // the reduce kernel's operand rows (a.sl)
 constexpr int kSrcPartials = 1;  // the head's chunk partials, summed here

@@ -124,7 +124,10 @@ int gla_forward(const void* q, const void* k, const void* v, const void* g,
 /* Same as gla_forward with a caller-owned device workspace (>= the size
  * gla_workspace_bytes returns, 256-byte aligned, overlapping none of the
  * tensors: GLA_ERR_ALIAS otherwise).  The workspace must not be used by
- * other work while this call's kernels run.  Never allocates. */
+ * other work while this call's kernels run.  Never allocates.  Short passes
+ * (D <= 64) may run in fewer launches and use less of the workspace (one
+ * launch with none of it for N * D <= 32768); the result does not depend on
+ * the workspace's contents either way. */
 int gla_forward_ws(const void* q, const void* k, const void* v, const void* g,
                    const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
                    void* workspace, size_t workspace_bytes, void* stream);
