@@ -261,8 +261,12 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
   unsigned char* my_a = atile + 16 * wave * TP;
   unsigned char* my_rq = rqtile + 16 * wave * TP;
 
+  // QR (D = 128): q is loaded as whole rows only; its A operand comes from
+  // the rows through the wave's a-tile rows (free until this step writes a),
+  // which also keep the row chunks for the dq mask and dz until then
+  constexpr bool QR = D == 128;
   int base = n_begin + 16 * wave;
-  issue_q(base);
+  if (!QR) issue_q(base);
   issue_gd(base);
   issue_qc(base);
   wait_vmem_all();
@@ -274,6 +278,15 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
       int t, y, x;
       grid_pos(a, (uint32_t)min(base + col, n_end - 1), t, y, x);
       rof = row_offsets<D>(a, tv, t, y, x);
+    }
+    if constexpr (QR) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<OChunk*>(my_a + (4 * m + i) * TP + OB * col) = qc[i];
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        qv[s2] = *reinterpret_cast<const u32x4*>(my_a + col * TP + 16 * (4 * s2 + m));
+      issue_qc(next);
     }
     // den: phi(q) against z_hi (even lane columns) and z_lo (odd ones)
     u32x4 fq[KS];
@@ -292,7 +305,7 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
       constexpr int s2 = decltype(S2)::value;
       Aq[s2] = __builtin_bit_cast(bf16x8, ROPE ? rope_chunk<D, s2>(fq[s2], tv, rof, m) : fq[s2]);
     });
-    issue_q(next);
+    if (!QR) issue_q(next);
     // R phi(q) of token col, features 32 s + 8 m .. + 7, into the rq tile
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2)
@@ -302,6 +315,13 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
     f32x4 acc[MB];
     contract_rows<D>(sS, Aq, col, m, acc);
 
+    // QR: the q row chunks back from the a tile before a overwrites them
+    OChunk qk[4];
+    if constexpr (QR) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qk[i] = *reinterpret_cast<const OChunk*>(my_a + (4 * m + i) * TP + OB * col);
+    }
     // dg, a and the row sums of dout o
     float rden[4], part[4];
 #pragma unroll
@@ -363,7 +383,7 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
           xr = x * cs[u].x + y * cs[u].y;
           yr = y * cs[u].x - x * cs[u].y;
         }
-        const float q0 = bf_lo(qc[i][u]), q1 = bf_hi(qc[i][u]);
+        const float q0 = bf_lo(QR ? qk[i][u] : qc[i][u]), q1 = bf_hi(QR ? qk[i][u] : qc[i][u]);
         const float g0 = q0 > 0.f ? xr + dden[i] * zl[2 * u] : 0.f;
         const float g1 = q1 > 0.f ? yr + dden[i] * zl[2 * u + 1] : 0.f;
         dzacc[2 * u] += dden[i] * fmaxf(q0, 0.f);
@@ -372,7 +392,7 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
       }
       store_chunk_nt<OB>(rdq, r_offset(base, i), wq);
     }
-    issue_qc(next);
+    if (!QR) issue_qc(next);
     __builtin_amdgcn_sched_barrier(0);
 
     // dS += rq a^T over the block step's 16 NW tokens
