@@ -39,7 +39,7 @@ namespace gla {
 namespace {
 
 constexpr int kQueryWaves = 8;
-constexpr int kKeyWaves = 8;
+constexpr int kKeyWaves = 4;
 
 template <int D>
 struct BwdCfg {
@@ -449,14 +449,16 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
   }
 }
 
-// Key kernel.  Block = 8 waves (the two operands take about half the LDS,
-// so one block per compute unit: 8 waves make two per SIMD), one (token
-// range, head); grid (B H, C2).
+// Key kernel.  Block = 4 waves, one (head, c) of grid (B H, C2): the two
+// operands, the k and v tiles and the table take most of the LDS, so one block per
+// compute unit, one wave per SIMD (measured faster than 8 waves, two per
+// SIMD: 500.7 against 519.1 us per backward pass at 5B 720p/193f).  The block
+// walks the head's 64-token ranges c, c + C2, ...
 // LDS holds the head's dS^T and dS row operands and fp32 dz.  Per 16-token
 // step: R phi(k) against dS^T gives dv; v (as loaded) against dS rows gives
 // dS v, rotated back by R^T, plus dz, masked by k > 0: dk.
 template <int D, bool ROPE, bool TLDS>
-__global__ __launch_bounds__(64 * kKeyWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kKeyWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_key_kernel(KArgs a, BArgs bw) {
   using Cf = BwdCfg<D>;
   constexpr int KS = Cf::KS, MB = Cf::MB, OB = Cf::OB, PU = Cf::PU;
