@@ -1178,8 +1178,13 @@ constexpr int kSrcReduced = 0;   // the reduce kernel's operand rows (a.sl)
 constexpr int kSrcPartials = 1;  // the head's chunk partials, summed here
 constexpr int kSrcInBlock = 2;   // the head's state, formed here from all N tokens
 
+// Register budget: the RoPE forms allocate about 220 VGPRs either way, and
+// keep the allocation of a one-wave-per-SIMD target.  Without RoPE that
+// target let the grouped kernels grow past 256 and shuttle values through
+// the accumulation registers (about 8% slower); the two-wave target keeps
+// them in 256.
 template <int D, bool ROPE, bool TLDS, int G, bool T16, bool QROWS, int SRC = kSrcReduced>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROPE ? 1 : 2, 2)))
 void output_persist_kernel(KArgs a, int nsub) {
   // QROWS: whole-row q loads (four rows of 16 chunks) through a per-wave LDS
   // tile (D = 128)
@@ -1209,11 +1214,12 @@ void output_persist_kernel(KArgs a, int nsub) {
   // operand
   constexpr int SCR = SRC == kSrcInBlock ? StateCfg<D>::LDS_BYTES : 0;
   float2* ltab = reinterpret_cast<float2*>(smem + G * OPB + (QROWS ? 4 * QT : 0) + SCR);
-  // head groups vary fastest over the grid; wave w takes head G g + w % G of
-  // the group's batch element, and tokens 16 (w / G) .. of each range
-  const int hgs = a.H / G;
-  const int b = (int)blockIdx.x / hgs;
-  const int h = ((int)blockIdx.x - b * hgs) * G + wave % G;
+  // grid (head group, range, batch element): wave w takes head G g + w % G,
+  // and tokens 16 (w / G) .. of each range.  (A batch index divided out of
+  // one grid dimension can land in vector registers; the compiler then
+  // wraps buffer loads in loops over the lanes.)
+  const int b = blockIdx.z;
+  const int h = (int)blockIdx.x * G + wave % G;
   const int bh = b * a.H + h;
   const int s = blockIdx.y;
   const int N = a.N;
@@ -1526,21 +1532,40 @@ void output_persist_kernel(KArgs a, int nsub) {
 
   // three register sets: the loads of the next two steps are in flight
   // during a step
+  // At D = 128 without q tiles the loop runs whole rounds of three steps with
+  // no exit inside a round, and the last one or two steps follow it: with an
+  // exit after every step, the compiler merges the exits' state into the loop
+  // head, which then waits for the next step's loads as well (3.5% of the
+  // kernel at 5B 720p/60s).  With q tiles, or at D <= 64, the whole-round
+  // form needs more registers than it saves, and the loop keeps its exits.
   u32x4 qc[KS];
   OChunk gc[4];
   if (base < N) {
     load_qg(base + stride, qb, gb);
-    for (;;) {
-      load_qg(base + 2 * stride, qc, gc);
-      step(base, qa, ga);
-      if (base + stride >= N) break;
-      load_qg(base + 3 * stride, qa, ga);
-      step(base + stride, qb, gb);
-      if (base + 2 * stride >= N) break;
-      load_qg(base + 4 * stride, qb, gb);
-      step(base + 2 * stride, qc, gc);
-      if (base + 3 * stride >= N) break;
-      base += 3 * stride;
+    if constexpr (QROWS || D < 128) {
+      for (;;) {
+        load_qg(base + 2 * stride, qc, gc);
+        step(base, qa, ga);
+        if (base + stride >= N) break;
+        load_qg(base + 3 * stride, qa, ga);
+        step(base + stride, qb, gb);
+        if (base + 2 * stride >= N) break;
+        load_qg(base + 4 * stride, qb, gb);
+        step(base + 2 * stride, qc, gc);
+        if (base + 3 * stride >= N) break;
+        base += 3 * stride;
+      }
+    } else {
+      for (; base + 2 * stride < N; base += 3 * stride) {
+        load_qg(base + 2 * stride, qc, gc);
+        step(base, qa, ga);
+        load_qg(base + 3 * stride, qa, ga);
+        step(base + stride, qb, gb);
+        load_qg(base + 4 * stride, qb, gb);
+        step(base + 2 * stride, qc, gc);
+      }
+      if (base < N) step(base, qa, ga);
+      if (base + stride < N) step(base + stride, qb, gb);
     }
   }
 }
@@ -1651,7 +1676,6 @@ int persist_nsub(const Plan& p, int G) {
 
 template <int D, int G, bool QR, int SRC = kSrcReduced>
 hipError_t launch_output_persist(const Plan& p, KArgs a, hipStream_t stream) {
-  const int groups = p.BH / G;
   // kSrcInBlock: one block per head, which forms the state itself
   const int nsub = SRC == kSrcInBlock ? 1 : persist_nsub(p, G);
   const size_t pairs = persist_table_pairs(a);
@@ -1661,7 +1685,7 @@ hipError_t launch_output_persist(const Plan& p, KArgs a, hipStream_t stream) {
   const bool t16 = G > 1 && a.cs && !t32 && fixed + 4 * pairs <= kMaxLdsPerBlock;
   size_t lds = fixed + (t32 ? 8 * pairs : (t16 ? 4 * pairs : 0));
   if (lds < kPersistLdsBytes) lds = kPersistLdsBytes;
-  const dim3 g(groups, nsub);
+  const dim3 g(p.H / G, nsub, p.B);
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = allow_lds<decltype(kern)::value>(lds);
     if (e != hipSuccess) return e;
