@@ -1532,17 +1532,18 @@ void output_persist_kernel(KArgs a, int nsub) {
 
   // three register sets: the loads of the next two steps are in flight
   // during a step
-  // At D = 128 without q tiles the loop runs whole rounds of three steps with
-  // no exit inside a round, and the last one or two steps follow it: with an
-  // exit after every step, the compiler merges the exits' state into the loop
-  // head, which then waits for the next step's loads as well (3.5% of the
-  // kernel at 5B 720p/60s).  With q tiles, or at D <= 64, the whole-round
-  // form needs more registers than it saves, and the loop keeps its exits.
+  // At D = 128 the loop runs whole rounds of three steps with no exit inside
+  // a round, and the last one or two steps follow it: with an exit after
+  // every step, the compiler merges the exits' state into the loop head,
+  // which then waits for the next step's loads as well (3.5% of the kernel
+  // at 5B 720p/60s, 4% at 5B 480p/81f).  With four heads' q tiles, or at
+  // D <= 64, the whole-round form needs more registers than it saves, and
+  // the loop keeps its exits.
   u32x4 qc[KS];
   OChunk gc[4];
   if (base < N) {
     load_qg(base + stride, qb, gb);
-    if constexpr (QROWS || D < 128) {
+    if constexpr ((QROWS && G == 4) || D < 128) {
       for (;;) {
         load_qg(base + 2 * stride, qc, gc);
         step(base, qa, ga);
