@@ -445,6 +445,20 @@ def backward_bench(args, w, gla, dev, tensors, rope, stream):
         "frac": sv_achieved / PEAK_HBM_GBPS, "traffic": sv_traffic,
         "traffic_over_algorithmic": sv_traffic / nbytes if sv_traffic else None,
         "algorithmic_bytes": nbytes}
+    # What the pass would take if each kernel streamed its algorithmic bytes
+    # at the plain-streaming rate of its own mix (query 10 D, key 8 D, state
+    # 4 D per (token, head); the small partial and reduce traffic left out).
+    log("bench: streaming ceiling of the backward mixes")
+    ceil = backward_stream_ceiling(gla, dev, stream)
+    del sets, grads, ws
+    q_ms = 10 * w.D * units / (ceil["read_3_write_2"]["GB/s"] * 1e9) * 1e3
+    k_ms = 8 * w.D * units / (ceil["read_2_write_2"]["GB/s"] * 1e9) * 1e3
+    s_ms = 4 * w.D * units / (ceil["read_2_streams"]["GB/s"] * 1e9) * 1e3
+    ceil["pass_ms_at_these_rates"] = q_ms + k_ms + s_ms
+    ceil["saved_state_pass_ms_at_these_rates"] = q_ms + k_ms
+    result["streaming_ceiling"] = ceil
+    result["frac_of_streaming_ceiling"] = (q_ms + k_ms + s_ms) / ev_ms
+    result["saved_state"]["frac_of_streaming_ceiling"] = (q_ms + k_ms) / sv_ms
     if not args.no_cpu_baseline:
         log("bench: timing the oracle (cpu_baseline)")
         q, k, v, g = (t.cpu() for t in tensors)
@@ -580,6 +594,50 @@ def stream_ceiling(gla, dev, stream, reps=20):
     del sets
     torch.cuda.synchronize()
     res["buffers"] = (f"3 rotating sets of 3 x {STREAM_PROBE_BYTES >> 20} MiB, contiguous 16 KB "
+                      f"pieces per block")
+    return res
+
+
+def backward_stream_ceiling(gla, dev, stream, reps=20):
+    """Plain-streaming rates of the backward kernels' mixes on the same load
+    path (gla_stream_probe_mix, and gla_stream_probe for two reads): three
+    reads and two writes (the query kernel: q, g, dout in, dq, dg out), two
+    reads and two writes (the key kernel: k, v in, dk, dv out), and two reads
+    (the state kernel), over three rotating sets of 768 MiB buffers, median of
+    `reps` timed launches each."""
+    import torch
+    sets = [[torch.empty(STREAM_PROBE_BYTES, dtype=torch.uint8, device=dev) for _ in range(5)]
+            for _ in range(ROTATE)]
+    for st in sets:
+        for t in st:
+            t.fill_(1)
+    mixes = (("read_3_write_2", 3, 2), ("read_2_write_2", 2, 2), ("read_2_streams", 2, 0))
+
+    def run(i, ns, nd):
+        st = sets[i % ROTATE]
+        if nd == 0:
+            gla.gla_stream_probe(st[0], st[1], st[2], 0, stream)
+        else:
+            gla.gla_stream_probe_mix(st[:ns], st[3:3 + nd], stream)
+
+    res = {}
+    for name, ns, nd in mixes:
+        for i in range(3):
+            run(i, ns, nd)
+        ts = []
+        for i in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run(i, ns, nd)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = statistics.median(ts)
+        res[name] = {"GB/s": (ns + nd) * STREAM_PROBE_BYTES / (ms * 1e-3) / 1e9, "ms": ms}
+    del sets
+    torch.cuda.synchronize()
+    res["buffers"] = (f"3 rotating sets of 5 x {STREAM_PROBE_BYTES >> 20} MiB, contiguous 16 KB "
                       f"pieces per block")
     return res
 

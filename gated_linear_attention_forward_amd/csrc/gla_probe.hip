@@ -56,8 +56,82 @@ __global__ __launch_bounds__(kProbeThreads) void stream_probe_kernel(const unsig
     store16_nt(rd, threadIdx.x * 16u, acc);
 }
 
+// Any mix of one to three read streams and one or two write streams (each
+// destination gets the XOR of the sources): the backward kernels' mixes.
+// Same pieces and loads in flight per buffer as above.
+struct ProbeBufs {
+  const unsigned char* src[3];
+  unsigned char* dst[2];
+};
+
+template <int NS, int ND>
+__global__ __launch_bounds__(kProbeThreads) void stream_mix_kernel(ProbeBufs p, uint32_t bytes) {
+  __amdgpu_buffer_rsrc_t rs[NS], rd[ND];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) rs[i] = make_rsrc(p.src[i], bytes);
+#pragma unroll
+  for (int j = 0; j < ND; ++j) rd[j] = make_rsrc(p.dst[j], bytes);
+  const uint32_t begin = blockIdx.x * kProbeBlockBytes;
+  const uint32_t end = begin + kProbeBlockBytes < bytes ? begin + kProbeBlockBytes : bytes;
+  for (uint32_t o = begin + threadIdx.x * 16u; o < end; o += kProbeThreads * 16u * kProbeInFlight) {
+    u32x4 v[kProbeInFlight][NS];
+#pragma unroll
+    for (int k = 0; k < kProbeInFlight; ++k) {
+      const uint32_t off = o + (uint32_t)k * kProbeThreads * 16u;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) v[k][i] = load16_nt(rs[i], off < end ? off : kOob);
+    }
+#pragma unroll
+    for (int k = 0; k < kProbeInFlight; ++k) {
+      const uint32_t off = o + (uint32_t)k * kProbeThreads * 16u;
+      u32x4 x = v[k][0];
+#pragma unroll
+      for (int i = 1; i < NS; ++i) x ^= v[k][i];
+#pragma unroll
+      for (int j = 0; j < ND; ++j) store16_nt(rd[j], off < end ? off : kOob, x);
+    }
+  }
+}
+
+template <int NS, int ND>
+int launch_mix(const ProbeBufs& p, uint32_t bytes, hipStream_t s) {
+  const unsigned blocks = (bytes + kProbeBlockBytes - 1) / kProbeBlockBytes;
+  hipLaunchKernelGGL((stream_mix_kernel<NS, ND>), dim3(blocks), dim3(kProbeThreads), 0, s, p, bytes);
+  return hipGetLastError() == hipSuccess ? GLA_OK : GLA_ERR_LAUNCH;
+}
+
 }  // namespace
 }  // namespace gla
+
+extern "C" int gla_stream_probe_mix(const void* const* srcs, int nsrc, void* const* dsts, int ndst,
+                                    size_t bytes, void* stream) {
+  if (!srcs || !dsts) return GLA_ERR_NULL;
+  if (nsrc < 1 || nsrc > 3 || ndst < 1 || ndst > 2) return GLA_ERR_DIM;
+  gla::ProbeBufs p{};
+  for (int i = 0; i < nsrc; ++i) {
+    if (!srcs[i]) return GLA_ERR_NULL;
+    p.src[i] = static_cast<const unsigned char*>(srcs[i]);
+  }
+  for (int j = 0; j < ndst; ++j) {
+    if (!dsts[j]) return GLA_ERR_NULL;
+    p.dst[j] = static_cast<unsigned char*>(dsts[j]);
+  }
+  for (int i = 0; i < nsrc; ++i)
+    if ((uintptr_t)p.src[i] & 15u) return GLA_ERR_ALIGN;
+  for (int j = 0; j < ndst; ++j)
+    if ((uintptr_t)p.dst[j] & 15u) return GLA_ERR_ALIGN;
+  if (bytes == 0 || bytes % 16 != 0 || bytes >= (size_t)1 << 31) return GLA_ERR_DIM;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t n = (uint32_t)bytes;
+  switch (nsrc * 4 + ndst) {
+    case 1 * 4 + 1: return gla::launch_mix<1, 1>(p, n, s);
+    case 1 * 4 + 2: return gla::launch_mix<1, 2>(p, n, s);
+    case 2 * 4 + 1: return gla::launch_mix<2, 1>(p, n, s);
+    case 2 * 4 + 2: return gla::launch_mix<2, 2>(p, n, s);
+    case 3 * 4 + 1: return gla::launch_mix<3, 1>(p, n, s);
+    default: return gla::launch_mix<3, 2>(p, n, s);
+  }
+}
 
 extern "C" int gla_stream_probe(const void* src0, const void* src1, void* dst, size_t bytes,
                                 int mode, void* stream) {

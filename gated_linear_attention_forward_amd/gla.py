@@ -38,7 +38,7 @@ EXPORTS = (
     "gla_backward_ws", "gla_backward_workspace_bytes", "gla_backward_check",
     "gla_backward_saved", "gla_backward_saved_ws", "gla_backward_saved_check",
     "gla_forward_proj", "gla_forward_proj_ws", "gla_proj_workspace_bytes",
-    "gla_forward_proj_check", "gla_stream_probe",
+    "gla_forward_proj_check", "gla_stream_probe", "gla_stream_probe_mix",
 )
 
 
@@ -109,6 +109,7 @@ def load_library():
         "gla_proj_workspace_bytes": ([i32] * 5, sz),
         "gla_forward_proj_check": ([vp, vp, rp, vp] + [i32] * 5, i32),
         "gla_stream_probe": ([vp, vp, vp, sz, i32, vp], i32),
+        "gla_stream_probe_mix": ([ctypes.POINTER(vp), i32, ctypes.POINTER(vp), i32, sz, vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -685,3 +686,21 @@ def gla_stream_probe(src0: torch.Tensor, src1: torch.Tensor, dst: torch.Tensor, 
         _ok(load_library().gla_stream_probe(src0.data_ptr(), src1.data_ptr(), dst.data_ptr(),
                                             nbytes, int(mode), _stream_handle(stream, src0.device)),
             "gla_stream_probe")
+
+
+def gla_stream_probe_mix(srcs, dsts, stream=None):
+    """Streams every tensor of `srcs` (1 to 3) and writes every tensor of
+    `dsts` (1 or 2) with their XOR, through the library's bandwidth probe;
+    all same-sized contiguous device tensors."""
+    bufs = list(srcs) + list(dsts)
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    for t in bufs:
+        if t.numel() * t.element_size() != nbytes or not t.is_contiguous():
+            raise ValueError("probe buffers must be contiguous and of one size")
+    vp = ctypes.c_void_p
+    sarr = (vp * max(len(srcs), 1))(*[t.data_ptr() for t in srcs])
+    darr = (vp * max(len(dsts), 1))(*[t.data_ptr() for t in dsts])
+    with torch.cuda.device(bufs[0].device):
+        _ok(load_library().gla_stream_probe_mix(sarr, len(srcs), darr, len(dsts), nbytes,
+                                                _stream_handle(stream, bufs[0].device)),
+            "gla_stream_probe_mix")

@@ -394,7 +394,7 @@ int gla_forward_proj_check(const void* x, const void* w, const gla_rope_tables* 
  *
  * Streams `bytes` (a multiple of 16, below 2 GiB) of each of two device
  * buffers through the load path the mixer's kernels use (16-byte buffer
- * loads with the non-temporal hint, 64 KB contiguous per block):
+ * loads with the non-temporal hint, 16 KB contiguous per block):
  *   mode 0: reads src0 and src1 (the state half's two read streams);
  *   mode 1: also writes dst = src0 ^ src1 with non-temporal stores (the
  *           output half's two reads and one write).
@@ -403,6 +403,16 @@ int gla_forward_proj_check(const void* x, const void* w, const gla_rope_tables* 
  * call.  Enqueued on `stream`; the caller times it. */
 int gla_stream_probe(const void* src0, const void* src1, void* dst, size_t bytes, int mode,
                      void* stream);
+
+/* The same probe for any mix of `nsrc` (1..3) read streams and `ndst` (1..2)
+ * write streams, `bytes` of each buffer (the backward pass's query kernel
+ * reads three tensors and writes two, its key kernel reads two and writes
+ * two).  srcs and dsts are host arrays of device pointers; every destination
+ * receives the XOR of the sources, written with non-temporal stores.  Same
+ * rules and error codes as gla_stream_probe (GLA_ERR_DIM also for nsrc or
+ * ndst out of range), all checked before any HIP call. */
+int gla_stream_probe_mix(const void* const* srcs, int nsrc, void* const* dsts, int ndst,
+                         size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

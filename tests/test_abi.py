@@ -439,3 +439,27 @@ def test_stream_probe_validates_before_launching():
     assert lib.gla_stream_probe(A, 2 * A, 3 * A, 1000, 0, None) == glamod.GLA_ERR_DIM
     assert lib.gla_stream_probe(A, 2 * A, 3 * A, 1 << 31, 0, None) == glamod.GLA_ERR_DIM
     assert lib.gla_stream_probe(A, 2 * A, 3 * A, 1 << 20, 2, None) == glamod.GLA_ERR_DIM
+
+
+def test_stream_probe_mix_validates_before_launching():
+    lib = gla.load_library()
+    vp = ctypes.c_void_p
+
+    def arr(*ptrs):
+        return (vp * len(ptrs))(*ptrs)
+
+    ok_s, ok_d = arr(A, 2 * A, 3 * A), arr(4 * A, 5 * A)
+    mix = lib.gla_stream_probe_mix
+    assert mix(None, 3, ok_d, 2, 1 << 20, None) == glamod.GLA_ERR_NULL
+    assert mix(ok_s, 3, None, 2, 1 << 20, None) == glamod.GLA_ERR_NULL
+    for ns, nd in ((0, 1), (4, 1), (1, 0), (1, 3), (-1, 1)):
+        assert mix(ok_s, ns, ok_d, nd, 1 << 20, None) == glamod.GLA_ERR_DIM
+    assert mix(arr(A, 0, 3 * A), 3, ok_d, 2, 1 << 20, None) == glamod.GLA_ERR_NULL
+    assert mix(ok_s, 3, arr(4 * A, 0), 2, 1 << 20, None) == glamod.GLA_ERR_NULL
+    assert mix(arr(A, 2 * A + 8, 3 * A), 3, ok_d, 2, 1 << 20, None) == glamod.GLA_ERR_ALIGN
+    assert mix(ok_s, 3, arr(4 * A, 5 * A + 4), 2, 1 << 20, None) == glamod.GLA_ERR_ALIGN
+    for nbytes in (0, 1000, 1 << 31):
+        assert mix(ok_s, 3, ok_d, 2, nbytes, None) == glamod.GLA_ERR_DIM
+    # only the first nsrc / ndst entries are read: a null past them is fine
+    # for validation, which then fails on the size
+    assert mix(arr(A, 0, 0), 1, arr(4 * A, 0), 1, 1000, None) == glamod.GLA_ERR_DIM

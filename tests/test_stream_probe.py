@@ -35,3 +35,24 @@ def test_probe_read_mode_leaves_the_destination():
     gla.gla_stream_probe(a, b, d, 0)
     torch.cuda.synchronize()
     assert (d == 7).all()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nsrc,ndst", [(1, 1), (2, 2), (3, 2), (3, 1)])
+@pytest.mark.parametrize("nbytes", [16, 5 * 16 * 1024 + 48])
+def test_probe_mix_writes_the_xor_to_every_destination(nsrc, ndst, nbytes):
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device="cpu").manual_seed(nbytes + 10 * nsrc + ndst)
+    srcs = [torch.randint(0, 256, (nbytes,), generator=gen, dtype=torch.uint8)
+            for _ in range(nsrc)]
+    want = srcs[0].clone()
+    for t in srcs[1:]:
+        want ^= t
+    dbufs = [torch.zeros(nbytes + 256, dtype=torch.uint8, device=dev) for _ in range(ndst)]
+    print(f"stream probe mix {nsrc} reads {ndst} writes, {nbytes} bytes", flush=True)
+    gla.gla_stream_probe_mix([t.to(dev) for t in srcs], [d[:nbytes] for d in dbufs])
+    torch.cuda.synchronize()
+    for d in dbufs:
+        d = d.cpu()
+        assert torch.equal(d[:nbytes], want)
+        assert not d[nbytes:].any()  # nothing past the end
