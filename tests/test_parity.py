@@ -78,6 +78,8 @@ SMALL = [
     (1, 4, 128, (64, 32, 33)),  # 67,584 tokens: four heads to an output block, ragged
     (2, 8, 128, (16, 40, 103)), # 65,920 tokens, B = 2: two head groups per batch element
     (1, 4, 128, (200, 3, 110)), # four heads, a RoPE table too long for LDS beside the q tiles
+                                # (16 or 17 steps per wave: one or two after the whole rounds)
+    (1, 4, 128, (192, 16, 24)), # the same path with 18 steps per wave: whole rounds only
     (1, 6, 128, (45, 31, 32)),  # six heads: two to an output block
 ]
 
