@@ -545,12 +545,16 @@ int gla_state(const void* k, const void* v, const gla_rope_tables* rope, float* 
                 overlap2(z, zbytes, k, bytes) || overlap2(z, zbytes, v, bytes)))
     return GLA_ERR_ALIAS;
   if (overlap2(S, sbytes, z, zbytes)) return GLA_ERR_ALIAS;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (N == 0) {
-    // empty sequence: S = 0, z = 0
-    if (hipMemsetAsync(S, 0, sbytes, s) != hipSuccess) return GLA_ERR_HIP;
-    if (hipMemsetAsync(z, 0, zbytes, s) != hipSuccess) return GLA_ERR_HIP;
-    return GLA_OK;
+    // empty sequence: S = 0, z = 0, written by the reduce kernel with no
+    // partials and no carried state (a kernel, not a memset, so the call
+    // can be captured into a graph)
+    Plan p{};
+    p.B = B; p.N = 0; p.H = H; p.D = D; p.BH = B * H;
+    gla::KArgs a{};
+    a.H = H;
+    a.S_out = S; a.z_out = z;
+    return status_of(gla::launch_carry(p, a, static_cast<hipStream_t>(stream)));
   }
   Plan p = gla::make_plan(B, N, H, D);
   void* ws = nullptr;

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "gla_internal.h"
@@ -444,25 +445,26 @@ inline int table_lds_bytes(const KArgs& a) {
 
 // A kernel that takes more than 64 KB of dynamic LDS raises its limit on the
 // current device to the largest size asked for there so far (one record per
-// kernel and device).  Concurrent callers may both set the attribute, which
-// is harmless; the record only grows (compare-and-swap).
+// kernel and device).  Raising happens under a per-kernel lock, so the
+// attribute only ever grows: a caller asking for less can never lower it
+// below a size another thread has already recorded and launched with.
 constexpr int kMaxLdsDevices = 64;
 template <auto K>
 hipError_t allow_lds(size_t bytes) {
   static std::atomic<size_t> granted[kMaxLdsDevices];
+  static std::mutex mu;
   if (bytes <= 65536) return hipSuccess;
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxLdsDevices) return hipErrorInvalidDevice;
   if (bytes <= granted[dev].load(std::memory_order_acquire)) return hipSuccess;
+  std::lock_guard<std::mutex> lock(mu);
+  if (bytes <= granted[dev].load(std::memory_order_relaxed)) return hipSuccess;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(K),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
-  size_t cur = granted[dev].load(std::memory_order_relaxed);
-  while (cur < bytes && !granted[dev].compare_exchange_weak(cur, bytes, std::memory_order_release,
-                                                           std::memory_order_relaxed)) {
-  }
+  granted[dev].store(bytes, std::memory_order_release);
   return hipSuccess;
 }
 

@@ -378,9 +378,19 @@ def test_empty_inputs_are_noops():
         q = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
         out = gla.gla_forward(q, q.clone(), q.clone(), q.clone(), None)
         assert out.shape == q.shape
-    S, z = gla.gla_state(*(torch.empty((1, 0, 2, 32), dtype=torch.bfloat16, device=DEV),) * 2)
-    torch.cuda.synchronize()
-    assert torch.all(S == 0) and torch.all(z == 0)
+    # no tokens: the state is exactly zero (written by a kernel, every element)
+    for D in (32, 64, 128):
+        k = torch.empty((2, 0, 3, D), dtype=torch.bfloat16, device=DEV)
+        # freed NaN blocks of the same sizes, which torch's caching allocator
+        # hands out again for S and z
+        junk = (torch.full((2, 3, D, D), float("nan"), device=DEV),
+                torch.full((2, 3, D), float("nan"), device=DEV))
+        torch.cuda.synchronize()
+        del junk
+        S, z = gla.gla_state(k, k.clone())
+        torch.cuda.synchronize()
+        assert S.shape == (2, 3, D, D) and z.shape == (2, 3, D)
+        assert torch.all(S == 0) and torch.all(z == 0)
 
 
 def test_bad_calls_raise():
