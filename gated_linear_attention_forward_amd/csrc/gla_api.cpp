@@ -117,6 +117,7 @@ int check_shape(int B, int N, int H, int D, size_t* bytes) {
 int check_rope(const gla_rope_tables* rope, int N, int D) {
   if (!rope) return GLA_OK;
   if (!rope->cs) return GLA_ERR_NULL;
+  if (!aligned16(rope->cs)) return GLA_ERR_ALIGN;  // the kernels copy it in 16-byte loads
   if (rope->D != D) return GLA_ERR_ROPE;
   if ((long long)rope->T * rope->Hh * rope->W != (long long)N) return GLA_ERR_ROPE;
   // the kernels fix the axis split for each D (as gla_rope_create builds it)

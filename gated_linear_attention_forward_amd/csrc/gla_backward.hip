@@ -188,7 +188,7 @@ void bwd_query_kernel(KArgs a, BArgs bw) {
     const float zv = tid < D ? bw.z[(size_t)bh * D + tid] : 0.f;
     if (ROPE) {
       if (TLDS) {
-        copy_to_lds<NT>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        copy_table_to_lds<NT, 8, false>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
         tv.tab = ltab;
       } else {
         tv.tab = a.cs;
@@ -495,7 +495,7 @@ void bwd_key_kernel(KArgs a, BArgs bw) {
     const float zv = tid < D ? bw.dz[(size_t)bh * D + tid] : 0.f;
     if (ROPE) {
       if (TLDS) {
-        copy_to_lds<NT>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        copy_table_to_lds<NT, 8, false>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
         tv.tab = ltab;
       } else {
         tv.tab = a.cs;

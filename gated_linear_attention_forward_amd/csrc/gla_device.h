@@ -20,6 +20,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kEps = 1e-6f;
@@ -112,46 +113,103 @@ struct TabView {
   const uint32_t* tab16;  // the same pairs as packed fp16 (cos, sin), when so staged
 };
 
-// Copies n float2 from global memory to LDS with a block of NT threads,
-// four loads in flight per thread before their LDS writes (one wait for
-// memory per four loads, not one per load).  Caller synchronises.
-template <int NT>
-__device__ __forceinline__ void copy_to_lds(float2* dst, const float2* src, int n) {
-  for (int b0 = threadIdx.x; b0 < n; b0 += 4 * NT) {
-    float2 v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = b0 + k * NT;
-      if (i < n) v[k] = src[i];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = b0 + k * NT;
-      if (i < n) dst[i] = v[k];
-    }
+// Copies the n (cos, sin) pairs of a RoPE table from global memory to LDS
+// with a block of NT threads, as fp32 pairs (F16 = false) or as packed fp16
+// pairs (F16 = true, rounded to nearest even).  Whole pairs of pairs go as
+// 16-byte loads, R of them per thread issued before any LDS write, so a
+// table of up to 2 R NT pairs takes one memory round trip; loads past them
+// read zero (buffer bounds) and are not written.  An odd last pair is read
+// on its own.  Caller synchronises.
+template <bool F16>
+__device__ __forceinline__ void put_table_pair(void* dst, int i, float c, float sn) {
+  if constexpr (F16) {
+    const _Float16 hc = (_Float16)c, hs = (_Float16)sn;
+    static_cast<uint32_t*>(dst)[i] = (uint32_t)__builtin_bit_cast(uint16_t, hc) |
+                                     ((uint32_t)__builtin_bit_cast(uint16_t, hs) << 16);
+  } else {
+    static_cast<float2*>(dst)[i] = make_float2(c, sn);
   }
 }
-
-// copy_to_lds, rounding each (cos, sin) pair to fp16 (round to nearest even)
-// and packing it into one dword: half the LDS of the fp32 pairs.
-template <int NT>
-__device__ __forceinline__ void copy_to_lds_f16(uint32_t* dst, const float2* src, int n) {
-  for (int b0 = threadIdx.x; b0 < n; b0 += 4 * NT) {
-    float2 v[4];
+// One round of a table copy: R chunks per thread from chunk c0 on.
+template <int NT, int R>
+struct TableRound {
+  u32x4 v[R];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int c0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = b0 + k * NT;
-      if (i < n) v[k] = src[i];
-    }
+    for (int k = 0; k < R; ++k)
+      v[k] = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, (uint32_t)(c0 + k * NT + (int)threadIdx.x) * 16u, 0, 0);
+  }
+  template <bool F16>
+  __device__ __forceinline__ void store(void* dst, int c0, int nc) const {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = b0 + k * NT;
-      if (i < n) {
-        const _Float16 c = (_Float16)v[k].x, sn = (_Float16)v[k].y;
-        dst[i] = (uint32_t)__builtin_bit_cast(uint16_t, c) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, sn) << 16);
+    for (int k = 0; k < R; ++k) {
+      const int ci = c0 + k * NT + (int)threadIdx.x;
+      if (ci < nc) {
+        put_table_pair<F16>(dst, 2 * ci, __uint_as_float(v[k][0]), __uint_as_float(v[k][1]));
+        put_table_pair<F16>(dst, 2 * ci + 1, __uint_as_float(v[k][2]), __uint_as_float(v[k][3]));
       }
     }
+  }
+};
+// A table of n pairs: its whole 16-byte chunks (n / 2 of them; loads past
+// them read zero) and, for odd n, its last pair on its own.
+struct TableSrc {
+  __amdgpu_buffer_rsrc_t rs;
+  int n, nc;
+  __device__ __forceinline__ TableSrc(const float2* src, int n_) : n(n_), nc(n_ / 2) {
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(src), (short)0,
+                                           (int)((uint32_t)n_ * 8u), kRsrcWord3);
+  }
+  // the odd last pair (every thread loads it; thread 0 writes it)
+  __device__ __forceinline__ u32x2 load_tail() const {
+    return n & 1 ? __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 rs, (uint32_t)(n - 1) * 8u, 0, 0))
+                 : u32x2{0u, 0u};
+  }
+  template <bool F16>
+  __device__ __forceinline__ void store_tail(void* dst, u32x2 t) const {
+    if ((n & 1) && threadIdx.x == 0)
+      put_table_pair<F16>(dst, n - 1, __uint_as_float(t[0]), __uint_as_float(t[1]));
+  }
+};
+// The first round's loads (and the odd pair's) are issued together, so a
+// table of up to 2 R NT pairs costs one memory round trip; longer tables
+// take further rounds.
+template <int NT, int R, bool F16>
+__device__ __forceinline__ void copy_table_to_lds(void* dst, const float2* src, int n) {
+  const TableSrc ts(src, n);
+  TableRound<NT, R> r;
+  r.load(ts.rs, 0);
+  const u32x2 tail = ts.load_tail();
+  r.template store<F16>(dst, 0, ts.nc);
+  ts.template store_tail<F16>(dst, tail);
+  for (int c0 = R * NT; c0 < ts.nc; c0 += R * NT) {
+    r.load(ts.rs, c0);
+    r.template store<F16>(dst, c0, ts.nc);
+  }
+}
+// Two tables (fp32 pairs) whose first rounds share one memory round trip.
+template <int NT, int R0, int R1>
+__device__ __forceinline__ void copy_two_tables_to_lds(float2* dst0, const float2* src0, int n0,
+                                                       float2* dst1, const float2* src1, int n1) {
+  const TableSrc t0(src0, n0), t1(src1, n1);
+  TableRound<NT, R0> r0;
+  TableRound<NT, R1> r1;
+  r0.load(t0.rs, 0);
+  r1.load(t1.rs, 0);
+  const u32x2 e0 = t0.load_tail(), e1 = t1.load_tail();
+  r0.template store<false>(dst0, 0, t0.nc);
+  r1.template store<false>(dst1, 0, t1.nc);
+  t0.template store_tail<false>(dst0, e0);
+  t1.template store_tail<false>(dst1, e1);
+  for (int c0 = R0 * NT; c0 < t0.nc; c0 += R0 * NT) {
+    r0.load(t0.rs, c0);
+    r0.template store<false>(dst0, c0, t0.nc);
+  }
+  for (int c0 = R1 * NT; c0 < t1.nc; c0 += R1 * NT) {
+    r1.load(t1.rs, c0);
+    r1.template store<false>(dst1, c0, t1.nc);
   }
 }
 
@@ -167,9 +225,11 @@ __device__ __forceinline__ TabView stage_table(const KArgs& a, float2* ltab, boo
   tv.t_last = (int)fast_div((uint32_t)(n_end - 1), a.div_hw);
   if (in_lds) {
     const int nt_blk = tv.t_last - t_first + 1;
-    copy_to_lds<NT>(ltab, a.cs + (size_t)t_first * X::Pt, nt_blk * X::Pt);
-    copy_to_lds<NT>(ltab + a.nt * X::Pt, a.cs + (size_t)a.T * X::Pt,
-                    a.Hh * X::Py + a.W * X::Px);
+    // the block's t-rows and the y and x tables in one memory round trip
+    // (while they fit in one or two 16-byte loads per thread)
+    copy_two_tables_to_lds<NT, 1, 2>(ltab, a.cs + (size_t)t_first * X::Pt, nt_blk * X::Pt,
+                                     ltab + a.nt * X::Pt, a.cs + (size_t)a.T * X::Pt,
+                                     a.Hh * X::Py + a.W * X::Px);
     tv.tab = ltab;
     tv.tbase = t_first;
     tv.ntr = a.nt;

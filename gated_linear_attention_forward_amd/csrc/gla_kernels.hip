@@ -1343,34 +1343,29 @@ void output_persist_kernel(KArgs a, int nsub) {
   if (base < N) load_qg(base, qa, ga);
   if constexpr (G > 1) {
     // the waves of head slot w % G (4 / G of them) stage that head's operand
-    // together, eight 16-byte chunks per lane in flight at a time
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.sl + (size_t)bh * ROWS * D);
-    constexpr int CH = ROWS * D / 8;
-    constexpr int WPH = 4 / G;  // waves per head
+    // together: every chunk a lane copies is loaded before any is written
+    // (33 chunks per lane at G = 4), and the table's loads are issued right
+    // behind them, so the staging costs one memory round trip where chunks
+    // issued eight at a time cost five
+    constexpr int CH = ROWS * D / 8;            // 16-byte chunks of one operand
+    constexpr int WPH = 4 / G;                  // waves per head
+    constexpr int LPH = 64 * WPH;               // lanes per head
+    constexpr int NCH = (CH + LPH - 1) / LPH;   // chunks per lane
     const int li = (wave / G) * 64 + lane;
+    const __amdgpu_buffer_rsrc_t rsl =
+        make_rsrc(a.sl + (size_t)bh * ROWS * D, (uint32_t)CH * 16u);  // past CH: zero
+    u32x4 v[NCH];
 #pragma unroll
-    for (int k0 = 0; k0 < CH; k0 += 8 * 64 * WPH) {
-      u32x4 v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = k0 + 64 * WPH * k + li;
-        if (i < CH) v[k] = src[i];
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = k0 + 64 * WPH * k + li;
-        if (i < CH)
-          *reinterpret_cast<u32x4*>(sS + row_tile_offset<D>(i / (D / 8), 16 * (i % (D / 8)))) = v[k];
-      }
-    }
+    for (int k = 0; k < NCH; ++k) v[k] = load16(rsl, (uint32_t)(k * LPH + li) * 16u);
     if (ROPE) {
+      const int pairs = a.T * a.Pt + a.Hh * a.Py + a.W * a.Px;
       if (T16) {
         uint32_t* lt16 = reinterpret_cast<uint32_t*>(ltab);
-        copy_to_lds_f16<256>(lt16, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        copy_table_to_lds<256, 8, true>(lt16, a.cs, pairs);
         tv.tab16 = lt16;
         tv.tab = nullptr;
       } else if (TLDS) {
-        copy_to_lds<256>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        copy_table_to_lds<256, 8, false>(ltab, a.cs, pairs);
         tv.tab = ltab;
       } else {
         tv.tab = a.cs;
@@ -1378,6 +1373,12 @@ void output_persist_kernel(KArgs a, int nsub) {
       tv.tbase = 0;
       tv.ntr = a.T;
       tv.t_last = a.T - 1;
+    }
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int i = k * LPH + li;
+      if ((k + 1) * LPH <= CH || i < CH)
+        *reinterpret_cast<u32x4*>(sS + row_tile_offset<D>(i / (D / 8), 16 * (i % (D / 8)))) = v[k];
     }
   } else if constexpr (SRC == kSrcInBlock) {
     // the whole pass in one block per head: the table, then the state over
@@ -1389,7 +1390,7 @@ void output_persist_kernel(KArgs a, int nsub) {
     unsigned char* scr = smem + OPB;
     if (ROPE) {
       if (TLDS) {
-        copy_to_lds<256>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        copy_table_to_lds<256, 8, false>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
         tv.tab = ltab;
       } else {
         tv.tab = a.cs;
@@ -1499,7 +1500,7 @@ void output_persist_kernel(KArgs a, int nsub) {
     }
     if (ROPE) {
       if (TLDS) {
-        copy_to_lds<256>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        copy_table_to_lds<256, 8, false>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
         tv.tab = ltab;
       } else {
         tv.tab = a.cs;
@@ -1516,7 +1517,7 @@ void output_persist_kernel(KArgs a, int nsub) {
     st_z.load(sl);
     if (ROPE) {
       if (TLDS) {
-        copy_to_lds<256>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
+        copy_table_to_lds<256, 8, false>(ltab, a.cs, a.T * a.Pt + a.Hh * a.Py + a.W * a.Px);
         tv.tab = ltab;
       } else {
         tv.tab = a.cs;

@@ -79,7 +79,7 @@ typedef struct gla_rope_tables {
   int32_t Pt, Py, Px;    /* rotation pairs per axis; Pt + Py + Px = D/2 */
   int32_t t0, y0, x0;    /* index offsets added to every position */
   double theta;          /* RoPE base (10000 in the Wan convention) */
-  const float* cs;       /* device pointer: the (cos, sin) pairs above */
+  const float* cs;       /* device pointer, 16-byte aligned: the (cos, sin) pairs above */
   size_t cs_floats;      /* number of floats behind cs */
   int32_t device;        /* HIP device that holds cs */
 } gla_rope_tables;

@@ -99,6 +99,8 @@ def test_rope_mismatch_rejected():
     assert check(N=64, rope=_host_rope(4, 4, 5, 128)) == glamod.GLA_ERR_ROPE
     assert check(N=64, D=64, rope=_host_rope(4, 4, 4, 128)) == glamod.GLA_ERR_ROPE
     assert check(N=64, rope=_host_rope(4, 4, 4, 128, cs=0)) == glamod.GLA_ERR_NULL
+    # the kernels read the table in 16-byte loads
+    assert check(N=64, rope=_host_rope(4, 4, 4, 128, cs=A + 8)) == glamod.GLA_ERR_ALIGN
 
 
 def test_workspace_size_formula():
