@@ -1,9 +1,10 @@
 """GPU parity of the gated softmax anchor attention (through the C ABI)
 against the fp64 oracle: relative L2 <= 5e-3 and max abs <= 3e-2 on the bf16
 output.  The GPU rounds R q (scaled) and R k to bf16, the softmax weights to
-bf16 for the value MFMA and the output to bf16.  Small shapes are compared
-in full; the anchor layers of the 5B and 14B models on sampled query rows
-that the oracle computes one by one."""
+bf16 for the value MFMA and the output to bf16.  Small shapes and the 5B
+and 14B 480p anchor layers are compared in full; the 720p anchor layer
+(22,000 tokens, quadratic in N for the oracle) on sampled query rows that
+the oracle computes one by one."""
 import numpy as np
 import pytest
 import torch
@@ -62,6 +63,32 @@ def test_softmax_small_shapes(B, H, D, grid, rope):
     got = gpu_softmax(q, k, v, g, grid if rope else None).double().cpu().numpy()
     ref = oracle.softmax_forward(q, k, v, g, oracle.Grid(*grid) if rope else None)
     assert_close(got, ref, "out")
+
+
+@pytest.mark.parametrize("name", ["anchor_5b_480p_81f", "anchor_14b_480p_193f"])
+def test_anchor_layer_every_output(name):
+    """The 5B and 14B 480p anchor layers (10 heads x 4,290 tokens; 2 x 16
+    heads x 9,750 tokens; D = 256): every output of every head against the
+    oracle, a head at a time (about 2 s and 10 s of oracle work per head on
+    8 threads)."""
+    w = BY_NAME[name]
+    say(f"case softmax every output {w.name} B={w.B} N={w.N} H={w.H} D={w.D}")
+    q, k, v, g = make_inputs(w)
+    out = gpu_softmax(q, k, v, g, (w.T, w.Hh, w.W)).double().cpu().numpy()
+    grid = oracle.Grid(w.T, w.Hh, w.W)
+    rows = np.arange(w.N)
+    d2 = r2 = mx = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            ref = oracle.softmax_rows(q, k, v, g, grid, b, h, rows)
+            got = out[b, :, h]
+            d2 += float(np.sum((got - ref) ** 2))
+            r2 += float(np.sum(ref ** 2))
+            mx = max(mx, float(np.max(np.abs(got - ref))))
+        say(f"  batch element {b}: {w.H} heads done")
+    rel = (d2 / r2) ** 0.5
+    say(f"  {w.name} all outputs: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_TOL and mx <= ABS_TOL
 
 
 @pytest.mark.parametrize("name", [w.name for w in ANCHOR_WORKLOADS])
