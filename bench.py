@@ -702,6 +702,9 @@ def forward_bench(args, w, gla, dev, stream, host_inputs, dev_inputs):
 
     npass = max(50, args.steps)
     configs = list(WORKLOADS) if any(x.name == w.name for x in WORKLOADS) else [w]
+    # the headline workload last, so the headline's warmup follows its own
+    # passes (not the 10 GB of the 60 s layer's inputs)
+    configs = [x for x in configs if x.name != w.name] + [w]
     if args.no_sweep:
         configs = [w]
     scratch = torch.zeros(EVICT_BYTES // 4, dtype=torch.float32, device=dev)
@@ -790,6 +793,9 @@ def forward_bench(args, w, gla, dev, stream, host_inputs, dev_inputs):
             units = wl.B * wl.N * wl.H
             t_ceil = 4 * wl.D * units / (rd * 1e9) + 6 * wl.D * units / (rw * 1e9)
             fig["frac_of_streaming_ceiling"] = t_ceil * 1e3 / fig["ms"]
+    # reported in the canonical order of the five layer shapes
+    rank = {x.name: i for i, x in enumerate(WORKLOADS)}
+    all_cfg.sort(key=lambda f: rank.get(f["workload"], len(rank)))
 
     units = w.B * w.N * w.H
     out_bytes = 6 * w.D * units
