@@ -229,6 +229,31 @@ int get_workspace(size_t bytes, void* stream, void** out, std::unique_lock<std::
   return GLA_OK;
 }
 
+// Frees the current device's cached workspaces.  The device is synchronised
+// first, under the cache's lock: every kernel enqueued with one of these
+// buffers was enqueued while the lock was held, so it has finished before the
+// buffer goes.  Later calls allocate afresh.
+int release_workspaces() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  if (!g_ws) return GLA_OK;
+  bool any = false;
+  for (const auto& kv : *g_ws) any = any || (kv.first.device == dev && kv.second.ptr);
+  if (!any) return GLA_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return GLA_ERR_HIP;
+  int rc = GLA_OK;
+  for (auto it = g_ws->begin(); it != g_ws->end();) {
+    if (it->first.device == dev) {
+      if (it->second.ptr && hipFree(it->second.ptr) != hipSuccess) rc = GLA_ERR_HIP;
+      it = g_ws->erase(it);
+    } else {
+      ++it;
+    }
+  }
+  return rc;
+}
+
 int check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
   if (!ws) return GLA_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return GLA_ERR_WORKSPACE;
@@ -418,6 +443,8 @@ size_t gla_workspace_bytes(int B, int N, int H, int D) {
   if (bytes == 0) return 0;
   return gla::make_plan(B, N, H, D).ws_bytes;
 }
+
+int gla_workspace_release(void) { return release_workspaces(); }
 
 int gla_forward_check(const void* q, const void* k, const void* v, const void* g,
                       const gla_rope_tables* rope, const void* out, int B, int N, int H, int D) {

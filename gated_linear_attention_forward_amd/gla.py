@@ -30,7 +30,8 @@ GLA_ERR_SCRATCH = -10
 
 EXPORTS = (
     "gla_strerror", "gla_rope_table_floats", "gla_rope_fill_host", "gla_rope_create",
-    "gla_rope_destroy", "gla_workspace_bytes", "gla_forward", "gla_forward_ws",
+    "gla_rope_destroy", "gla_workspace_bytes", "gla_workspace_release", "gla_forward",
+    "gla_forward_ws",
     "gla_forward_check", "gla_forward_noalloc", "gla_state_ws", "gla_output_ws", "gla_state",
     "gla_forward_blocks", "gla_forward_blocks_ws", "gla_workspace_bytes_blocks",
     "gla_forward_blocks_check", "gla_softmax_forward", "gla_softmax_forward_ws",
@@ -82,6 +83,7 @@ def load_library():
         "gla_rope_create": ([i32] * 4 + [dbl] + [i32] * 3 + [vp, ctypes.POINTER(rp)], i32),
         "gla_rope_destroy": ([rp], i32),
         "gla_workspace_bytes": ([i32] * 4, sz),
+        "gla_workspace_release": ([], i32),
         "gla_forward": ([vp] * 4 + [rp, vp] + [i32] * 4 + [vp], i32),
         "gla_forward_ws": ([vp] * 4 + [rp, vp] + [i32] * 4 + [vp, sz, vp], i32),
         "gla_forward_check": ([vp] * 4 + [rp, vp] + [i32] * 4, i32),
@@ -224,6 +226,14 @@ def _rope_ptr(rope):
 
 def gla_workspace_bytes(B: int, N: int, H: int, D: int) -> int:
     return load_library().gla_workspace_bytes(B, N, H, D)
+
+
+def gla_workspace_release(device=None) -> None:
+    """Frees the library-owned workspaces of `device` (default: the current
+    one) after synchronising it; later calls allocate new ones."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        _ok(load_library().gla_workspace_release(), "gla_workspace_release")
 
 
 def alloc_workspace(B: int, N: int, H: int, D: int, device=None) -> torch.Tensor:

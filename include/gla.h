@@ -121,6 +121,18 @@ int gla_forward(const void* q, const void* k, const void* v, const void* g,
                 const gla_rope_tables* rope, void* out, int B, int N, int H, int D,
                 void* stream);
 
+/* Frees the library-owned workspaces of the current device: the ones
+ * gla_forward, gla_forward_blocks, gla_softmax_forward, gla_backward,
+ * gla_backward_saved and gla_forward_proj cache per (device, stream) and
+ * otherwise keep until the process ends.  It first synchronises the device
+ * (hipDeviceSynchronize), so every kernel that may still read one of them
+ * has finished; the next call that needs a workspace allocates a new one.
+ * Caller-owned workspaces, RoPE tables and gla_forward_noalloc's fixed
+ * scratch are not touched.  Returns GLA_OK (also when nothing is cached) or
+ * GLA_ERR_HIP if the synchronisation or a hipFree fails; a device fault of
+ * earlier work surfaces here as GLA_ERR_HIP. */
+int gla_workspace_release(void);
+
 /* Same as gla_forward with a caller-owned device workspace (>= the size
  * gla_workspace_bytes returns, 256-byte aligned, overlapping none of the
  * tensors: GLA_ERR_ALIAS otherwise).  The workspace must not be used by

@@ -297,6 +297,29 @@ def test_bitwise_deterministic_and_entry_points_agree():
     assert torch.equal(o1.view(torch.int16), o4.view(torch.int16))
 
 
+def test_workspace_release_then_calls_allocate_again():
+    """gla_workspace_release frees the cached workspaces (after a device
+    synchronisation); calls before and after it give the same bits, twice in a
+    row, and a release with nothing cached is a no-op."""
+    w = BY_NAME["5b_480p_81f"]
+    say("case workspace release")
+    q, k, v, g = to_dev(*make_inputs(w))
+    dout = torch.randn_like(q)
+    rope = gla.gla_rope_create(w.T, w.Hh, w.W, w.D)
+    o1 = gla.gla_forward(q, k, v, g, rope)
+    d1 = gla.gla_backward(q, k, v, g, dout, rope)
+    gla.gla_workspace_release()
+    gla.gla_workspace_release()
+    o2 = gla.gla_forward(q, k, v, g, rope)
+    d2 = gla.gla_backward(q, k, v, g, dout, rope)
+    gla.gla_workspace_release()
+    torch.cuda.synchronize()
+    rope.close()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    for a, b in zip(d1, d2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 @pytest.mark.parametrize("B,H,D,grid", [(1, 2, 32, (10, 12, 16)), (3, 1, 32, (9, 11, 12)),
                                         (1, 1, 32, (1, 1, 1100))])
 @pytest.mark.parametrize("rope", [True, False])
