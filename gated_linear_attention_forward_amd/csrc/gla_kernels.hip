@@ -1225,8 +1225,14 @@ void output_persist_kernel(KArgs a, int nsub) {
   const int b = blockIdx.z;
   const int h = (int)blockIdx.x * G + wave % G;
   const int bh = b * a.H + h;
-  const int s = blockIdx.y;
-  const int N = a.N;
+  // attention block ab of the block-causal form: grid.y = NB x nsub, and the
+  // block walks only ab's tokens [n0, N) with ab's state operand.  The
+  // bidirectional mixer is one attention block: ab = 0, tokens [0, a.N).
+  const int ab = __builtin_amdgcn_readfirstlane((int)blockIdx.y / nsub);
+  const int s = (int)blockIdx.y - ab * nsub;
+  const int n0 = ab * a.BT;
+  const int N = min(n0 + a.BT, a.N);  // end of the block's window
+  const int bhb = bh * a.NB + ab;     // (head, attention block) operand
   TabView tv{};
 
   const size_t boff = (size_t)b * a.N * a.H * D;
@@ -1340,7 +1346,7 @@ void output_persist_kernel(KArgs a, int nsub) {
   // the wave's steps: tokens RANGE r + 16 (wave / G) .. for ranges
   // r = s + k nsub
   const int stride = RANGE * nsub;
-  int base = RANGE * s + 16 * (wave / G);
+  int base = n0 + RANGE * s + 16 * (wave / G);
   if (ROPE) gw.init(a, (uint32_t)min(base + col, N - 1), (uint32_t)stride);
   u32x4 qa[KS], qb[KS];
   OChunk ga[4], gb[4];
@@ -1357,7 +1363,7 @@ void output_persist_kernel(KArgs a, int nsub) {
     constexpr int NCH = (CH + LPH - 1) / LPH;   // chunks per lane
     const int li = (wave / G) * 64 + lane;
     const __amdgpu_buffer_rsrc_t rsl =
-        make_rsrc(a.sl + (size_t)bh * ROWS * D, (uint32_t)CH * 16u);  // past CH: zero
+        make_rsrc(a.sl + (size_t)bhb * ROWS * D, (uint32_t)CH * 16u);  // past CH: zero
     u32x4 v[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) v[k] = load16(rsl, (uint32_t)(k * LPH + li) * 16u);
@@ -1516,7 +1522,7 @@ void output_persist_kernel(KArgs a, int nsub) {
   } else {
     RowStage<D, D, 256> st_s;
     RowStage<D, 2, 256, D> st_z;
-    const uint16_t* sl = a.sl + (size_t)bh * ROWS * D;
+    const uint16_t* sl = a.sl + (size_t)bhb * ROWS * D;
     st_s.load(sl);
     st_z.load(sl);
     if (ROPE) {
@@ -1673,10 +1679,13 @@ constexpr size_t persist_fixed_lds() {
 // blocks only) as fp16 pairs, else it is read from global memory.
 // Blocks per head group of the persistent output launch: about
 // kPersistBlocks in all, but no more per group than it has ranges.
+// A group is G heads of one attention block (the whole sequence for the
+// bidirectional mixer), so a block-causal pass has NB times as many.
+long long persist_groups(const Plan& p, int G) { return (long long)(p.BH / G) * p.NB; }
 int persist_nsub(const Plan& p, int G) {
-  const int groups = p.BH / G;
-  const int ranges = (p.N + 64 / G - 1) / (64 / G);
-  const int nsub = kPersistBlocks / groups > 0 ? kPersistBlocks / groups : 1;
+  const long long groups = persist_groups(p, G);
+  const int ranges = (p.BT + 64 / G - 1) / (64 / G);
+  const int nsub = kPersistBlocks / groups > 0 ? (int)(kPersistBlocks / groups) : 1;
   return nsub < ranges ? nsub : ranges;
 }
 
@@ -1691,7 +1700,7 @@ hipError_t launch_output_persist(const Plan& p, KArgs a, hipStream_t stream) {
   const bool t16 = G > 1 && a.cs && !t32 && fixed + 4 * pairs <= kMaxLdsPerBlock;
   size_t lds = fixed + (t32 ? 8 * pairs : (t16 ? 4 * pairs : 0));
   if (lds < kPersistLdsBytes) lds = kPersistLdsBytes;
-  const dim3 g(p.H / G, nsub, p.B);
+  const dim3 g(p.H / G, nsub * p.NB, p.B);
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = allow_lds<decltype(kern)::value>(lds);
     if (e != hipSuccess) return e;
@@ -1712,33 +1721,42 @@ hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream, int src) 
     if (src == kSrcPartials) return launch_output_persist<D, 1, false, kSrcPartials>(p, a, stream);
     if (src == kSrcInBlock) return launch_output_persist<D, 1, false, kSrcInBlock>(p, a, stream);
   }
-  if (p.NB == 1) {
-    if constexpr (D == 128) {
-      // as many heads per block (4, then 2) as divide H with the table in LDS
-      // (fp16 pairs at least; whole-row q tiles if they fit beside it): the
-      // blocks of a group read whole contiguous runs of the group's heads,
-      // which streams faster than one head's rows.  A block stages G heads'
-      // operands, so this pays only where each wave then runs at least
-      // kGroupMinSteps steps (5B 480p/81f, with about 5, measured 19.5 us
-      // per output pass with one head per block and 22.7 with four).
-      const size_t tb16 = a.cs ? 4 * persist_table_pairs(a) : 0;
-      auto steps = [&](int G) {
-        const int groups = p.BH / G;
-        const int nsub = kPersistBlocks / groups > 0 ? kPersistBlocks / groups : 1;
-        return (p.N + 64 / G * nsub - 1) / (64 / G * nsub);
-      };
-      if (p.H % 4 == 0 && steps(4) >= kGroupMinSteps) {
-        if (persist_fixed_lds<D, 4, true>() + tb16 <= kMaxLdsPerBlock)
-          return launch_output_persist<D, 4, true>(p, a, stream);
-        if (persist_fixed_lds<D, 4, false>() + tb16 <= kMaxLdsPerBlock)
-          return launch_output_persist<D, 4, false>(p, a, stream);
-      }
-      if (p.H % 2 == 0 && steps(2) >= kGroupMinSteps &&
-          persist_fixed_lds<D, 2, true>() + tb16 <= kMaxLdsPerBlock)
-        return launch_output_persist<D, 2, true>(p, a, stream);
-      return launch_output_persist<D, 1, true>(p, a, stream);
+  if constexpr (D == 128) {
+    // as many heads per block (4, then 2) as divide H with the table in LDS
+    // (fp16 pairs at least; whole-row q tiles if they fit beside it): the
+    // blocks of a group read whole contiguous runs of the group's heads,
+    // which streams faster than one head's rows.  A block stages G heads'
+    // operands, so this pays only where each wave then runs at least
+    // kGroupMinSteps steps (5B 480p/81f, with about 5, measured 19.5 us
+    // per output pass with one head per block and 22.7 with four).
+    // Block-causal passes (NB > 1) take the persistent kernel too while
+    // their groups, one per (attention block, G heads), fit one round of
+    // blocks that fills at least 7/8 of the chip; other lists of attention
+    // blocks keep output_kernel (5B 720p/60s in 5-frame blocks: 185
+    // persistent blocks measured 825 us per pass against 820 with it).
+    const size_t tb16 = a.cs ? 4 * persist_table_pairs(a) : 0;
+    auto fits = [&](int G) {
+      if (p.NB == 1) return true;
+      const long long groups = persist_groups(p, G);
+      return groups <= kPersistBlocks && groups * persist_nsub(p, G) >= kPersistBlocks * 7 / 8;
+    };
+    auto steps = [&](int G) {
+      const long long groups = persist_groups(p, G);
+      const int nsub = kPersistBlocks / groups > 0 ? (int)(kPersistBlocks / groups) : 1;
+      return (p.BT + 64 / G * nsub - 1) / (64 / G * nsub);
+    };
+    if (p.H % 4 == 0 && fits(4) && steps(4) >= kGroupMinSteps) {
+      if (persist_fixed_lds<D, 4, true>() + tb16 <= kMaxLdsPerBlock)
+        return launch_output_persist<D, 4, true>(p, a, stream);
+      if (persist_fixed_lds<D, 4, false>() + tb16 <= kMaxLdsPerBlock)
+        return launch_output_persist<D, 4, false>(p, a, stream);
     }
-    return launch_output_persist<D, 1, false>(p, a, stream);
+    if (p.H % 2 == 0 && fits(2) && steps(2) >= kGroupMinSteps &&
+        persist_fixed_lds<D, 2, true>() + tb16 <= kMaxLdsPerBlock)
+      return launch_output_persist<D, 2, true>(p, a, stream);
+    if (fits(1)) return launch_output_persist<D, 1, true>(p, a, stream);
+  } else {
+    if (p.NB == 1) return launch_output_persist<D, 1, false>(p, a, stream);
   }
   const dim3 g3(p.BH, p.C2);
   const bool tl = a.cs && table_lds_bytes(a) <= kMaxLdsTableBytes;

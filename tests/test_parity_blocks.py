@@ -175,6 +175,37 @@ def test_workload_720p_in_five_frame_blocks():
     assert r_S <= 3e-3 and r_z <= 1e-6
 
 
+# Shapes sized so that the output half runs on the persistent kernel, one
+# block per (attention block, G heads) walking only its attention block's
+# tokens: the launch takes it for several attention blocks when those groups
+# fill at least 7/8 of one round of 256 blocks (and, for G > 1, each wave runs
+# at least 16 steps).  B, H, grid, block tokens, RoPE, carried state, G:
+PERSISTENT_BLOCKS = [
+    (1, 3, (5, 20, 50), 1350, True, True),      # G = 1: 4 blocks x 3 heads x 21 ranges
+    (1, 3, (5, 20, 50), 1350, False, False),    # G = 1 without RoPE
+    (1, 2, (50, 50, 50), 62000, True, False),   # G = 2: a 1,000-token last block
+    (1, 4, (40, 30, 52), 31000, True, True),    # G = 4 (fp16 table pairs, q tiles)
+]
+
+
+@pytest.mark.parametrize("B,H,grid,L,rope,state", PERSISTENT_BLOCKS)
+def test_blocks_on_the_persistent_output_kernel(B, H, grid, L, rope, state):
+    """Every output and the returned state against oracle.forward_blocks."""
+    D = 128
+    N = grid[0] * grid[1] * grid[2]
+    say(f"case blocks persistent B={B} H={H} grid={grid} L={L} rope={rope} state={state}")
+    q, k, v, g = random_inputs(B, N, H, D, seed=3000 + H + L)
+    S_in, z_in = carried(B, H, D, seed=L) if state else (None, None)
+    got, S_got, z_got = run_gpu(q, k, v, g, grid if rope else None, L, S_in, z_in)
+    ref, S_ref, z_ref = oracle.forward_blocks(
+        q, k, v, g, oracle.Grid(*grid) if rope else None, L,
+        S_in.double().numpy() if state else None, z_in.double().numpy() if state else None)
+    assert_close(got, ref, "out")
+    rs, rz = rel(S_got, S_ref), rel(z_got, z_ref)
+    say(f"  state: S rel_l2={rs:.3e} z rel_l2={rz:.3e}")
+    assert rs <= 3e-3 and rz <= 1e-6
+
+
 def test_empty_sequence_returns_the_carried_state():
     say("case blocks empty")
     B, H, D = 2, 3, 64
