@@ -1730,15 +1730,24 @@ hipError_t launch_output_d(const Plan& p, KArgs a, hipStream_t stream, int src) 
     // kGroupMinSteps steps (5B 480p/81f, with about 5, measured 19.5 us
     // per output pass with one head per block and 22.7 with four).
     // Block-causal passes (NB > 1) take the persistent kernel too while
-    // their groups, one per (attention block, G heads), fit one round of
-    // blocks that fills at least 7/8 of the chip; other lists of attention
-    // blocks keep output_kernel (5B 720p/60s in 5-frame blocks: 185
-    // persistent blocks measured 825 us per pass against 820 with it).
+    // their groups, one per (attention block, G heads), fill at least 7/8
+    // of the chip's rounds of blocks; other lists of attention blocks keep
+    // output_kernel (5B 720p/60s in 5-frame blocks: 185 persistent blocks
+    // measured 825 us per pass against 820 with it).
     const size_t tb16 = a.cs ? 4 * persist_table_pairs(a) : 0;
     auto fits = [&](int G) {
       if (p.NB == 1) return true;
       const long long groups = persist_groups(p, G);
-      return groups <= kPersistBlocks && groups * persist_nsub(p, G) >= kPersistBlocks * 7 / 8;
+      if (groups > kPersistBlocks) {
+        // one block per group (nsub = 1) in several rounds, with the rounds
+        // 7/8 full on average, and grouped heads only: 5B 720p/60s in
+        // 1-frame blocks (905 four-head groups) 1,047 -> 1,016 us per pass,
+        // but 14B 480p in 1-frame blocks (1,600 one-head groups) 248 -> 258
+        if (G == 1) return false;
+        const long long rounds = (groups + kPersistBlocks - 1) / kPersistBlocks;
+        return groups * 8 >= rounds * kPersistBlocks * 7;
+      }
+      return groups * persist_nsub(p, G) >= kPersistBlocks * 7 / 8;
     };
     auto steps = [&](int G) {
       const long long groups = persist_groups(p, G);

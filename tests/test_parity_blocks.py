@@ -178,13 +178,14 @@ def test_workload_720p_in_five_frame_blocks():
 # Shapes sized so that the output half runs on the persistent kernel, one
 # block per (attention block, G heads) walking only its attention block's
 # tokens: the launch takes it for several attention blocks when those groups
-# fill at least 7/8 of one round of 256 blocks (and, for G > 1, each wave runs
-# at least 16 steps).  B, H, grid, block tokens, RoPE, carried state, G:
+# fill at least 7/8 of its rounds of 256 blocks (one round, or several with
+# G > 1), and, for G > 1, each wave runs at least 16 steps.  B, H, grid, block tokens, RoPE, carried state, G:
 PERSISTENT_BLOCKS = [
     (1, 3, (5, 20, 50), 1350, True, True),      # G = 1: 4 blocks x 3 heads x 21 ranges
     (1, 3, (5, 20, 50), 1350, False, False),    # G = 1 without RoPE
     (1, 2, (50, 50, 50), 62000, True, False),   # G = 2: a 1,000-token last block
     (1, 4, (40, 30, 52), 31000, True, True),    # G = 4 (fp16 table pairs, q tiles)
+    (1, 4, (45, 40, 64), 257, True, False),     # G = 4, 449 groups in two rounds of blocks
 ]
 
 
