@@ -230,7 +230,8 @@ def gla_workspace_bytes(B: int, N: int, H: int, D: int) -> int:
 
 def gla_workspace_release(device=None) -> None:
     """Frees the library-owned workspaces of `device` (default: the current
-    one) after synchronising it; later calls allocate new ones."""
+    one) after synchronising it; later calls allocate new ones.  Not while a
+    stream of that device is being captured into a graph."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     with torch.cuda.device(dev):
         _ok(load_library().gla_workspace_release(), "gla_workspace_release")

@@ -130,7 +130,9 @@ int gla_forward(const void* q, const void* k, const void* v, const void* g,
  * Caller-owned workspaces, RoPE tables and gla_forward_noalloc's fixed
  * scratch are not touched.  Returns GLA_OK (also when nothing is cached) or
  * GLA_ERR_HIP if the synchronisation or a hipFree fails; a device fault of
- * earlier work surfaces here as GLA_ERR_HIP. */
+ * earlier work surfaces here as GLA_ERR_HIP.  Do not call it while a stream
+ * of the device is being captured into a HIP graph: a device synchronisation
+ * is not allowed then, and the capture would be invalidated. */
 int gla_workspace_release(void);
 
 /* Same as gla_forward with a caller-owned device workspace (>= the size
